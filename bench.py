@@ -1,0 +1,215 @@
+"""Benchmark of the FP8-moment AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2_7b]
+
+Times K whole optimizer steps (every tensor of the list, one fp8adam_step
+each) after W warm-up steps, with inputs resident in HBM, and prints one JSON
+line: params updated/s, the roofline of the dominant kernel (algorithmic
+bytes / its HIP-event duration, against 8 TB/s), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Other modes (used to make the committed profiles):
+    --calibrate-copy   a plain device copy of 2 GiB, for HBM counter scaling
+    --no-cpu-baseline  skip the oracle timing
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# algorithmic HBM bytes per parameter of the dominant kernel (one launch covers every parameter)
+#   update pass, fp32 master: read p4 g2 m1 v1, write p4 m1 v1                 = 14
+#   update pass, bf16 master: read p2 g2 m1 v1, write p2 m1 v1                 = 10
+#   block-128 pass, fp32 master: 14 + 2 scales * (read 4 + write 4) / 128      = 14.125
+BYTES_PER_PARAM = {("tensor", "fp32"): 14.0, ("tensor", "bf16"): 10.0,
+                   ("block128", "fp32"): 14.125, ("block128", "bf16"): 10.125}
+KERNEL_SOURCES = ["precision_adam_optimizer_amd/csrc/fp8adam.hip", "precision_adam_optimizer_amd/csrc/fp8_codec.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes 5 times")
+
+
+def cpu_baseline(w, shapes, idx):
+    """The oracle, single-threaded, on step 1 of the tensors `idx` (inputs drawn
+    with the same generators on the GPU, copied to the host)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    total, elapsed = 0, 0.0
+    h = oracle.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
+    cfg = oracle.make_config(h, 0 if w.m_fmt == "e4m3" else 1, 0 if w.v_fmt == "e4m3" else 1,
+                             block=128 if w.granularity == "block128" else 0, master_bf16=(w.master == "bf16"))
+    for i in idx:
+        name, s = shapes[i]
+        n = workloads.numel(s)
+        p = workloads.make_param(w, i, s, "cuda").cpu()
+        p = p.view(torch.int16).numpy().view(np.uint16).copy() if w.master == "bf16" else p.numpy().copy()
+        g = workloads.make_grad(w, i, s, 1, "cuda").cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        nb = 1 if w.granularity == "tensor" else -(-n // 128)
+        cm, cv = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+        sm, sv = np.ones(nb, np.float32), np.ones(nb, np.float32)
+        t0 = time.perf_counter()
+        oracle.step(cfg, p, g, cm, cv, sm, sv)
+        elapsed += time.perf_counter() - t0
+        total += n
+    return total, elapsed
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama2_7b",
+                    choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_13b_bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in the design notes); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import torch
+
+    import precision_adam_optimizer_amd as pk
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = w.shapes
+    total = w.total_params
+    log(f"workload {w.name}: {len(shapes)} tensors, {total} params; generating inputs")
+    params = [workloads.make_param(w, i, s, dev) for i, (_, s) in enumerate(shapes)]
+    grads = [workloads.make_grad(w, i, s, 1, dev) for i, (_, s) in enumerate(shapes)]
+    torch.cuda.synchronize()
+    opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    log(f"context: {opt.num_chunks} chunks; warmup {args.warmup} steps")
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        opt.step(step=t, **hp)
+    torch.cuda.synchronize()
+
+    opt.set_timing(True)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        t += 1
+        opt.step(step=t, **hp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ktimes = opt.kernel_times()
+    opt.set_timing(False)
+    ms_per_step = ms_total / args.steps
+    value = total / (ms_per_step / 1e3)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
+    for k, (tot, cnt) in ktimes.items():
+        if cnt:
+            log(f"  {k}: {cnt} launches, avg {tot / cnt * 1e3:.1f} us")
+
+    kernel = "block128_pass" if w.granularity == "block128" else "update_pass"
+    ktot, kcnt = ktimes[kernel]
+    kavg_s = ktot / kcnt / 1e3
+    bpp = BYTES_PER_PARAM[(w.granularity, w.master)]
+    alg_bytes = bpp * total
+    achieved = alg_bytes / kavg_s / 1e9
+    traffic = load_traffic(w.name, kernel)
+    step_bytes = alg_bytes + (4.0 * total if w.granularity == "tensor" else 0.0)  # + amax pass reads g, m, v
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
+                "bytes_per_param": bpp,
+                "whole_step_GBps_design_bytes": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # layer 0 of the list (its nine tensors), step 1, one thread
+        idx = [i for i, (n, _) in enumerate(shapes) if n.startswith("layers.0.")] or [0]
+        n_cpu, sec = cpu_baseline(w, shapes, idx)
+        cpu = {"value": round(n_cpu / sec, 1), "unit": "params/s", "cores": 1, "kind": "oracle",
+               "sample": f"step 1 of the {len(idx)} tensors of layer 0 ({n_cpu} params) of the same list, "
+                         f"single-threaded C oracle, {sec:.1f} s"}
+        log(f"cpu oracle: {n_cpu / sec:.3e} params/s over {n_cpu} params")
+
+    out = {
+        "metric": "params updated/sec + achieved HBM GB/s (% of peak), 7B-shaped FP8-moment Adam step",
+        "value": round(value, 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.master == "fp32" else "bf16-master/f32-math",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tensors": len(shapes), "params": total, "m_format": w.m_fmt,
+                   "v_format": w.v_fmt, "scale": w.granularity, "master": w.master, "grad": "bf16",
+                   "weight_decay": w.weight_decay, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    opt.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

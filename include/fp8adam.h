@@ -1,0 +1,172 @@
+/*
+ * fp8adam.h -- C ABI of the FP8-moment Adam/AdamW step for AMD MI355X (gfx950).
+ *
+ * The step is Adam/AdamW whose two moments are stored as FP8 codes with a
+ * scale: the first moment m in E4M3, the second moment v in E5M2 by default.
+ * Sources (the three pages the method is taken from):
+ *   - daoxuan.cc explainer of arXiv 2409.12517 (blog.daoxuan.cc/posts/32114),
+ *     section on why Adam keeps m in E4M3 and v in E5M2: the format table,
+ *     the asymmetry of the update (m in the numerator times the learning rate,
+ *     v under a square root in the denominator), and the numerical example
+ *     (epsilon added after the square root; E4M3 smallest normal 2^-6).
+ *   - shd-paper.top summary of arXiv 2409.12517v2 ("Scaling FP8 training to
+ *     trillion-token LLMs"), method details and abstract: both Adam moments
+ *     are quantized to FP8.
+ *   - zyxy.net/?p=24419 (FP8 mixed-precision article), sections on FP8
+ *     formats, mixed-precision strategy (FP32 master weights), strategies
+ *     (dynamic range by max-abs tracking, exponent-offset adjustment,
+ *     round-to-nearest) and the code example (AdamW).
+ *
+ * Arithmetic, per element (fp32):
+ *   m  = decode(c_m) * s_m            v  = decode(c_v) * s_v
+ *   m' = fma(b1, m, (1-b1)*g)         v' = fma(b2, v, (1-b2)*(g*g))
+ *   p' = p*(1 - lr*wd) - lr/(1-b1^t) * m' / (sqrt(v'/(1-b2^t)) + eps)
+ *   s_m', s_v' chosen from max|m'| and max v' over the tensor (or over each
+ *   128-element block);  c_m' = encode(m' / s_m'),  c_v' = encode(v' / s_v')
+ * Encoding is OCP E4M3FN / E5M2, round-to-nearest-even, saturating at the
+ * format maximum (448 / 57344).  The FP8 codes and scales are bit-exact
+ * functions of the inputs; p' is within 1e-6 relative of the exact update
+ * (fast sqrt / reciprocal on the device).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative FP8ADAM_E* code; fp8adam_last_error()
+ *     then gives a message (thread-local, valid until the next call on that
+ *     thread).  Nothing aborts and no C++ exception crosses the ABI.
+ *   - Pointers named "device" are HIP device memory of the current device;
+ *     pointers named "host" are ordinary host memory.
+ *   - Work is enqueued on the given stream (0 = the null stream) and runs
+ *     asynchronously unless stated otherwise.
+ */
+#ifndef FP8ADAM_H
+#define FP8ADAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8ADAM_OK 0
+#define FP8ADAM_EINVAL (-1) /* bad argument (null, n <= 0, numel < 0, t < 1, beta outside [0,1), eps < 0, bad enum) */
+#define FP8ADAM_EALIGN (-2) /* a device pointer is not 16-byte aligned */
+#define FP8ADAM_ENOMEM (-3) /* host or device allocation failed */
+#define FP8ADAM_EHIP (-4)   /* a HIP runtime call failed; the message holds hipGetErrorString */
+
+/* FP8 storage formats (OCP): E4M3FN (bias 7, max 448, no Inf) and E5M2 (bias 15, max 57344). */
+typedef enum { FP8ADAM_E4M3 = 0, FP8ADAM_E5M2 = 1 } fp8adam_format;
+/* One scale per tensor, or one per contiguous run of 128 elements of the flattened tensor. */
+typedef enum { FP8ADAM_SCALE_TENSOR = 0, FP8ADAM_SCALE_BLOCK128 = 1 } fp8adam_granularity;
+/* POW2: smallest power of two s with amax/s <= FMAX (exponent clamped to [-126,126]).
+ * AMAX: s = amax/FMAX and inv_s = FMAX/amax (s raised to 2^-126 if smaller).
+ * amax = 0 or non-finite gives s = 1 in both modes. */
+typedef enum { FP8ADAM_SCALE_POW2 = 0, FP8ADAM_SCALE_AMAX = 1 } fp8adam_scale_mode;
+/* Master weights: fp32, or bf16 (the update is rounded to nearest-even bf16). */
+typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master;
+
+typedef struct {
+    int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
+    int32_t v_format;      /* fp8adam_format of the second moment (default E5M2) */
+    int32_t granularity;   /* fp8adam_granularity */
+    int32_t scale_mode;    /* fp8adam_scale_mode */
+    int32_t master;        /* fp8adam_master */
+    int32_t collect_stats; /* nonzero: count underflow / saturation / non-finite per tensor */
+} fp8adam_config;
+
+/* One parameter tensor.  All pointers are device pointers owned by the caller,
+ * 16-byte aligned, and must stay valid and unchanged until fp8adam_destroy.
+ *   param   : numel fp32 (or bf16) master weights, updated in place
+ *   grad    : numel bf16 gradients, read only
+ *   m, v    : numel FP8 codes of the moments, updated in place
+ *   m_scale : 1 float (tensor granularity) or ceil(numel/128) floats (block), in place
+ *   v_scale : same as m_scale, for v
+ * The state before the first step is all-zero codes with scales 1.0. */
+typedef struct {
+    void *param;
+    const void *grad;
+    uint8_t *m;
+    uint8_t *v;
+    float *m_scale;
+    float *v_scale;
+    int64_t numel;
+} fp8adam_tensor;
+
+/* Hyperparameters of one step.  step is the 1-based t used for bias correction. */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} fp8adam_hparams;
+
+/* Per-tensor diagnostics of the most recent step (amax tracking and
+ * under/overflow monitoring).  In block mode amax_* is the max over the
+ * tensor's blocks and scale_* the largest block scale; both need collect_stats
+ * in block mode (else 0). */
+typedef struct {
+    float amax_m, amax_v;   /* max |m'| and max v' over the tensor */
+    float scale_m, scale_v; /* new scales */
+    int64_t underflow_m, underflow_v; /* nonzero moment stored as a +-0 code */
+    int64_t saturated_m, saturated_v; /* |x * inv_s| > FMAX before clamping */
+    int64_t nonfinite;                /* elements with a non-finite m' or v' */
+} fp8adam_stats_t;
+
+typedef struct fp8adam_ctx fp8adam_ctx;
+
+/* Build a context over n tensors: validates them (EINVAL / EALIGN), builds the
+ * multi-tensor chunk table and the per-tensor descriptors on the device
+ * (allocates; ENOMEM / EHIP), and synchronizes `stream` before returning.
+ * *out receives the handle (NULL on failure).  The device is the current one. */
+int fp8adam_init(fp8adam_ctx **out, const fp8adam_tensor *tensors, int32_t n,
+                 const fp8adam_config *cfg, hipStream_t stream);
+
+/* One optimizer step over every tensor of the context, enqueued on `stream`
+ * and returning at once.  Validates hp (EINVAL).  Allocates nothing.  After the
+ * stream reaches the end of the step each tensor's (codes, scale) pair is
+ * consistent.  Steps of one context must not overlap. */
+int fp8adam_step(fp8adam_ctx *ctx, const fp8adam_hparams *hp, hipStream_t stream);
+
+/* Copy the diagnostics of the last step into out_host[0..n) (n = the context's
+ * tensor count; EINVAL otherwise).  Synchronizes `stream`. */
+int fp8adam_stats(fp8adam_ctx *ctx, fp8adam_stats_t *out_host, int32_t n, hipStream_t stream);
+
+/* Free the context (device buffers and events).  NULL is ignored.  The caller
+ * must make sure no step of this context is still running. */
+void fp8adam_destroy(fp8adam_ctx *ctx);
+
+/* Message for the last nonzero return on this thread ("" if none). */
+const char *fp8adam_last_error(void);
+
+/* ---- device codec (the same converts the step uses), for verification ---- */
+
+/* out[i] = encode_fmt(x[i]) for i < n.  x, out: device.  RNE, saturating. */
+int fp8adam_encode(int32_t fmt, const float *x, uint8_t *out, int64_t n, hipStream_t stream);
+/* out[i] = decode_fmt(codes[i]) for i < n.  codes, out: device.  Exact. */
+int fp8adam_decode(int32_t fmt, const uint8_t *codes, float *out, int64_t n, hipStream_t stream);
+/* out[i] = encode_fmt(fp32 with bit pattern start + i), i < count, count <= 2^32 - start.
+ * out: device, count bytes. */
+int fp8adam_encode_bits_range(int32_t fmt, uint32_t start, int64_t count, uint8_t *out,
+                              hipStream_t stream);
+
+/* ---- measurement ---- */
+
+/* Enable (1) or disable (0) per-kernel timing with HIP events around every
+ * launch of later steps (creates the events; may allocate).  Timing records
+ * at most 4096 launches between two fp8adam_kernel_times calls. */
+int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
+
+/* Per-kernel timing since the last call (or since timing was enabled):
+ * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale commit,
+ * 3 = block-scaled single pass, 4 = stats reset), total_ms[k] and count[k].
+ * Host arrays of length max.  Synchronizes the recorded events, then clears. */
+int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);
+
+/* HIP runtime version the library runs on (hipRuntimeGetVersion), in *version. */
+int fp8adam_runtime_version(int32_t *version);
+
+/* Number of chunks (work-groups of the streaming passes) of the context. */
+int64_t fp8adam_num_chunks(const fp8adam_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8ADAM_H */

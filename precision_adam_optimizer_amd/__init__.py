@@ -1,0 +1,267 @@
+"""Python binding of the FP8-moment Adam/AdamW step for MI355X.
+
+A thin ctypes layer over ``libfp8adam.so`` (C ABI in ``include/fp8adam.h``):
+the functions below carry the C names and only marshal arguments; every step
+of the optimizer runs in the library's HIP kernels.  PyTorch supplies device
+memory and the stream.  There is no fallback: if the library is missing,
+``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp8adam.so")
+
+E4M3, E5M2 = 0, 1
+SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
+SCALE_POW2, SCALE_AMAX = 0, 1
+MASTER_FP32, MASTER_BF16 = 0, 1
+BLOCK = 128
+
+_FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
+_GRAN = {"tensor": SCALE_TENSOR, "block128": SCALE_BLOCK128}
+_SMODE = {"pow2": SCALE_POW2, "amax": SCALE_AMAX}
+
+KERNEL_KINDS = ("amax_pass", "update_pass", "scale_commit", "block128_pass", "stats_reset")
+
+# names of every entry point the header declares
+EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
+           "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
+           "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks")
+
+
+class Fp8AdamError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fp8adam error {code}: {msg}")
+        self.code = code
+
+
+class TensorArg(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("m_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("numel", ctypes.c_int64)]
+
+
+class ConfigArg(ctypes.Structure):
+    _fields_ = [("m_format", ctypes.c_int32), ("v_format", ctypes.c_int32),
+                ("granularity", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("master", ctypes.c_int32), ("collect_stats", ctypes.c_int32)]
+
+
+class HParamsArg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
+
+
+class StatsArg(ctypes.Structure):
+    _fields_ = [("amax_m", ctypes.c_float), ("amax_v", ctypes.c_float),
+                ("scale_m", ctypes.c_float), ("scale_v", ctypes.c_float),
+                ("underflow_m", ctypes.c_int64), ("underflow_v", ctypes.c_int64),
+                ("saturated_m", ctypes.c_int64), ("saturated_v", ctypes.c_int64),
+                ("nonfinite", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the HIP library (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m precision_adam_optimizer_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.fp8adam_init.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg), vp]
+    L.fp8adam_step.argtypes = [vp, ctypes.POINTER(HParamsArg), vp]
+    L.fp8adam_stats.argtypes = [vp, ctypes.POINTER(StatsArg), i32, vp]
+    L.fp8adam_destroy.argtypes = [vp]
+    L.fp8adam_destroy.restype = None
+    L.fp8adam_last_error.restype = ctypes.c_char_p
+    L.fp8adam_encode.argtypes = [i32, vp, vp, i64, vp]
+    L.fp8adam_decode.argtypes = [i32, vp, vp, i64, vp]
+    L.fp8adam_encode_bits_range.argtypes = [i32, ctypes.c_uint32, i64, vp, vp]
+    L.fp8adam_set_timing.argtypes = [vp, i32]
+    L.fp8adam_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), i32]
+    L.fp8adam_runtime_version.argtypes = [ctypes.POINTER(i32)]
+    L.fp8adam_num_chunks.argtypes = [vp]
+    L.fp8adam_num_chunks.restype = i64
+    for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
+                 "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
+                 "fp8adam_runtime_version"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise Fp8AdamError(rc, load().fp8adam_last_error().decode())
+
+
+def current_stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+# ---------------------------------------------------------------- C names
+
+def fp8adam_init(tensors: list[TensorArg], cfg: ConfigArg, stream: int | None = None) -> int:
+    arr = (TensorArg * len(tensors))(*tensors)
+    h = ctypes.c_void_p()
+    _check(load().fp8adam_init(ctypes.byref(h), arr, len(tensors), ctypes.byref(cfg),
+                               current_stream() if stream is None else stream))
+    return h.value
+
+
+def fp8adam_step(ctx: int, hp: HParamsArg, stream: int | None = None) -> None:
+    _check(load().fp8adam_step(ctx, ctypes.byref(hp), current_stream() if stream is None else stream))
+
+
+def fp8adam_stats(ctx: int, n: int, stream: int | None = None) -> list[dict]:
+    out = (StatsArg * n)()
+    _check(load().fp8adam_stats(ctx, out, n, current_stream() if stream is None else stream))
+    return [s.as_dict() for s in out]
+
+
+def fp8adam_destroy(ctx: int) -> None:
+    load().fp8adam_destroy(ctx)
+
+
+def fp8adam_last_error() -> str:
+    return load().fp8adam_last_error().decode()
+
+
+def fp8adam_encode(fmt: int, x: torch.Tensor, out: torch.Tensor, stream: int | None = None) -> None:
+    assert x.dtype == torch.float32 and out.dtype == torch.uint8 and x.is_contiguous() and out.is_contiguous()
+    assert out.numel() >= x.numel()
+    _check(load().fp8adam_encode(fmt, _ptr(x), _ptr(out), x.numel(),
+                                 current_stream() if stream is None else stream))
+
+
+def fp8adam_decode(fmt: int, codes: torch.Tensor, out: torch.Tensor, stream: int | None = None) -> None:
+    assert codes.dtype == torch.uint8 and out.dtype == torch.float32 and codes.is_contiguous() and out.is_contiguous()
+    assert out.numel() >= codes.numel()
+    _check(load().fp8adam_decode(fmt, _ptr(codes), _ptr(out), codes.numel(),
+                                 current_stream() if stream is None else stream))
+
+
+def fp8adam_encode_bits_range(fmt: int, start: int, count: int, out: torch.Tensor,
+                              stream: int | None = None) -> None:
+    assert out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= count
+    _check(load().fp8adam_encode_bits_range(fmt, start, count, _ptr(out),
+                                            current_stream() if stream is None else stream))
+
+
+def fp8adam_set_timing(ctx: int, enable: bool) -> None:
+    _check(load().fp8adam_set_timing(ctx, int(enable)))
+
+
+def fp8adam_kernel_times(ctx: int) -> dict:
+    n = len(KERNEL_KINDS)
+    tot = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(load().fp8adam_kernel_times(ctx, tot, cnt, n))
+    return {k: (tot[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def fp8adam_runtime_version() -> int:
+    v = ctypes.c_int32()
+    _check(load().fp8adam_runtime_version(ctypes.byref(v)))
+    return v.value
+
+
+def fp8adam_num_chunks(ctx: int) -> int:
+    return load().fp8adam_num_chunks(ctx)
+
+
+# ------------------------------------------------------------ torch wrapper
+
+class FP8AdamW:
+    """FP8-moment AdamW over lists of torch tensors on one GPU.
+
+    params: fp32 or bf16 master weights (all the same dtype); grads: bf16, same
+    numel as their parameter.  The moment codes (uint8) and scales (fp32) are
+    allocated here, zero codes with unit scales, unless ``state`` supplies
+    (m, v, m_scale, v_scale) lists.  Every tensor must be contiguous and
+    16-byte aligned on the same device, and must stay alive with the same
+    storage while this object exists.
+    """
+
+    def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
+                 scale_mode="pow2", collect_stats=False, state=None):
+        params, grads = list(params), list(grads)
+        if len(params) != len(grads) or not params:
+            raise ValueError("need one gradient per parameter and at least one parameter")
+        master = params[0].dtype
+        if master not in (torch.float32, torch.bfloat16):
+            raise ValueError("master weights must be float32 or bfloat16")
+        self.granularity = _GRAN[granularity]
+        self.params, self.grads = params, grads
+        if state is None:
+            m = [torch.zeros(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
+            v = [torch.zeros(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
+            ms = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
+            vs = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
+            state = (m, v, ms, vs)
+        self.m, self.v, self.m_scale, self.v_scale = [list(x) for x in state]
+        args = []
+        for i, (p, g) in enumerate(zip(params, grads)):
+            if p.dtype != master or g.dtype != torch.bfloat16 or p.numel() != g.numel():
+                raise ValueError(f"tensor {i}: dtype or size mismatch")
+            for t in (p, g, self.m[i], self.v[i], self.m_scale[i], self.v_scale[i]):
+                if not t.is_contiguous() or t.device != p.device:
+                    raise ValueError(f"tensor {i}: every buffer must be contiguous on one device")
+            args.append(TensorArg(p.data_ptr(), g.data_ptr(), self.m[i].data_ptr(), self.v[i].data_ptr(),
+                                  self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel()))
+        self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
+                             MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats))
+        self.n = len(params)
+        self.device = params[0].device
+        with torch.cuda.device(self.device):
+            self._ctx = fp8adam_init(args, self.cfg)
+
+    def num_scales(self, numel: int) -> int:
+        return 1 if self.granularity == SCALE_TENSOR else max(1, -(-numel // BLOCK))
+
+    def step(self, *, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+             weight_decay: float = 0.0, step: int) -> None:
+        with torch.cuda.device(self.device):
+            fp8adam_step(self._ctx, HParamsArg(lr, beta1, beta2, eps, weight_decay, step))
+
+    def stats(self) -> list[dict]:
+        with torch.cuda.device(self.device):
+            return fp8adam_stats(self._ctx, self.n)
+
+    def set_timing(self, enable: bool) -> None:
+        fp8adam_set_timing(self._ctx, enable)
+
+    def kernel_times(self) -> dict:
+        return fp8adam_kernel_times(self._ctx)
+
+    @property
+    def num_chunks(self) -> int:
+        return fp8adam_num_chunks(self._ctx)
+
+    def close(self) -> None:
+        if getattr(self, "_ctx", None):
+            torch.cuda.synchronize(self.device)
+            fp8adam_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,156 @@
+// fp8_codec.h -- device-side FP8 codec and step arithmetic for gfx950 (CDNA4).
+//
+// Formats: OCP E4M3FN and E5M2, the two FP8 formats whose bit splits the
+// daoxuan.cc explainer of arXiv 2409.12517 tabulates (section on why Adam keeps
+// m in E4M3 and v in E5M2, "The two FP8 formats") and the zyxy.net FP8
+// article lists ("FP8 formats").  gfx950's packed converts implement exactly
+// these (OCP) encodings with round-to-nearest-even; saturation is done by
+// clamping to +-FMAX with v_med3_f32 first, so the converts never overflow.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8adam {
+
+// FMAX = 0.875 * 2^kMaxExp for both formats: 448 = 0.875 * 2^9, 57344 = 0.875 * 2^16.
+template <int FMT> struct Format;
+template <> struct Format<0> {  // E4M3
+  static constexpr float kMax = 448.0f;
+  static constexpr int kMaxExp = 9;
+};
+template <> struct Format<1> {  // E5M2
+  static constexpr float kMax = 57344.0f;
+  static constexpr int kMaxExp = 16;
+};
+
+// Four codes packed little-endian in a dword -> four floats (exact).
+template <int FMT>
+__device__ __forceinline__ void decode4(uint32_t w, float (&out)[4]) {
+  if constexpr (FMT == 0) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  } else {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    out[0] = lo[0]; out[1] = lo[1]; out[2] = hi[0]; out[3] = hi[1];
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ float decode1(uint32_t code) {
+  if constexpr (FMT == 0) return __builtin_amdgcn_cvt_pk_f32_fp8((int)code, false)[0];
+  else return __builtin_amdgcn_cvt_pk_f32_bf8((int)code, false)[0];
+}
+
+// Four floats -> four codes (RNE, saturating at +-FMAX), packed little-endian.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) {
+  constexpr float M = Format<FMT>::kMax;
+  a = __builtin_amdgcn_fmed3f(a, -M, M);
+  b = __builtin_amdgcn_fmed3f(b, -M, M);
+  c = __builtin_amdgcn_fmed3f(c, -M, M);
+  d = __builtin_amdgcn_fmed3f(d, -M, M);
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode1(float a) {
+  return encode4<FMT>(a, 0.0f, 0.0f, 0.0f) & 0xFFu;
+}
+
+// bf16 <-> fp32.  Widening is exact (shift); narrowing rounds to nearest even.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN, sign kept
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Scale from the amax of a block (fp32 bit pattern, sign bit clear).
+// POW2 (mode 0): smallest power of two s with amax/s <= FMAX; with
+// amax = f * 2^e, f in [0.5, 1): k = e - kMaxExp + [f > 0.875], clamped to
+// [-126, 126]; f > 0.875 <=> the fp32 mantissa field exceeds 0x600000.
+// AMAX (mode 1): s = amax/FMAX, inv = FMAX/amax, correctly rounded; s below
+// 2^-126 is raised to it.  amax = 0 or non-finite gives s = inv = 1.
+// The dynamic-range rule follows the zyxy.net article's "Strategies" section
+// (track the max-abs value, adjust the exponent offset).
+template <int FMT, int SMODE>
+__device__ __forceinline__ void choose_scale(uint32_t amax_bits, float& s, float& inv) {
+  const uint32_t ef = amax_bits >> 23;
+  if (amax_bits == 0u || ef >= 255u) {
+    s = 1.0f;
+    inv = 1.0f;
+    return;
+  }
+  if constexpr (SMODE == 0) {
+    int k = (ef == 0u) ? -126
+                       : (int)ef - 126 - Format<FMT>::kMaxExp + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    k = k < -126 ? -126 : (k > 126 ? 126 : k);
+    s = __uint_as_float((uint32_t)(k + 127) << 23);
+    inv = __uint_as_float((uint32_t)(127 - k) << 23);
+  } else {
+    const float a = __uint_as_float(amax_bits);
+    const float sc = __fdiv_rn(a, Format<FMT>::kMax);
+    if (sc < 0x1p-126f) {
+      s = 0x1p-126f;
+      inv = 0x1p126f;
+    } else {
+      s = sc;
+      inv = __fdiv_rn(Format<FMT>::kMax, a);
+    }
+  }
+}
+
+// Per-step constants, computed on the host from the hyperparameters.
+struct StepConsts {
+  float b1, b2;        // beta1, beta2
+  float omb1, omb2;    // 1 - beta (fp32)
+  float decay;         // 1 - lr * weight_decay
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_bc2;       // 1 / (1 - beta2^t)
+  float eps;
+};
+
+// Moment update (daoxuan.cc explainer, "Adam's update makes the needs
+// asymmetric": m averages g, v averages g^2).  Evaluated exactly as
+// fma(b1, m, (1-b1)*g) and fma(b2, v, (1-b2)*(g*g)) so the FP8 codes that
+// follow are bit-exact functions of the inputs; contraction is off here.
+__device__ __forceinline__ void moment_update(const StepConsts& c, float g, float m, float v,
+                                              float& m1, float& v1) {
+#pragma clang fp contract(off)
+  const float gm = c.omb1 * g;
+  const float gg = g * g;
+  const float gv = c.omb2 * gg;
+  m1 = __builtin_fmaf(c.b1, m, gm);
+  v1 = __builtin_fmaf(c.b2, v, gv);
+}
+
+// AdamW parameter update from the fresh moments: m in the numerator times the
+// bias-corrected step size, eps added after the square root of v-hat
+// (daoxuan.cc explainer, numerical example), decoupled decay (AdamW in the
+// zyxy.net code example).  Hardware sqrt / reciprocal: about 1 ulp each.
+__device__ __forceinline__ float param_update(const StepConsts& c, float p, float m1, float v1) {
+  const float den = __builtin_amdgcn_sqrtf(v1 * c.inv_bc2) + c.eps;
+  const float upd = (c.step_size * m1) * __builtin_amdgcn_rcpf(den);
+  return __builtin_fmaf(p, c.decay, -upd);
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+}  // namespace fp8adam

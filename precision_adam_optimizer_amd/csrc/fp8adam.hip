@@ -1,0 +1,948 @@
+// fp8adam.hip -- FP8-moment Adam/AdamW step for AMD MI355X (gfx950): kernels
+// and the C ABI declared in include/fp8adam.h.
+//
+// Method: Adam whose first moment is stored in FP8 E4M3 and second moment in
+// FP8 E5M2, each with a scale (daoxuan.cc explainer of arXiv 2409.12517,
+// section on why Adam keeps m in E4M3 and v in E5M2; shd-paper.top summary of
+// arXiv 2409.12517v2, method details: both Adam moments quantized to FP8).
+//
+// Device work per step:
+//   per-tensor scales (two streaming passes over a chunked multi-tensor list)
+//     k_amax    : dequantize, update m and v in registers, max|m'| / max v'
+//                 per chunk -> one atomic max per tensor per work-group
+//     k_update  : recompute m', v'; choose the new scales from the amax;
+//                 update p; requantize m', v' with saturation; write p, m, v
+//     k_commit  : new scales into the caller's scale slots, amax reset
+//   per-128-element scales (one streaming pass)
+//     k_block   : eight lanes own one 128-element block; the block amax is a
+//                 3-step DPP max, then update and requantize as above
+// Each work-group owns one chunk of kChunk elements of one tensor; the chunk
+// table is built once at init.  Loads and stores are dword-granular per lane
+// and contiguous across the wave (fp32 master: 16 B per lane).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fp8adam.h"
+#include "fp8_codec.h"
+
+using namespace fp8adam;
+
+namespace {
+
+constexpr int kThreads = 256;                   // 4 waves of 64
+constexpr int kGroup = 4;                       // consecutive elements per lane per access
+constexpr int kSubTile = kThreads * kGroup;     // 1024 elements per work-group access
+constexpr int kUnroll = 4;                      // accesses in flight per lane
+constexpr int64_t kChunk = 16384;               // elements per work-group (multiple of 4096)
+constexpr int kBlock = 128;                     // block-scale granularity
+constexpr int kStatsPerTensor = 5;
+
+static_assert(kChunk % (kSubTile * kUnroll) == 0, "chunk must hold whole unrolled tiles");
+static_assert(kChunk % (kBlock * 32) == 0, "chunk must hold whole block tiles");
+
+struct TensorDesc {
+  void* p;
+  const uint16_t* g;
+  uint8_t* m;
+  uint8_t* v;
+  float* sm;
+  float* sv;
+  int64_t numel;
+  int64_t chunk0;  // index of the tensor's first chunk
+};
+
+enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
+  return x;
+}
+
+// Max over each group of 8 consecutive lanes with DPP (quad swaps, then the
+// half-row mirror); every lane of the group ends with the group max.
+__device__ __forceinline__ uint32_t group8_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return x;
+}
+
+// Work-group max of two values; result valid in thread 0.
+__device__ __forceinline__ void block_max2(uint32_t& a, uint32_t& b) {
+  __shared__ uint32_t red[2][kThreads / 64];
+  a = wave_max(a);
+  b = wave_max(b);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    red[0][wave] = a;
+    red[1][wave] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; w++) {
+      a = max(a, red[0][w]);
+      b = max(b, red[1][w]);
+    }
+  }
+}
+
+template <bool STATS>
+__device__ __forceinline__ void flush_counters(unsigned long long* counters, int tid,
+                                               const uint32_t (&cnt)[kStatsPerTensor]) {
+  if constexpr (STATS) {
+#pragma unroll
+    for (int k = 0; k < kStatsPerTensor; k++) {
+      const uint32_t s = wave_sum(cnt[k]);
+      if ((threadIdx.x & 63) == 0 && s != 0)
+        atomicAdd(&counters[(int64_t)tid * kStatsPerTensor + k], (unsigned long long)s);
+    }
+  }
+}
+
+template <int MF, int VF, bool STATS>
+__device__ __forceinline__ void count_element(uint32_t (&cnt)[kStatsPerTensor], float m1, float v1,
+                                              float qm, float qv, uint32_t cm, uint32_t cv) {
+  if constexpr (STATS) {
+    cnt[kUnderM] += (m1 != 0.0f && (cm & 0x7Fu) == 0u);
+    cnt[kUnderV] += (v1 != 0.0f && (cv & 0x7Fu) == 0u);
+    cnt[kSatM] += (fabsf(qm) > Format<MF>::kMax);
+    cnt[kSatV] += (fabsf(qv) > Format<VF>::kMax);
+    cnt[kNonFinite] += (!isfinite(m1) || !isfinite(v1));
+  }
+}
+
+// Loads of one group of four consecutive elements.
+struct Group {
+  uint2 g;       // 4 bf16
+  uint32_t cm;   // 4 codes
+  uint32_t cv;   // 4 codes
+  float4 p;      // fp32 master (or 4 bf16 in .x/.y)
+};
+
+template <bool BF16P>
+__device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group& G, bool with_p) {
+  G.g = *reinterpret_cast<const uint2*>(d.g + i);
+  G.cm = *reinterpret_cast<const uint32_t*>(d.m + i);
+  G.cv = *reinterpret_cast<const uint32_t*>(d.v + i);
+  if (with_p) {
+    if constexpr (BF16P) {
+      const uint2 pb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.p) + i);
+      G.p = make_float4(__uint_as_float(pb.x), __uint_as_float(pb.y), 0.0f, 0.0f);
+    } else {
+      G.p = *reinterpret_cast<const float4*>(static_cast<const float*>(d.p) + i);
+    }
+  }
+}
+
+// Unpack 4 grads, 4 dequantized moments, and the fresh moments.
+template <int MF, int VF>
+__device__ __forceinline__ void fresh_moments(const StepConsts& c, const Group& G, float sm, float sv,
+                                              float (&m1)[4], float (&v1)[4]) {
+  float g[4] = {bf16_lo(G.g.x), bf16_hi(G.g.x), bf16_lo(G.g.y), bf16_hi(G.g.y)};
+  float m[4], v[4];
+  decode4<MF>(G.cm, m);
+  decode4<VF>(G.cv, v);
+#pragma unroll
+  for (int j = 0; j < 4; j++) moment_update(c, g[j], m[j] * sm, v[j] * sv, m1[j], v1[j]);
+}
+
+template <bool BF16P>
+__device__ __forceinline__ void unpack_p(const Group& G, float (&p)[4]) {
+  if constexpr (BF16P) {
+    const uint32_t a = __float_as_uint(G.p.x), b = __float_as_uint(G.p.y);
+    p[0] = bf16_lo(a); p[1] = bf16_hi(a); p[2] = bf16_lo(b); p[3] = bf16_hi(b);
+  } else {
+    p[0] = G.p.x; p[1] = G.p.y; p[2] = G.p.z; p[3] = G.p.w;
+  }
+}
+
+template <bool BF16P>
+__device__ __forceinline__ void store_p4(const TensorDesc& d, int64_t i, const float (&p)[4]) {
+  if constexpr (BF16P) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d.p) + i) =
+        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(d.p) + i) = make_float4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+template <bool BF16P>
+__device__ __forceinline__ float load_p1(const TensorDesc& d, int64_t i) {
+  if constexpr (BF16P) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(d.p)[i] << 16);
+  else return static_cast<const float*>(d.p)[i];
+}
+
+template <bool BF16P>
+__device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x) {
+  if constexpr (BF16P) static_cast<uint16_t*>(d.p)[i] = (uint16_t)f32_to_bf16_rne(x);
+  else static_cast<float*>(d.p)[i] = x;
+}
+
+// ------------------------------------------------------------------ pass 1
+
+template <int MF, int VF>
+__global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
+                                                   const int32_t* __restrict__ chunk_tid,
+                                                   uint32_t* __restrict__ amax, StepConsts c) {
+  const int tid = chunk_tid[blockIdx.x];
+  const TensorDesc d = descs[tid];
+  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
+  const int64_t end = min(start + kChunk, d.numel);
+  const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
+  const float sm = *d.sm, sv = *d.sv;
+  uint32_t am = 0, av = 0;
+
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUnroll) {
+    Group G[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) load_group<false>(d, i, G[u], false);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) {
+        float m1[4], v1[4];
+        fresh_moments<MF, VF>(c, G[u], sm, sv, m1, v1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          am = max(am, abs_bits(m1[j]));
+          av = max(av, abs_bits(v1[j]));
+        }
+      }
+    }
+  }
+  // ragged tail (< 4 elements at the end of a tensor)
+  if (gend + threadIdx.x < end) {
+    const int64_t i = gend + threadIdx.x;
+    const float g = __uint_as_float((uint32_t)d.g[i] << 16);
+    float m1, v1;
+    moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, m1, v1);
+    am = max(am, abs_bits(m1));
+    av = max(av, abs_bits(v1));
+  }
+  block_max2(am, av);
+  if (threadIdx.x == 0) {
+    if (am) atomicMax(&amax[2 * tid], am);
+    if (av) atomicMax(&amax[2 * tid + 1], av);
+  }
+}
+
+// ------------------------------------------------------------------ pass 2
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+__global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
+                                                     const int32_t* __restrict__ chunk_tid,
+                                                     const uint32_t* __restrict__ amax, StepConsts c,
+                                                     unsigned long long* __restrict__ counters) {
+  const int tid = chunk_tid[blockIdx.x];
+  const TensorDesc d = descs[tid];
+  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
+  const int64_t end = min(start + kChunk, d.numel);
+  const int64_t gend = start + ((end - start) & ~(int64_t)3);
+  const float sm = *d.sm, sv = *d.sv;
+  float nsm, ism, nsv, isv;
+  choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
+  choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
+  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
+
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUnroll) {
+    Group G[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) load_group<BF16P>(d, i, G[u], true);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) {
+        float m1[4], v1[4], p[4], qm[4], qv[4];
+        fresh_moments<MF, VF>(c, G[u], sm, sv, m1, v1);
+        unpack_p<BF16P>(G[u], p);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          p[j] = param_update(c, p[j], m1[j], v1[j]);
+          qm[j] = m1[j] * ism;
+          qv[j] = v1[j] * isv;
+        }
+        const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
+        const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
+        if constexpr (STATS) {
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
+        }
+        store_p4<BF16P>(d, i, p);
+        *reinterpret_cast<uint32_t*>(d.m + i) = wm;
+        *reinterpret_cast<uint32_t*>(d.v + i) = wv;
+      }
+    }
+  }
+  if (gend + threadIdx.x < end) {
+    const int64_t i = gend + threadIdx.x;
+    const float g = __uint_as_float((uint32_t)d.g[i] << 16);
+    float m1, v1;
+    moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, m1, v1);
+    const float p = param_update(c, load_p1<BF16P>(d, i), m1, v1);
+    const float qm = m1 * ism, qv = v1 * isv;
+    const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
+    count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
+    store_p1<BF16P>(d, i, p);
+    d.m[i] = (uint8_t)cm;
+    d.v[i] = (uint8_t)cv;
+  }
+  flush_counters<STATS>(counters, tid, cnt);
+}
+
+// ------------------------------------------------------------------ commit
+
+template <int MF, int VF, int SMODE>
+__global__ __launch_bounds__(kThreads) void k_commit(const TensorDesc* __restrict__ descs, int n,
+                                                     uint32_t* __restrict__ amax,
+                                                     uint32_t* __restrict__ last_amax) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const uint32_t am = amax[2 * t], av = amax[2 * t + 1];
+  const TensorDesc d = descs[t];
+  if (d.numel > 0) {
+    float s, inv;
+    choose_scale<MF, SMODE>(am, s, inv);
+    *d.sm = s;
+    choose_scale<VF, SMODE>(av, s, inv);
+    *d.sv = s;
+  }
+  last_amax[2 * t] = am;
+  last_amax[2 * t + 1] = av;
+  amax[2 * t] = 0u;
+  amax[2 * t + 1] = 0u;
+}
+
+// Zero the stats counters (and, in block mode, the amax used for stats).
+__global__ __launch_bounds__(kThreads) void k_reset(unsigned long long* __restrict__ counters, int64_t ncnt,
+                                                    uint32_t* __restrict__ amax, int64_t namax) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncnt; i += (int64_t)gridDim.x * blockDim.x)
+    counters[i] = 0ull;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < namax; i += (int64_t)gridDim.x * blockDim.x)
+    amax[i] = 0u;
+}
+
+// ------------------------------------------------------------ block-128 mode
+//
+// Wave layout: lanes 8b..8b+7 own block b of the wave's 8 consecutive blocks
+// (1024 elements).  Lane l of a block touches elements 32*j + 4*l .. +3 for
+// j = 0..3, so each access of the wave covers 32 contiguous elements of every
+// block.  The block amax is the max of the lane's 16 values, then a DPP max
+// over the 8 lanes.
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+__global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
+                                                    const int32_t* __restrict__ chunk_tid, StepConsts c,
+                                                    unsigned long long* __restrict__ counters,
+                                                    uint32_t* __restrict__ amax) {
+  const int tid = chunk_tid[blockIdx.x];
+  const TensorDesc d = descs[tid];
+  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
+  const int64_t end = min(start + kChunk, d.numel);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & 7, bw = lane >> 3;
+  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
+  uint32_t tam = 0, tav = 0;  // tensor-wide amax, for stats
+  float tsm = 0.0f, tsv = 0.0f;
+
+  for (int64_t tile = start; tile < end; tile += (int64_t)kBlock * 32) {
+    const int64_t b0 = tile + (int64_t)(wave * 8 + bw) * kBlock;  // this lane's block start
+    const bool exists = b0 < end;
+    const bool full = b0 + kBlock <= end;
+    const int64_t blk = b0 / kBlock;
+    float sm = 1.0f, sv = 1.0f;
+    if (exists) {
+      sm = d.sm[blk];
+      sv = d.sv[blk];
+    }
+    float m1[16], v1[16], p[16];
+    Group G[4];
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) load_group<BF16P>(d, b0 + 32 * j + 4 * sub, G[j], true);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float a[4], b[4], q[4];
+        fresh_moments<MF, VF>(c, G[j], sm, sv, a, b);
+        unpack_p<BF16P>(G[j], q);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          m1[4 * j + r] = a[r];
+          v1[4 * j + r] = b[r];
+          p[4 * j + r] = q[r];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int64_t i = b0 + 32 * j + 4 * sub + r;
+          float a = 0.0f, b = 0.0f, q = 0.0f;
+          if (exists && i < end) {
+            const float g = __uint_as_float((uint32_t)d.g[i] << 16);
+            moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, a, b);
+            q = load_p1<BF16P>(d, i);
+          }
+          m1[4 * j + r] = a;
+          v1[4 * j + r] = b;
+          p[4 * j + r] = q;
+        }
+      }
+    }
+    uint32_t am = 0, av = 0;
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      am = max(am, abs_bits(m1[k]));
+      av = max(av, abs_bits(v1[k]));
+    }
+    am = group8_max(am);
+    av = group8_max(av);
+    float nsm, ism, nsv, isv;
+    choose_scale<MF, SMODE>(am, nsm, ism);
+    choose_scale<VF, SMODE>(av, nsv, isv);
+    if constexpr (STATS) {
+      if (exists) {
+        tam = max(tam, am);
+        tav = max(tav, av);
+        tsm = fmaxf(tsm, nsm);
+        tsv = fmaxf(tsv, nsv);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k++) p[k] = param_update(c, p[k], m1[k], v1[k]);
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float qm[4], qv[4], pj[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          qm[r] = m1[4 * j + r] * ism;
+          qv[r] = v1[4 * j + r] * isv;
+          pj[r] = p[4 * j + r];
+        }
+        const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
+        const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
+        if constexpr (STATS) {
+#pragma unroll
+          for (int r = 0; r < 4; r++)
+            count_element<MF, VF, STATS>(cnt, m1[4 * j + r], v1[4 * j + r], qm[r], qv[r], wm >> (8 * r),
+                                         wv >> (8 * r));
+        }
+        const int64_t i = b0 + 32 * j + 4 * sub;
+        store_p4<BF16P>(d, i, pj);
+        *reinterpret_cast<uint32_t*>(d.m + i) = wm;
+        *reinterpret_cast<uint32_t*>(d.v + i) = wv;
+      }
+    } else if (exists) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int64_t i = b0 + 32 * j + 4 * sub + r;
+          if (i < end) {
+            const int k = 4 * j + r;
+            const float qm = m1[k] * ism, qv = v1[k] * isv;
+            const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
+            count_element<MF, VF, STATS>(cnt, m1[k], v1[k], qm, qv, cm, cv);
+            store_p1<BF16P>(d, i, p[k]);
+            d.m[i] = (uint8_t)cm;
+            d.v[i] = (uint8_t)cv;
+          }
+        }
+      }
+    }
+    if (exists && sub == 0) {
+      d.sm[blk] = nsm;
+      d.sv[blk] = nsv;
+    }
+  }
+  if constexpr (STATS) {
+    flush_counters<STATS>(counters, tid, cnt);
+    // tensor-wide amax for the stats (scales follow from it); non-negative floats order as u32
+    uint32_t sa = __float_as_uint(tsm), sb = __float_as_uint(tsv);
+    uint32_t a = tam, b = tav;
+    a = wave_max(a);
+    b = wave_max(b);
+    sa = wave_max(sa);
+    sb = wave_max(sb);
+    if (lane == 0) {
+      if (a) atomicMax(&amax[4 * tid], a);
+      if (b) atomicMax(&amax[4 * tid + 1], b);
+      if (sa) atomicMax(&amax[4 * tid + 2], sa);
+      if (sb) atomicMax(&amax[4 * tid + 3], sb);
+    }
+  }
+}
+
+// ------------------------------------------------------------- codec probes
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_encode(const float* __restrict__ x, uint8_t* __restrict__ out,
+                                                     int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n && (((uintptr_t)(x + i) | (uintptr_t)(out + i)) & 3) == 0 &&
+        ((uintptr_t)(x + i) & 15) == 0) {
+      const float4 v = *reinterpret_cast<const float4*>(x + i);
+      *reinterpret_cast<uint32_t*>(out + i) = encode4<FMT>(v.x, v.y, v.z, v.w);
+    } else {
+      for (int64_t k = i; k < n && k < i + 4; k++) out[k] = (uint8_t)encode1<FMT>(x[k]);
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_encode_bits(uint32_t start, int64_t count,
+                                                          uint8_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < count; i += stride) {
+    const uint32_t b = start + (uint32_t)i;
+    if (i + 4 <= count && (((uintptr_t)(out + i)) & 3) == 0) {
+      *reinterpret_cast<uint32_t*>(out + i) =
+          encode4<FMT>(__uint_as_float(b), __uint_as_float(b + 1u), __uint_as_float(b + 2u), __uint_as_float(b + 3u));
+    } else {
+      for (int64_t k = i; k < count && k < i + 4; k++)
+        out[k] = (uint8_t)encode1<FMT>(__uint_as_float(start + (uint32_t)k));
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__ codes, float* __restrict__ out,
+                                                     int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = decode1<FMT>(codes[i]);
+}
+
+// ================================================================== host side
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FP8ADAM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr)                                    \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr);    \
+  } while (0)
+
+constexpr int kMaxTimed = 4096;
+
+}  // namespace
+
+struct fp8adam_ctx {
+  int device = 0;
+  fp8adam_config cfg{};
+  int32_t n = 0;
+  int64_t nchunks = 0;
+  TensorDesc* d_desc = nullptr;
+  int32_t* d_chunk_tid = nullptr;
+  uint32_t* d_amax = nullptr;       // tensor mode: [n][2] running amax; block mode: [n][4] stats
+  uint32_t* d_last_amax = nullptr;  // tensor mode: [n][2] amax of the last step
+  unsigned long long* d_counters = nullptr;  // [n][5]
+  bool timing = false;
+  std::vector<hipEvent_t> ev;  // pairs
+  std::vector<int> ev_kind;
+  int ev_used = 0;
+};
+
+namespace {
+
+bool valid_fmt(int32_t f) { return f == FP8ADAM_E4M3 || f == FP8ADAM_E5M2; }
+
+int check_aligned(const void* p, const char* what, int32_t t) {
+  if (((uintptr_t)p & 15u) != 0)
+    return fail(FP8ADAM_EALIGN, std::string(what) + " of tensor " + std::to_string(t) + " is not 16-byte aligned");
+  return 0;
+}
+
+void free_ctx(fp8adam_ctx* c) {
+  if (!c) return;
+  if (c->d_desc) (void)hipFree(c->d_desc);
+  if (c->d_chunk_tid) (void)hipFree(c->d_chunk_tid);
+  if (c->d_amax) (void)hipFree(c->d_amax);
+  if (c->d_last_amax) (void)hipFree(c->d_last_amax);
+  if (c->d_counters) (void)hipFree(c->d_counters);
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  delete c;
+}
+
+int timed_begin(fp8adam_ctx* c, int kind, hipStream_t s, int* slot) {
+  *slot = -1;
+  if (!c->timing || c->ev_used >= kMaxTimed) return 0;
+  *slot = c->ev_used++;
+  c->ev_kind[*slot] = kind;
+  HIP_TRY(hipEventRecord(c->ev[2 * *slot], s));
+  return 0;
+}
+
+int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
+  if (slot < 0) return 0;
+  HIP_TRY(hipEventRecord(c->ev[2 * slot + 1], s));
+  return 0;
+}
+
+// ---- kernel dispatch over the template parameters ----
+
+template <int MF, int VF>
+void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, c->d_desc,
+                     c->d_chunk_tid, c->d_amax, k);
+}
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s,
+                     c->d_desc, c->d_chunk_tid, c->d_amax, k, c->d_counters);
+}
+
+template <int MF, int VF, int SMODE>
+void launch_commit(fp8adam_ctx* c, hipStream_t s) {
+  hipLaunchKernelGGL((k_commit<MF, VF, SMODE>), dim3((unsigned)((c->n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, c->d_desc, c->n, c->d_amax, c->d_last_amax);
+}
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s,
+                     c->d_desc, c->d_chunk_tid, k, c->d_counters, c->d_amax);
+}
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+int run_step_t(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  int slot;
+  if (STATS) {
+    const int64_t namax = c->cfg.granularity == FP8ADAM_SCALE_BLOCK128 ? 4 * (int64_t)c->n : 0;
+    if (int r = timed_begin(c, 4, s, &slot)) return r;
+    hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
+                       dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
+    if (int r = timed_end(c, slot, s)) return r;
+  }
+  if (c->nchunks > 0) {
+    if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
+      if (int r = timed_begin(c, 3, s, &slot)) return r;
+      launch_block<MF, VF, BF16P, STATS, SMODE>(c, k, s);
+      if (int r = timed_end(c, slot, s)) return r;
+    } else {
+      if (int r = timed_begin(c, 0, s, &slot)) return r;
+      launch_amax<MF, VF>(c, k, s);
+      if (int r = timed_end(c, slot, s)) return r;
+      if (int r = timed_begin(c, 1, s, &slot)) return r;
+      launch_update<MF, VF, BF16P, STATS, SMODE>(c, k, s);
+      if (int r = timed_end(c, slot, s)) return r;
+    }
+  }
+  if (c->cfg.granularity != FP8ADAM_SCALE_BLOCK128) {
+    if (int r = timed_begin(c, 2, s, &slot)) return r;
+    launch_commit<MF, VF, SMODE>(c, s);
+    if (int r = timed_end(c, slot, s)) return r;
+  }
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+template <int MF, int VF, bool BF16P, bool STATS>
+int run_step_s(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_t<MF, VF, BF16P, STATS, 0>(c, k, s)
+                                                 : run_step_t<MF, VF, BF16P, STATS, 1>(c, k, s);
+}
+
+template <int MF, int VF, bool BF16P>
+int run_step_b(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  return c->cfg.collect_stats ? run_step_s<MF, VF, BF16P, true>(c, k, s) : run_step_s<MF, VF, BF16P, false>(c, k, s);
+}
+
+template <int MF, int VF>
+int run_step_f(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  return c->cfg.master == FP8ADAM_MASTER_BF16 ? run_step_b<MF, VF, true>(c, k, s) : run_step_b<MF, VF, false>(c, k, s);
+}
+
+int run_step(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  const int mf = c->cfg.m_format, vf = c->cfg.v_format;
+  if (mf == 0 && vf == 1) return run_step_f<0, 1>(c, k, s);
+  if (mf == 1 && vf == 1) return run_step_f<1, 1>(c, k, s);
+  if (mf == 1 && vf == 0) return run_step_f<1, 0>(c, k, s);
+  return run_step_f<0, 0>(c, k, s);
+}
+
+unsigned probe_grid(int64_t n, int per_thread) {
+  const int64_t blocks = (n + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 65536));
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+
+extern "C" {
+
+const char* fp8adam_last_error(void) { return g_last_error.c_str(); }
+
+int fp8adam_runtime_version(int32_t* version) {
+  if (!version) return fail(FP8ADAM_EINVAL, "version is null");
+  int v = 0;
+  HIP_TRY(hipRuntimeGetVersion(&v));
+  *version = v;
+  return 0;
+}
+
+int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, const fp8adam_config* cfg,
+                 hipStream_t stream) {
+  try {
+    if (!out) return fail(FP8ADAM_EINVAL, "out is null");
+    *out = nullptr;
+    if (!tensors || !cfg) return fail(FP8ADAM_EINVAL, "tensors or cfg is null");
+    if (n <= 0) return fail(FP8ADAM_EINVAL, "n must be positive");
+    if (!valid_fmt(cfg->m_format) || !valid_fmt(cfg->v_format))
+      return fail(FP8ADAM_EINVAL, "m_format / v_format must be FP8ADAM_E4M3 or FP8ADAM_E5M2");
+    if (cfg->granularity != FP8ADAM_SCALE_TENSOR && cfg->granularity != FP8ADAM_SCALE_BLOCK128)
+      return fail(FP8ADAM_EINVAL, "bad granularity");
+    if (cfg->scale_mode != FP8ADAM_SCALE_POW2 && cfg->scale_mode != FP8ADAM_SCALE_AMAX)
+      return fail(FP8ADAM_EINVAL, "bad scale_mode");
+    if (cfg->master != FP8ADAM_MASTER_FP32 && cfg->master != FP8ADAM_MASTER_BF16)
+      return fail(FP8ADAM_EINVAL, "bad master dtype");
+
+    std::vector<TensorDesc> desc((size_t)n);
+    std::vector<int32_t> chunk_tid;
+    int64_t nchunks = 0;
+    for (int32_t t = 0; t < n; t++) {
+      const fp8adam_tensor& T = tensors[t];
+      if (T.numel < 0) return fail(FP8ADAM_EINVAL, "numel of tensor " + std::to_string(t) + " is negative");
+      if (T.numel > 0) {
+        if (!T.param || !T.grad || !T.m || !T.v || !T.m_scale || !T.v_scale)
+          return fail(FP8ADAM_EINVAL, "null pointer in tensor " + std::to_string(t));
+        if (int r = check_aligned(T.param, "param", t)) return r;
+        if (int r = check_aligned(T.grad, "grad", t)) return r;
+        if (int r = check_aligned(T.m, "m", t)) return r;
+        if (int r = check_aligned(T.v, "v", t)) return r;
+        if (!T.m_scale || ((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
+          return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
+      }
+      const int64_t nc = (T.numel + kChunk - 1) / kChunk;
+      desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
+                           T.numel, nchunks};
+      if (nchunks + nc > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "too many elements for one context");
+      for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
+      nchunks += nc;
+    }
+
+    fp8adam_ctx* c = new (std::nothrow) fp8adam_ctx();
+    if (!c) return fail(FP8ADAM_ENOMEM, "host allocation failed");
+    c->cfg = *cfg;
+    c->n = n;
+    c->nchunks = nchunks;
+    hipError_t e = hipGetDevice(&c->device);
+    const size_t namax = (size_t)n * 4;
+    if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * (size_t)n);
+    if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
+    if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
+    if (e == hipSuccess) e = hipMalloc(&c->d_last_amax, sizeof(uint32_t) * namax);
+    if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * (size_t)n, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && nchunks > 0)
+      e = hipMemcpyAsync(c->d_chunk_tid, chunk_tid.data(), sizeof(int32_t) * (size_t)nchunks, hipMemcpyHostToDevice,
+                         stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->d_amax, 0, sizeof(uint32_t) * namax, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->d_last_amax, 0, sizeof(uint32_t) * namax, stream);
+    if (e == hipSuccess)
+      e = hipMemsetAsync(c->d_counters, 0, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+      free_ctx(c);
+      return e == hipErrorOutOfMemory ? fail(FP8ADAM_ENOMEM, "device allocation failed")
+                                      : hip_fail(e, "fp8adam_init");
+    }
+    *out = c;
+    return 0;
+  } catch (const std::bad_alloc&) {
+    return fail(FP8ADAM_ENOMEM, "host allocation failed");
+  } catch (...) {
+    return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_init");
+  }
+}
+
+int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream) {
+  try {
+    if (!ctx || !hp) return fail(FP8ADAM_EINVAL, "ctx or hp is null");
+    if (hp->step < 1) return fail(FP8ADAM_EINVAL, "step must be >= 1");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+      return fail(FP8ADAM_EINVAL, "beta1 and beta2 must lie in [0, 1)");
+    if (!(hp->eps >= 0.0f) || !isfinite(hp->eps)) return fail(FP8ADAM_EINVAL, "eps must be finite and >= 0");
+    if (!isfinite(hp->lr) || !isfinite(hp->weight_decay)) return fail(FP8ADAM_EINVAL, "lr and weight_decay must be finite");
+    const double bc1 = 1.0 - pow((double)hp->beta1, (double)hp->step);
+    const double bc2 = 1.0 - pow((double)hp->beta2, (double)hp->step);
+    StepConsts k;
+    k.b1 = hp->beta1;
+    k.b2 = hp->beta2;
+    k.omb1 = 1.0f - hp->beta1;
+    k.omb2 = 1.0f - hp->beta2;
+    k.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+    k.step_size = (float)((double)hp->lr / bc1);
+    k.inv_bc2 = (float)(1.0 / bc2);
+    k.eps = hp->eps;
+    return run_step(ctx, k, stream);
+  } catch (...) {
+    return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step");
+  }
+}
+
+int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStream_t stream) {
+  try {
+    if (!ctx || !out_host) return fail(FP8ADAM_EINVAL, "ctx or out is null");
+    if (n != ctx->n) return fail(FP8ADAM_EINVAL, "n must equal the context's tensor count");
+    std::vector<uint32_t> amax((size_t)n * 4, 0u);
+    std::vector<unsigned long long> cnt((size_t)n * kStatsPerTensor, 0ull);
+    std::vector<TensorDesc> desc((size_t)n);
+    const bool block = ctx->cfg.granularity == FP8ADAM_SCALE_BLOCK128;
+    HIP_TRY(hipMemcpyAsync(amax.data(), block ? ctx->d_amax : ctx->d_last_amax,
+                           sizeof(uint32_t) * (size_t)n * (block ? 4 : 2), hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipMemcpyAsync(cnt.data(), ctx->d_counters, sizeof(unsigned long long) * cnt.size(),
+                           hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipMemcpyAsync(desc.data(), ctx->d_desc, sizeof(TensorDesc) * (size_t)n, hipMemcpyDeviceToHost, stream));
+    std::vector<float> sm((size_t)n, 0.0f), sv((size_t)n, 0.0f);
+    if (!block) {
+      for (int32_t t = 0; t < n; t++) {
+        if (desc[t].numel == 0) continue;
+        HIP_TRY(hipMemcpyAsync(&sm[t], desc[t].sm, sizeof(float), hipMemcpyDeviceToHost, stream));
+        HIP_TRY(hipMemcpyAsync(&sv[t], desc[t].sv, sizeof(float), hipMemcpyDeviceToHost, stream));
+      }
+    }
+    HIP_TRY(hipStreamSynchronize(stream));
+    for (int32_t t = 0; t < n; t++) {
+      fp8adam_stats_t& o = out_host[t];
+      auto f = [](uint32_t b) {
+        float x;
+        memcpy(&x, &b, 4);
+        return x;
+      };
+      if (block) {
+        o.amax_m = f(amax[4 * t]);
+        o.amax_v = f(amax[4 * t + 1]);
+        o.scale_m = f(amax[4 * t + 2]);
+        o.scale_v = f(amax[4 * t + 3]);
+      } else {
+        o.amax_m = f(amax[2 * t]);
+        o.amax_v = f(amax[2 * t + 1]);
+        o.scale_m = sm[t];
+        o.scale_v = sv[t];
+      }
+      o.underflow_m = (int64_t)cnt[kStatsPerTensor * t + kUnderM];
+      o.underflow_v = (int64_t)cnt[kStatsPerTensor * t + kUnderV];
+      o.saturated_m = (int64_t)cnt[kStatsPerTensor * t + kSatM];
+      o.saturated_v = (int64_t)cnt[kStatsPerTensor * t + kSatV];
+      o.nonfinite = (int64_t)cnt[kStatsPerTensor * t + kNonFinite];
+    }
+    return 0;
+  } catch (...) {
+    return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_stats");
+  }
+}
+
+void fp8adam_destroy(fp8adam_ctx* ctx) { free_ctx(ctx); }
+
+int64_t fp8adam_num_chunks(const fp8adam_ctx* ctx) { return ctx ? ctx->nchunks : -1; }
+
+int fp8adam_set_timing(fp8adam_ctx* ctx, int32_t enable) {
+  try {
+    if (!ctx) return fail(FP8ADAM_EINVAL, "ctx is null");
+    if (enable && ctx->ev.empty()) {
+      ctx->ev.resize(2 * kMaxTimed, nullptr);
+      ctx->ev_kind.resize(kMaxTimed, 0);
+      for (auto& e : ctx->ev) HIP_TRY(hipEventCreate(&e));
+    }
+    ctx->timing = enable != 0;
+    ctx->ev_used = 0;
+    return 0;
+  } catch (...) {
+    return fail(FP8ADAM_ENOMEM, "host allocation failed");
+  }
+}
+
+int fp8adam_kernel_times(fp8adam_ctx* ctx, double* total_ms, int32_t* count, int32_t max) {
+  if (!ctx || !total_ms || !count || max <= 0) return fail(FP8ADAM_EINVAL, "bad argument");
+  for (int32_t k = 0; k < max; k++) {
+    total_ms[k] = 0.0;
+    count[k] = 0;
+  }
+  for (int i = 0; i < ctx->ev_used; i++) {
+    HIP_TRY(hipEventSynchronize(ctx->ev[2 * i + 1]));
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, ctx->ev[2 * i], ctx->ev[2 * i + 1]));
+    const int kind = ctx->ev_kind[i];
+    if (kind < max) {
+      total_ms[kind] += ms;
+      count[kind] += 1;
+    }
+  }
+  ctx->ev_used = 0;
+  return 0;
+}
+
+int fp8adam_encode(int32_t fmt, const float* x, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (!valid_fmt(fmt) || n < 0 || (n > 0 && (!x || !out))) return fail(FP8ADAM_EINVAL, "bad argument");
+  if (n == 0) return 0;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_encode<0>, dim3(probe_grid(n, 4)), dim3(kThreads), 0, stream, x, out, n);
+  else
+    hipLaunchKernelGGL(k_encode<1>, dim3(probe_grid(n, 4)), dim3(kThreads), 0, stream, x, out, n);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_decode(int32_t fmt, const uint8_t* codes, float* out, int64_t n, hipStream_t stream) {
+  if (!valid_fmt(fmt) || n < 0 || (n > 0 && (!codes || !out))) return fail(FP8ADAM_EINVAL, "bad argument");
+  if (n == 0) return 0;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_decode<0>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, codes, out, n);
+  else
+    hipLaunchKernelGGL(k_decode<1>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, codes, out, n);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_encode_bits_range(int32_t fmt, uint32_t start, int64_t count, uint8_t* out, hipStream_t stream) {
+  if (!valid_fmt(fmt) || count < 0 || (count > 0 && !out) || count > (int64_t)(1ull << 32) - (int64_t)start)
+    return fail(FP8ADAM_EINVAL, "bad argument");
+  if (count == 0) return 0;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_encode_bits<0>, dim3(probe_grid(count, 4)), dim3(kThreads), 0, stream, start, count, out);
+  else
+    hipLaunchKernelGGL(k_encode_bits<1>, dim3(probe_grid(count, 4)), dim3(kThreads), 0, stream, start, count, out);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+"""The C-ABI library loads and exports every symbol the headers declare (CPU
+only: no compute call), and the oracle stays out of the product path."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import precision_adam_optimizer_amd as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols() -> set:
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fp8adam_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = declared_symbols()
+    for required in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error"):
+        assert required in names
+    assert names == set(pk.EXPORTS), f"binding and header disagree: {names ^ set(pk.EXPORTS)}"
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    if not os.path.exists(pk.LIB_PATH):
+        pytest.fail("libfp8adam.so is not built (run __graft_entry__.build())")
+    L = pk.load()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(fp8adam_\w+)\b", out))
+    assert declared_symbols() <= exported
+
+
+def test_library_targets_gfx950_and_uses_the_shared_hip_runtime():
+    out = subprocess.run(["readelf", "-d", pk.LIB_PATH], capture_output=True, text=True).stdout
+    assert "libamdhip64.so" in out
+    blob = open(pk.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_error_paths_without_a_gpu():
+    """Argument errors are reported through return codes and a message, with
+    no device work (these return before any HIP call)."""
+    L = pk.load()
+    h = ctypes.c_void_p()
+    cfg = pk.ConfigArg(0, 1, 0, 0, 0, 0)
+    rc = L.fp8adam_init(ctypes.byref(h), None, 1, ctypes.byref(cfg), None)
+    assert rc == -1 and "null" in pk.fp8adam_last_error()
+    arr = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10))
+    bad = pk.ConfigArg(7, 1, 0, 0, 0, 0)
+    assert L.fp8adam_init(ctypes.byref(h), arr, 1, ctypes.byref(bad), None) == -1
+    arr2 = (pk.TensorArg * 1)(pk.TensorArg(16 + 4, 32, 48, 64, 80, 96, 10))
+    assert L.fp8adam_init(ctypes.byref(h), arr2, 1, ctypes.byref(cfg), None) == -2
+    assert "aligned" in pk.fp8adam_last_error()
+    assert L.fp8adam_init(ctypes.byref(h), arr, 0, ctypes.byref(cfg), None) == -1
+    hp = pk.HParamsArg(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    assert L.fp8adam_step(None, ctypes.byref(hp), None) == -1
+    assert L.fp8adam_encode(3, None, None, 10, None) == -1
+    assert L.fp8adam_encode_bits_range(0, 10, (1 << 32), None, None) == -1
+    assert L.fp8adam_num_chunks(None) == -1
+
+
+def test_product_path_does_not_import_the_oracle():
+    for path in glob.glob(os.path.join(ROOT, "precision_adam_optimizer_amd", "**", "*"), recursive=True):
+        if path.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(path).read()
+            assert "import oracle" not in text and "from oracle" not in text, path
+            assert "liboracle" not in text and "fp8adam_oracle" not in text, path

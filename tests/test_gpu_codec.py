@@ -1,0 +1,78 @@
+"""Device FP8 codec (the gfx950 packed converts with the saturating clamp, as
+used by the step kernels) against the oracle codec: all 256 codes decoded,
+all 2^32 fp32 bit patterns encoded, through the C ABI."""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_adam_optimizer_amd as pk
+from tests.gpu_util import pool_size
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_decode_all_codes(fmt):
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    pk.fp8adam_decode(fmt, codes, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.decode(fmt, np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = ~np.isnan(want)
+    assert np.array_equal(got[fin].view(np.uint32), want[fin].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_encode_special_values(fmt):
+    vals = np.array([0.0, -0.0, 1e-45, -1e-45, 0.96875, 0.9375, 1.0625, 1.1875, 2.0 ** -10, 1.5 * 2.0 ** -9,
+                     1e-4, 448.0, 449.0, 464.0, 480.0, 57344.0, 61440.0, 1e30, -1e30, np.inf, -np.inf,
+                     2.0 ** -17, 3 * 2.0 ** -17, 1.17549435e-38, -1.17549435e-38], dtype=np.float32)
+    x = torch.from_numpy(vals).cuda()
+    out = torch.empty(vals.size, dtype=torch.uint8, device="cuda")
+    pk.fp8adam_encode(fmt, x, out)
+    torch.cuda.synchronize()
+    assert list(out.cpu().numpy()) == list(oracle.encode(fmt, vals))
+
+
+NAN_RANGES = ((0x7F800001, 0x80000000), (0xFF800001, 0x100000000))  # [lo, hi) of NaN bit patterns
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_encode_all_fp32_bit_patterns(fmt):
+    """Every fp32 pattern except NaNs (outside the contract): device code ==
+    oracle code.  Covers rounding, ties, subnormals, signed zeros, saturation
+    and the byte order of the packed converts."""
+    slice_len = 1 << 28
+    dev = torch.empty(slice_len, dtype=torch.uint8, device="cuda")
+    host = torch.empty(slice_len, dtype=torch.uint8, pin_memory=True)
+    parts = 16  # slices of the oracle's share, run on pool_size() threads
+    step = slice_len // parts
+
+    def oracle_part(start):
+        return oracle.encode_bits_range(fmt, start, step)
+
+    mismatches, first = 0, None
+    for s in range(0, 1 << 32, slice_len):
+        pk.fp8adam_encode_bits_range(fmt, s, slice_len, dev)
+        host.copy_(dev)
+        torch.cuda.synchronize()
+        got = host.numpy()
+        with cf.ThreadPoolExecutor(pool_size()) as ex:
+            want = np.concatenate(list(ex.map(oracle_part, [s + k * step for k in range(parts)])))
+        diff = got != want
+        for lo, hi in NAN_RANGES:
+            a, b = max(lo, s) - s, min(hi, s + slice_len) - s
+            if a < b:
+                diff[a:b] = False
+        if diff.any():
+            mismatches += int(diff.sum())
+            if first is None:
+                i = int(np.nonzero(diff)[0][0])
+                first = (s + i, int(got[i]), int(want[i]))
+    assert mismatches == 0, f"{mismatches} mismatches; first bits {first[0]:#010x}: gpu {first[1]:#04x} oracle {first[2]:#04x}"

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP step (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar (see tests/gpu_util.py): FP8 codes and scales bit-exact; fp32 weights
+within 1e-6 of max(|p_ref|, |p_old|); bf16 weights equal except <= 1 ulp on
+<= 1e-3 of the elements; stats counts and amax equal.
+
+Sizes: small ragged multi-tensor lists (1 element up to several chunks, tails
+of 1-3 elements, partial 128-blocks) over every format pair, granularity,
+scale mode, master dtype and stats setting; then the five synthetic workloads
+at full size (flat 1M, Llama-2-100M, 7B per-tensor, 7B block-128, 13B bf16)
+in the launch configuration the benchmark times, checked tensor by tensor on
+a sample of whole tensors plus size-independent properties on every tensor.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_adam_optimizer_amd as pk
+import workloads
+from tests.gpu_util import (OracleState, compare_tensor, np_host, oracle_config, random_grad, run_pool,
+                            upload_params)
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 2, 3, 4, 5, 7, 127, 128, 129, 255, 1000, 1023, 1024, 1025, 4095, 4096, 4097, 16383, 16384,
+         16385, 16387, 40000, 65539]
+FORMATS = [("e4m3", "e5m2"), ("e5m2", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e4m3")]
+COMBOS = list(itertools.product(FORMATS, ["tensor", "block128"], ["pow2", "amax"], ["fp32", "bf16"]))
+
+
+def _compare_stats(name, got: dict, want: dict, granularity: str):
+    for k in ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite"):
+        assert got[k] == want[k], f"{name}: stat {k} gpu {got[k]} oracle {want[k]}"
+    for k in ("amax_m", "amax_v", "scale_m", "scale_v"):
+        assert np.float32(got[k]).view(np.uint32) == np.float32(want[k]).view(np.uint32), \
+            f"{name}: stat {k} gpu {got[k]!r} oracle {want[k]!r}"
+
+
+def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init, sizes=SIZES, steps=3,
+              lr=3e-4, seed=0):
+    m_fmt, v_fmt = fmts
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    params = []
+    for n in sizes:
+        p = torch.randn(n, generator=gen, device=dev) * 0.02
+        params.append(p.to(torch.bfloat16) if master == "bf16" else p)
+    grads = [torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in sizes]
+    nb = [1 if granularity == "tensor" else -(-n // 128) for n in sizes]
+    state = ([], [], [], [])
+    for i, n in enumerate(sizes):
+        if random_init:
+            cm, cv, sm, sv = workloads.random_state(n, dev, seed * 1000 + i, workloads_fmt(m_fmt),
+                                                    workloads_fmt(v_fmt), nblocks=nb[i], scale_exp=(-24, 2),
+                                                    pow2=(scale_mode == "pow2"))
+        else:
+            cm, cv, sm, sv = workloads.make_state(n, dev, nblocks=nb[i])
+        for lst, x in zip(state, (cm, cv, sm, sv)):
+            lst.append(x)
+    host = [OracleState(np_host(params[i]), np_host(state[0][i]), np_host(state[1][i]), np_host(state[2][i]),
+                        np_host(state[3][i])) for i in range(len(sizes))]
+    opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, granularity=granularity,
+                      scale_mode=scale_mode, collect_stats=collect_stats, state=state)
+    try:
+        for t in range(1, steps + 1):
+            for i, n in enumerate(sizes):
+                grads[i].copy_(random_grad(n, seed * 7919 + t * 101 + i, dev))
+            opt.step(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            torch.cuda.synchronize()
+            h = oracle.Hyper(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            cfg = oracle_config(h, m_fmt, v_fmt, granularity, scale_mode, master)
+            gstats = opt.stats() if collect_stats else None
+            for i, n in enumerate(sizes):
+                host[i].step(cfg, np_host(grads[i]))
+                name = f"tensor {i} (numel {n}) step {t}"
+                compare_tensor(name, host[i], np_host(params[i]), np_host(opt.m[i]), np_host(opt.v[i]),
+                               np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), master)
+                if collect_stats:
+                    _compare_stats(name, gstats[i], host[i].stats, granularity)
+                upload_params(params[i], host[i])
+    finally:
+        opt.close()
+
+
+def workloads_fmt(f):
+    return 0 if f == "e4m3" else 1
+
+
+@pytest.mark.parametrize("combo", COMBOS, ids=[f"{a}-{b}_{g}_{s}_{m}" for (a, b), g, s, m in COMBOS])
+def test_small_ragged_lists(combo):
+    fmts, gran, smode, master = combo
+    k = COMBOS.index(combo)
+    run_small(fmts, gran, smode, master, collect_stats=(k % 2 == 0), random_init=(k % 4 < 2), seed=k)
+
+
+@pytest.mark.parametrize("gran", ["tensor", "block128"])
+def test_small_large_learning_rate_and_stats(gran):
+    """Big updates (lr 1e-2) from a random mid-training state, stats on."""
+    run_small(("e4m3", "e5m2"), gran, "pow2", "fp32", collect_stats=True, random_init=True, lr=1e-2,
+              steps=4, seed=99)
+
+
+def test_zero_sized_tensor_in_list():
+    dev = torch.device("cuda")
+    sizes = [10, 0, 5]
+    params = [torch.randn(n, device=dev) * 0.02 for n in sizes]
+    grads = [random_grad(n, 3 + n, dev) for n in sizes]
+    host = [OracleState(np_host(p), np.zeros(n, np.uint8), np.zeros(n, np.uint8), np.ones(1, np.float32),
+                        np.ones(1, np.float32)) for p, n in zip(params, sizes)]
+    opt = pk.FP8AdamW(params, grads)
+    opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0, step=1)
+    torch.cuda.synchronize()
+    cfg = oracle_config(oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, step=1), "e4m3", "e5m2",
+                        "tensor", "pow2", "fp32")
+    for i, n in enumerate(sizes):
+        host[i].step(cfg, np_host(grads[i]))
+        compare_tensor(f"tensor {i}", host[i], np_host(params[i]), np_host(opt.m[i]), np_host(opt.v[i]),
+                       np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), "fp32")
+    opt.close()
+
+
+# ------------------------------------------------------------ full-size lists
+
+def _top_code(fmt: str) -> int:
+    """Code of FMAX/2: the amax element of a tensor must land at or above it."""
+    return int(oracle.encode(fmt, [oracle.format_max(fmt) / 2])[0])
+
+
+def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0, collect_stats: bool = False):
+    dev = torch.device("cuda")
+    shapes = w.shapes
+    params = [workloads.make_param(w, i, s, dev, base_seed) for i, (_, s) in enumerate(shapes)]
+    grads = [torch.empty(workloads.numel(s), dtype=torch.bfloat16, device=dev) for _, s in shapes]
+    host = {}
+    for i in sample:
+        n = workloads.numel(shapes[i][1])
+        nb = 1 if w.granularity == "tensor" else -(-n // 128)
+        host[i] = OracleState(np_host(params[i]), np.zeros(n, np.uint8), np.zeros(n, np.uint8),
+                              np.ones(nb, np.float32), np.ones(nb, np.float32))
+    opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
+                      collect_stats=collect_stats)
+    top_m, top_v = _top_code(w.m_fmt), _top_code(w.v_fmt)
+    all_stats = []
+    try:
+        for t in range(1, steps + 1):
+            for i, (_, s) in enumerate(shapes):
+                grads[i].copy_(workloads.make_grad(w, i, s, t, dev, base_seed))
+            opt.step(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
+            torch.cuda.synchronize()
+            h = oracle.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
+            cfg = oracle_config(h, w.m_fmt, w.v_fmt, w.granularity, "pow2", w.master)
+
+            def check(i):
+                st = host[i]
+                st.step(cfg, np_host(grads[i]))
+                compare_tensor(f"{shapes[i][0]} step {t}", st, np_host(params[i]), np_host(opt.m[i]),
+                               np_host(opt.v[i]), np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), w.master)
+                upload_params(params[i], st)
+                return st.stats
+
+            ostats = dict(zip(sample, run_pool(check, sample)))
+            gstats = opt.stats() if collect_stats else None
+            if collect_stats:
+                for i in sample:
+                    _compare_stats(f"{shapes[i][0]} step {t}", gstats[i], ostats[i], w.granularity)
+                all_stats.append(gstats)
+            # properties of every tensor at any size
+            for i in range(len(shapes)):
+                assert not bool((opt.v[i] & 0x80).any()), f"{shapes[i][0]}: negative v code"
+                if w.granularity == "tensor":
+                    mm = int((opt.m[i] & 0x7F).max())
+                    vv = int((opt.v[i] & 0x7F).max())
+                    # skipped only for an all-zero moment (scale 1) or a clamped tiny scale
+                    if float(opt.m_scale[i]) > 2.0 ** -126 and not (mm == 0 and float(opt.m_scale[i]) == 1.0):
+                        assert mm >= top_m, f"{shapes[i][0]}: m amax not in the top binade"
+                    if float(opt.v_scale[i]) > 2.0 ** -126 and not (vv == 0 and float(opt.v_scale[i]) == 1.0):
+                        assert vv >= top_v, f"{shapes[i][0]}: v amax not in the top binade"
+    finally:
+        opt.close()
+        del params, grads
+        torch.cuda.empty_cache()
+    return all_stats
+
+
+def _layer_indices(n_layers: int, layers: list) -> list:
+    idx = [0]
+    for L in layers:
+        idx += list(range(1 + 9 * L, 1 + 9 * (L + 1)))
+    return idx
+
+
+@pytest.mark.timeout(300)
+def test_flat_1m_ten_steps():
+    run_full(workloads.flat_1m(), steps=10, sample=[0], collect_stats=True)
+
+
+@pytest.mark.timeout(600)
+def test_llama2_100m_all_format_pairs():
+    """Every tensor of the Llama-2-100M-shaped list checked against the oracle;
+    20 steps for (E4M3, E5M2), 3 for the other pairs; underflow and
+    saturation counts equal; v in E4M3 underflows far more than v in E5M2."""
+    under_v = {}
+    for m_fmt, v_fmt in FORMATS:
+        w = workloads.llama2_100m(m_fmt, v_fmt)
+        steps = 20 if (m_fmt, v_fmt) == ("e4m3", "e5m2") else 3
+        stats = run_full(w, steps=steps, sample=list(range(len(w.shapes))), collect_stats=True)
+        under_v[(m_fmt, v_fmt)] = sum(s["underflow_v"] for s in stats[2])
+        assert all(s["saturated_m"] == 0 and s["saturated_v"] == 0 for st in stats for s in st)
+    assert under_v[("e4m3", "e4m3")] > 20 * max(1, under_v[("e4m3", "e5m2")])
+    assert under_v[("e5m2", "e4m3")] > 20 * max(1, under_v[("e5m2", "e5m2")])
+
+
+@pytest.mark.timeout(900)
+def test_llama2_7b_per_tensor_full_size():
+    w = workloads.llama2_7b()
+    n = len(w.shapes)
+    sample = _layer_indices(32, [0, 17, 31]) + [n - 2, n - 1]
+    run_full(w, steps=2, sample=sample)
+
+
+@pytest.mark.timeout(900)
+def test_llama2_7b_block128_full_size():
+    w = workloads.llama2_7b_block128()
+    n = len(w.shapes)
+    sample = _layer_indices(32, [0, 31]) + [n - 2, n - 1]
+    run_full(w, steps=2, sample=sample, collect_stats=True)
+
+
+@pytest.mark.timeout(1200)
+def test_llama2_13b_bf16_master_full_size():
+    w = workloads.llama2_13b_bf16()
+    n = len(w.shapes)
+    sample = _layer_indices(40, [0]) + [n - 2, n - 1]
+    run_full(w, steps=5, sample=sample)
