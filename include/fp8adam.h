@@ -154,7 +154,7 @@ int fp8adam_encode_bits_range(int32_t fmt, uint32_t start, int64_t count, uint8_
 int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 
 /* Per-kernel timing since the last call (or since timing was enabled):
- * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale commit,
+ * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset), total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);

@@ -26,7 +26,7 @@ _FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
 _GRAN = {"tensor": SCALE_TENSOR, "block128": SCALE_BLOCK128}
 _SMODE = {"pow2": SCALE_POW2, "amax": SCALE_AMAX}
 
-KERNEL_KINDS = ("amax_pass", "update_pass", "scale_commit", "block128_pass", "stats_reset")
+KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",

@@ -9,15 +9,19 @@
 // Device work per step:
 //   per-tensor scales (two streaming passes over a chunked multi-tensor list)
 //     k_amax    : dequantize, update m and v in registers, max|m'| / max v'
-//                 per chunk -> one atomic max per tensor per work-group
-//     k_update  : recompute m', v'; choose the new scales from the amax;
-//                 update p; requantize m', v' with saturation; write p, m, v
-//     k_commit  : new scales into the caller's scale slots, amax reset
+//                 per chunk (wave DPP/shuffle max, then LDS) -> one partial
+//                 per chunk, no atomics
+//     k_reduce  : one work-group per tensor: max over the tensor's partials,
+//                 stage the old scales, write the new scales into the
+//                 caller's slots (and clear the tensor's stats counters)
+//     k_update  : recompute m', v' with the staged old scales; update p;
+//                 requantize m', v' with the new scales and saturation
 //   per-128-element scales (one streaming pass)
 //     k_block   : eight lanes own one 128-element block; the block amax is a
 //                 3-step DPP max, then update and requantize as above
-// Each work-group owns one chunk of kChunk elements of one tensor; the chunk
-// table is built once at init.  Loads and stores are dword-granular per lane
+// The chunk table (built once at init) cuts every tensor into chunks of
+// kChunk elements; an amax-pass work-group owns one chunk, an update- or
+// block-pass work-group owns one of the kSplit equal parts of a chunk.  Loads and stores are dword-granular per lane
 // and contiguous across the wave (fp32 master: 16 B per lane).
 #include <hip/hip_runtime.h>
 
@@ -38,16 +42,52 @@ using namespace fp8adam;
 
 namespace {
 
-constexpr int kThreads = 256;                   // 4 waves of 64
-constexpr int kGroup = 4;                       // consecutive elements per lane per access
-constexpr int kSubTile = kThreads * kGroup;     // 1024 elements per work-group access
-constexpr int kUnroll = 4;                      // accesses in flight per lane
-constexpr int64_t kChunk = 16384;               // elements per work-group (multiple of 4096)
-constexpr int kBlock = 128;                     // block-scale granularity
+// Launch-shape tunables (compile-time; the defaults are the measured best on MI355X).
+#ifndef FP8ADAM_CHUNK
+#define FP8ADAM_CHUNK 32768  // elements per chunk = per amax-pass work-group
+#endif
+#ifndef FP8ADAM_SPLIT
+#define FP8ADAM_SPLIT 8      // update / block work-groups per chunk
+#endif
+#ifndef FP8ADAM_AMAX_UNROLL
+#define FP8ADAM_AMAX_UNROLL 8
+#endif
+#ifndef FP8ADAM_UPDATE_UNROLL
+#define FP8ADAM_UPDATE_UNROLL 4
+#endif
+// 1: non-temporal loads / stores (each byte is touched once per pass)
+#ifndef FP8ADAM_NT_AMAX
+#define FP8ADAM_NT_AMAX 1
+#endif
+#ifndef FP8ADAM_NT_UPDATE_LD
+#define FP8ADAM_NT_UPDATE_LD 1
+#endif
+#ifndef FP8ADAM_NT_UPDATE_ST
+#define FP8ADAM_NT_UPDATE_ST 1
+#endif
+#ifndef FP8ADAM_NT_BLOCK_LD
+#define FP8ADAM_NT_BLOCK_LD 0
+#endif
+#ifndef FP8ADAM_NT_BLOCK_ST
+#define FP8ADAM_NT_BLOCK_ST 0
+#endif
+
+constexpr int kThreads = 256;                     // 4 waves of 64
+constexpr int kGroup = 4;                         // consecutive elements per lane per access
+constexpr int kSubTile = kThreads * kGroup;       // 1024 elements per work-group access
+constexpr int kAmaxUnroll = FP8ADAM_AMAX_UNROLL;  // accesses in flight per lane, amax pass
+constexpr int kUpdUnroll = FP8ADAM_UPDATE_UNROLL; // accesses in flight per lane, update pass
+constexpr int64_t kChunk = FP8ADAM_CHUNK;         // elements per chunk
+constexpr int kSplit = FP8ADAM_SPLIT;
+constexpr int64_t kPart = kChunk / kSplit;        // elements per update / block work-group
+constexpr int kBlock = 128;                       // block-scale granularity
+constexpr int kReduceThreads = 1024;              // one work-group per tensor in k_reduce
 constexpr int kStatsPerTensor = 5;
 
-static_assert(kChunk % (kSubTile * kUnroll) == 0, "chunk must hold whole unrolled tiles");
-static_assert(kChunk % (kBlock * 32) == 0, "chunk must hold whole block tiles");
+static_assert(kChunk % kSplit == 0, "chunk must split evenly");
+static_assert(kChunk % (kSubTile * kAmaxUnroll) == 0, "chunk must hold whole unrolled amax tiles");
+static_assert(kPart % (kSubTile * kUpdUnroll) == 0, "part must hold whole unrolled update tiles");
+static_assert(kPart % (kBlock * 32) == 0, "part must hold whole block tiles");
 
 struct TensorDesc {
   void* p;
@@ -128,25 +168,41 @@ __device__ __forceinline__ void count_element(uint32_t (&cnt)[kStatsPerTensor], 
   }
 }
 
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
+
+// Streamed loads and stores (optionally non-temporal: the data is touched once per pass).
+template <typename T, bool NT>
+__device__ __forceinline__ T ld_stream(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
+template <typename T, bool NT>
+__device__ __forceinline__ void st_stream(void* p, T x) {
+  if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<T*>(p));
+  else *reinterpret_cast<T*>(p) = x;
+}
+
 // Loads of one group of four consecutive elements.
 struct Group {
-  uint2 g;       // 4 bf16
+  vu2 g;         // 4 bf16
   uint32_t cm;   // 4 codes
   uint32_t cv;   // 4 codes
-  float4 p;      // fp32 master (or 4 bf16 in .x/.y)
+  vf4 p;         // fp32 master (or 4 bf16 in .x/.y)
 };
 
-template <bool BF16P>
+template <bool BF16P, bool NT>
 __device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group& G, bool with_p) {
-  G.g = *reinterpret_cast<const uint2*>(d.g + i);
-  G.cm = *reinterpret_cast<const uint32_t*>(d.m + i);
-  G.cv = *reinterpret_cast<const uint32_t*>(d.v + i);
+  G.g = ld_stream<vu2, NT>(d.g + i);
+  G.cm = ld_stream<uint32_t, NT>(d.m + i);
+  G.cv = ld_stream<uint32_t, NT>(d.v + i);
   if (with_p) {
     if constexpr (BF16P) {
-      const uint2 pb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.p) + i);
-      G.p = make_float4(__uint_as_float(pb.x), __uint_as_float(pb.y), 0.0f, 0.0f);
+      const vu2 pb = ld_stream<vu2, NT>(static_cast<const uint16_t*>(d.p) + i);
+      G.p = vf4{__uint_as_float(pb.x), __uint_as_float(pb.y), 0.0f, 0.0f};
     } else {
-      G.p = *reinterpret_cast<const float4*>(static_cast<const float*>(d.p) + i);
+      G.p = ld_stream<vf4, NT>(static_cast<const float*>(d.p) + i);
     }
   }
 }
@@ -173,13 +229,12 @@ __device__ __forceinline__ void unpack_p(const Group& G, float (&p)[4]) {
   }
 }
 
-template <bool BF16P>
+template <bool BF16P, bool NT>
 __device__ __forceinline__ void store_p4(const TensorDesc& d, int64_t i, const float (&p)[4]) {
   if constexpr (BF16P) {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d.p) + i) =
-        make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+    st_stream<vu2, NT>(static_cast<uint16_t*>(d.p) + i, vu2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
   } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(d.p) + i) = make_float4(p[0], p[1], p[2], p[3]);
+    st_stream<vf4, NT>(static_cast<float*>(d.p) + i, vf4{p[0], p[1], p[2], p[3]});
   }
 }
 
@@ -200,7 +255,7 @@ __device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x
 template <int MF, int VF>
 __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ chunk_tid,
-                                                   uint32_t* __restrict__ amax, StepConsts c) {
+                                                   uint2* __restrict__ partial, StepConsts c) {
   const int tid = chunk_tid[blockIdx.x];
   const TensorDesc d = descs[tid];
   const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
@@ -209,15 +264,15 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
   const float sm = *d.sm, sv = *d.sv;
   uint32_t am = 0, av = 0;
 
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUnroll) {
-    Group G[kUnroll];
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
+    Group G[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<false>(d, i, G[u], false);
+      if (i < gend) load_group<false, FP8ADAM_NT_AMAX != 0>(d, i, G[u], false);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
       if (i < gend) {
         float m1[4], v1[4];
@@ -240,9 +295,60 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
     av = max(av, abs_bits(v1));
   }
   block_max2(am, av);
+  if (threadIdx.x == 0) partial[blockIdx.x] = make_uint2(am, av);
+}
+
+// ------------------------------------------------------------------ reduce
+//
+// One work-group per tensor: amax over the tensor's chunk partials (unsigned
+// max of fp32 bit patterns of non-negative values: exact and order-free),
+// then the old scales are staged for the update pass and the new scales are
+// written into the caller's slots.  Non-finite amax (NaN/Inf bit patterns
+// are the largest) gives scale 1.
+
+template <int MF, int VF, int SMODE, bool STATS>
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __restrict__ descs,
+                                                           const uint2* __restrict__ partial,
+                                                           uint32_t* __restrict__ amax,
+                                                           float* __restrict__ old_scale,
+                                                           unsigned long long* __restrict__ counters) {
+  const int t = blockIdx.x;
+  const TensorDesc d = descs[t];
+  const int64_t nc = (d.numel + kChunk - 1) / kChunk;
+  uint32_t am = 0, av = 0;
+  for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) {
+    const uint2 pv = partial[d.chunk0 + k];
+    am = max(am, pv.x);
+    av = max(av, pv.y);
+  }
+  __shared__ uint32_t red[2][kReduceThreads / 64];
+  am = wave_max(am);
+  av = wave_max(av);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    red[0][wave] = am;
+    red[1][wave] = av;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    if (am) atomicMax(&amax[2 * tid], am);
-    if (av) atomicMax(&amax[2 * tid + 1], av);
+    for (int w = 1; w < kReduceThreads / 64; w++) {
+      am = max(am, red[0][w]);
+      av = max(av, red[1][w]);
+    }
+    amax[2 * t] = am;
+    amax[2 * t + 1] = av;
+    if (d.numel > 0) {
+      old_scale[2 * t] = *d.sm;
+      old_scale[2 * t + 1] = *d.sv;
+      float s, inv;
+      choose_scale<MF, SMODE>(am, s, inv);
+      *d.sm = s;
+      choose_scale<VF, SMODE>(av, s, inv);
+      *d.sv = s;
+    }
+  }
+  if constexpr (STATS) {
+    if (threadIdx.x < kStatsPerTensor) counters[(int64_t)t * kStatsPerTensor + threadIdx.x] = 0ull;
   }
 }
 
@@ -251,28 +357,31 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
                                                      const int32_t* __restrict__ chunk_tid,
-                                                     const uint32_t* __restrict__ amax, StepConsts c,
+                                                     const uint32_t* __restrict__ amax,
+                                                     const float* __restrict__ old_scale, StepConsts c,
                                                      unsigned long long* __restrict__ counters) {
-  const int tid = chunk_tid[blockIdx.x];
+  const int64_t chunk = blockIdx.x / kSplit;
+  const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
-  const int64_t end = min(start + kChunk, d.numel);
+  const int64_t start = (chunk - d.chunk0) * kChunk + (int64_t)(blockIdx.x % kSplit) * kPart;
+  const int64_t end = min(start + kPart, d.numel);
+  if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
-  const float sm = *d.sm, sv = *d.sv;
+  const float sm = old_scale[2 * tid], sv = old_scale[2 * tid + 1];
   float nsm, ism, nsv, isv;
   choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
   choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
 
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUnroll) {
-    Group G[kUnroll];
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUpdUnroll) {
+    Group G[kUpdUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kUpdUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P>(d, i, G[u], true);
+      if (i < gend) load_group<BF16P, FP8ADAM_NT_UPDATE_LD != 0>(d, i, G[u], true);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
+    for (int u = 0; u < kUpdUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
       if (i < gend) {
         float m1[4], v1[4], p[4], qm[4], qv[4];
@@ -291,9 +400,9 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
           for (int j = 0; j < 4; j++)
             count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
         }
-        store_p4<BF16P>(d, i, p);
-        *reinterpret_cast<uint32_t*>(d.m + i) = wm;
-        *reinterpret_cast<uint32_t*>(d.v + i) = wv;
+        store_p4<BF16P, FP8ADAM_NT_UPDATE_ST != 0>(d, i, p);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(d.m + i, wm);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(d.v + i, wv);
       }
     }
   }
@@ -311,29 +420,6 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     d.v[i] = (uint8_t)cv;
   }
   flush_counters<STATS>(counters, tid, cnt);
-}
-
-// ------------------------------------------------------------------ commit
-
-template <int MF, int VF, int SMODE>
-__global__ __launch_bounds__(kThreads) void k_commit(const TensorDesc* __restrict__ descs, int n,
-                                                     uint32_t* __restrict__ amax,
-                                                     uint32_t* __restrict__ last_amax) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
-  const uint32_t am = amax[2 * t], av = amax[2 * t + 1];
-  const TensorDesc d = descs[t];
-  if (d.numel > 0) {
-    float s, inv;
-    choose_scale<MF, SMODE>(am, s, inv);
-    *d.sm = s;
-    choose_scale<VF, SMODE>(av, s, inv);
-    *d.sv = s;
-  }
-  last_amax[2 * t] = am;
-  last_amax[2 * t + 1] = av;
-  amax[2 * t] = 0u;
-  amax[2 * t + 1] = 0u;
 }
 
 // Zero the stats counters (and, in block mode, the amax used for stats).
@@ -358,10 +444,11 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
                                                     const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                     unsigned long long* __restrict__ counters,
                                                     uint32_t* __restrict__ amax) {
-  const int tid = chunk_tid[blockIdx.x];
+  const int64_t chunk = blockIdx.x / kSplit;
+  const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
-  const int64_t end = min(start + kChunk, d.numel);
+  const int64_t start = (chunk - d.chunk0) * kChunk + (int64_t)(blockIdx.x % kSplit) * kPart;
+  const int64_t end = min(start + kPart, d.numel);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 7, bw = lane >> 3;
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
@@ -382,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
     Group G[4];
     if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) load_group<BF16P>(d, b0 + 32 * j + 4 * sub, G[j], true);
+      for (int j = 0; j < 4; j++) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0 + 32 * j + 4 * sub, G[j], true);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         float a[4], b[4], q[4];
@@ -453,9 +540,9 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
                                          wv >> (8 * r));
         }
         const int64_t i = b0 + 32 * j + 4 * sub;
-        store_p4<BF16P>(d, i, pj);
-        *reinterpret_cast<uint32_t*>(d.m + i) = wm;
-        *reinterpret_cast<uint32_t*>(d.v + i) = wv;
+        store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i, pj);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i, wm);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i, wv);
       }
     } else if (exists) {
 #pragma unroll
@@ -569,8 +656,9 @@ struct fp8adam_ctx {
   int64_t nchunks = 0;
   TensorDesc* d_desc = nullptr;
   int32_t* d_chunk_tid = nullptr;
-  uint32_t* d_amax = nullptr;       // tensor mode: [n][2] running amax; block mode: [n][4] stats
-  uint32_t* d_last_amax = nullptr;  // tensor mode: [n][2] amax of the last step
+  uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
+  uint2* d_partial = nullptr;       // tensor mode: [nchunks] per-chunk amax of m', v'
+  float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
   unsigned long long* d_counters = nullptr;  // [n][5]
   bool timing = false;
   std::vector<hipEvent_t> ev;  // pairs
@@ -593,7 +681,8 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_desc) (void)hipFree(c->d_desc);
   if (c->d_chunk_tid) (void)hipFree(c->d_chunk_tid);
   if (c->d_amax) (void)hipFree(c->d_amax);
-  if (c->d_last_amax) (void)hipFree(c->d_last_amax);
+  if (c->d_partial) (void)hipFree(c->d_partial);
+  if (c->d_old_scale) (void)hipFree(c->d_old_scale);
   if (c->d_counters) (void)hipFree(c->d_counters);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   delete c;
@@ -619,55 +708,58 @@ int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
 template <int MF, int VF>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, c->d_desc,
-                     c->d_chunk_tid, c->d_amax, k);
+                     c->d_chunk_tid, c->d_partial, k);
+}
+
+template <int MF, int VF, int SMODE, bool STATS>
+void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
+  hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s, c->d_desc,
+                     c->d_partial, c->d_amax, c->d_old_scale, c->d_counters);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s,
-                     c->d_desc, c->d_chunk_tid, c->d_amax, k, c->d_counters);
-}
-
-template <int MF, int VF, int SMODE>
-void launch_commit(fp8adam_ctx* c, hipStream_t s) {
-  hipLaunchKernelGGL((k_commit<MF, VF, SMODE>), dim3((unsigned)((c->n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, c->d_desc, c->n, c->d_amax, c->d_last_amax);
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks * kSplit)), dim3(kThreads), 0, s,
+                     c->d_desc, c->d_chunk_tid, c->d_amax, c->d_old_scale, k, c->d_counters);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks * kSplit)), dim3(kThreads), 0, s,
                      c->d_desc, c->d_chunk_tid, k, c->d_counters, c->d_amax);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 int run_step_t(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   int slot;
-  if (STATS) {
-    const int64_t namax = c->cfg.granularity == FP8ADAM_SCALE_BLOCK128 ? 4 * (int64_t)c->n : 0;
-    if (int r = timed_begin(c, 4, s, &slot)) return r;
-    hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
-                       dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
-    if (int r = timed_end(c, slot, s)) return r;
-  }
-  if (c->nchunks > 0) {
-    if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
+  if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
+    if (STATS) {
+      if (int r = timed_begin(c, 4, s, &slot)) return r;
+      hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
+                         dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax,
+                         4 * (int64_t)c->n);
+      if (int r = timed_end(c, slot, s)) return r;
+    }
+    if (c->nchunks > 0) {
       if (int r = timed_begin(c, 3, s, &slot)) return r;
       launch_block<MF, VF, BF16P, STATS, SMODE>(c, k, s);
       if (int r = timed_end(c, slot, s)) return r;
-    } else {
+    }
+  } else {
+    if (c->nchunks > 0) {
       if (int r = timed_begin(c, 0, s, &slot)) return r;
       launch_amax<MF, VF>(c, k, s);
       if (int r = timed_end(c, slot, s)) return r;
+    }
+    // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
+    if (int r = timed_begin(c, 2, s, &slot)) return r;
+    launch_reduce<MF, VF, SMODE, STATS>(c, s);
+    if (int r = timed_end(c, slot, s)) return r;
+    if (c->nchunks > 0) {
       if (int r = timed_begin(c, 1, s, &slot)) return r;
       launch_update<MF, VF, BF16P, STATS, SMODE>(c, k, s);
       if (int r = timed_end(c, slot, s)) return r;
     }
-  }
-  if (c->cfg.granularity != FP8ADAM_SCALE_BLOCK128) {
-    if (int r = timed_begin(c, 2, s, &slot)) return r;
-    launch_commit<MF, VF, SMODE>(c, s);
-    if (int r = timed_end(c, slot, s)) return r;
   }
   HIP_TRY(hipGetLastError());
   return 0;
@@ -753,7 +845,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       const int64_t nc = (T.numel + kChunk - 1) / kChunk;
       desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
                            T.numel, nchunks};
-      if (nchunks + nc > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "too many elements for one context");
+      if ((nchunks + nc) * kSplit > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "too many elements for one context");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
       nchunks += nc;
     }
@@ -768,7 +860,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
-    if (e == hipSuccess) e = hipMalloc(&c->d_last_amax, sizeof(uint32_t) * namax);
+    if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
+    if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 2 * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
     if (e == hipSuccess)
       e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * (size_t)n, hipMemcpyHostToDevice, stream);
@@ -776,7 +869,6 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       e = hipMemcpyAsync(c->d_chunk_tid, chunk_tid.data(), sizeof(int32_t) * (size_t)nchunks, hipMemcpyHostToDevice,
                          stream);
     if (e == hipSuccess) e = hipMemsetAsync(c->d_amax, 0, sizeof(uint32_t) * namax, stream);
-    if (e == hipSuccess) e = hipMemsetAsync(c->d_last_amax, 0, sizeof(uint32_t) * namax, stream);
     if (e == hipSuccess)
       e = hipMemsetAsync(c->d_counters, 0, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -827,7 +919,7 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
     std::vector<unsigned long long> cnt((size_t)n * kStatsPerTensor, 0ull);
     std::vector<TensorDesc> desc((size_t)n);
     const bool block = ctx->cfg.granularity == FP8ADAM_SCALE_BLOCK128;
-    HIP_TRY(hipMemcpyAsync(amax.data(), block ? ctx->d_amax : ctx->d_last_amax,
+    HIP_TRY(hipMemcpyAsync(amax.data(), ctx->d_amax,
                            sizeof(uint32_t) * (size_t)n * (block ? 4 : 2), hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipMemcpyAsync(cnt.data(), ctx->d_counters, sizeof(unsigned long long) * cnt.size(),
                            hipMemcpyDeviceToHost, stream));
