@@ -323,3 +323,16 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.step(cfg, np.zeros(1, np.float32), np.zeros(1, np.uint16), np.zeros(1, np.uint8),
                     np.zeros(1, np.uint8), np.ones(1, np.float32), np.ones(1, np.float32))
+
+
+def test_nonfinite_count_closed_form():
+    """An infinite gradient makes g*g and v' infinite (and m' infinite): exactly
+    one non-finite element; the tensor's amax is then non-finite and the scale 1."""
+    n = 8
+    g = bf16_bits([1e-3] * n)
+    g[3] = 0x7F80  # +Inf in bf16
+    p = np.zeros(n, np.float32)
+    cm, cv, sm, sv = [x.numpy().copy() for x in workloads.make_state(n, "cpu")]
+    st = oracle.step(oracle.make_config(oracle.Hyper(step=1)), p, g, cm, cv, sm, sv)
+    assert st["nonfinite"] == 1
+    assert sm[0] == 1.0 and sv[0] == 1.0
