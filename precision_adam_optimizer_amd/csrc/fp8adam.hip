@@ -20,8 +20,9 @@
 //     k_block   : eight lanes own one 128-element block; the block amax is a
 //                 3-step DPP max, then update and requantize as above
 // The chunk table (built once at init) cuts every tensor into chunks of
-// kChunk elements; an amax-pass work-group owns one chunk, an update- or
-// block-pass work-group owns one of the kSplit equal parts of a chunk.  Loads and stores are dword-granular per lane
+// 2^chunk_log2 elements (4096..32768, chosen per context so that even small
+// lists give a few thousand work-groups); an amax-pass work-group owns one
+// chunk, an update- or block-pass work-group owns one kPart-element part.  Loads and stores are dword-granular per lane
 // and contiguous across the wave (fp32 master: 16 B per lane).
 #include <hip/hip_runtime.h>
 
@@ -43,11 +44,11 @@ using namespace fp8adam;
 namespace {
 
 // Launch-shape tunables (compile-time; the defaults are the measured best on MI355X).
-#ifndef FP8ADAM_CHUNK
-#define FP8ADAM_CHUNK 32768  // elements per chunk = per amax-pass work-group
+#ifndef FP8ADAM_MAX_CHUNK_LOG2
+#define FP8ADAM_MAX_CHUNK_LOG2 15  // largest chunk = amax-pass work-group (32768 elements)
 #endif
-#ifndef FP8ADAM_SPLIT
-#define FP8ADAM_SPLIT 8      // update / block work-groups per chunk
+#ifndef FP8ADAM_PART_LOG2
+#define FP8ADAM_PART_LOG2 12       // update / block work-group (4096 elements)
 #endif
 #ifndef FP8ADAM_AMAX_UNROLL
 #define FP8ADAM_AMAX_UNROLL 8
@@ -77,15 +78,15 @@ constexpr int kGroup = 4;                         // consecutive elements per la
 constexpr int kSubTile = kThreads * kGroup;       // 1024 elements per work-group access
 constexpr int kAmaxUnroll = FP8ADAM_AMAX_UNROLL;  // accesses in flight per lane, amax pass
 constexpr int kUpdUnroll = FP8ADAM_UPDATE_UNROLL; // accesses in flight per lane, update pass
-constexpr int64_t kChunk = FP8ADAM_CHUNK;         // elements per chunk
-constexpr int kSplit = FP8ADAM_SPLIT;
-constexpr int64_t kPart = kChunk / kSplit;        // elements per update / block work-group
+constexpr int kPartLog2 = FP8ADAM_PART_LOG2;
+constexpr int64_t kPart = (int64_t)1 << kPartLog2;  // elements per update / block work-group
+constexpr int kMaxChunkLog2 = FP8ADAM_MAX_CHUNK_LOG2;
+constexpr int kMinAmaxGroups = 2048;                // 8 work-groups per CU
 constexpr int kBlock = 128;                       // block-scale granularity
 constexpr int kReduceThreads = 1024;              // one work-group per tensor in k_reduce
 constexpr int kStatsPerTensor = 5;
 
-static_assert(kChunk % kSplit == 0, "chunk must split evenly");
-static_assert(kChunk % (kSubTile * kAmaxUnroll) == 0, "chunk must hold whole unrolled amax tiles");
+static_assert(kMaxChunkLog2 >= kPartLog2, "a chunk holds whole parts");
 static_assert(kPart % (kSubTile * kUpdUnroll) == 0, "part must hold whole unrolled update tiles");
 static_assert(kPart % (kBlock * 32) == 0, "part must hold whole block tiles");
 
@@ -172,16 +173,33 @@ typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
 
 // Streamed loads and stores (optionally non-temporal: the data is touched once per pass).
+// The tensor pointers come from a descriptor in memory, so the compiler cannot
+// prove they are global and would emit flat instructions; these helpers cast
+// them into the global address space (global_load / global_store).
+#define FP8ADAM_GLOBAL __attribute__((address_space(1)))
+
 template <typename T, bool NT>
 __device__ __forceinline__ T ld_stream(const void* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-  else return *reinterpret_cast<const T*>(p);
+  const FP8ADAM_GLOBAL T* g = (const FP8ADAM_GLOBAL T*)(p);
+  if constexpr (NT) return __builtin_nontemporal_load(g);
+  else return *g;
 }
 
 template <typename T, bool NT>
 __device__ __forceinline__ void st_stream(void* p, T x) {
-  if constexpr (NT) __builtin_nontemporal_store(x, reinterpret_cast<T*>(p));
-  else *reinterpret_cast<T*>(p) = x;
+  FP8ADAM_GLOBAL T* g = (FP8ADAM_GLOBAL T*)(p);
+  if constexpr (NT) __builtin_nontemporal_store(x, g);
+  else *g = x;
+}
+
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+  return *(const FP8ADAM_GLOBAL T*)(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void st_global(void* p, T x) {
+  *(FP8ADAM_GLOBAL T*)(p) = x;
 }
 
 // Loads of one group of four consecutive elements.
@@ -240,14 +258,14 @@ __device__ __forceinline__ void store_p4(const TensorDesc& d, int64_t i, const f
 
 template <bool BF16P>
 __device__ __forceinline__ float load_p1(const TensorDesc& d, int64_t i) {
-  if constexpr (BF16P) return __uint_as_float((uint32_t) static_cast<const uint16_t*>(d.p)[i] << 16);
-  else return static_cast<const float*>(d.p)[i];
+  if constexpr (BF16P) return __uint_as_float((uint32_t)ld_global<uint16_t>(static_cast<const uint16_t*>(d.p) + i) << 16);
+  else return ld_global<float>(static_cast<const float*>(d.p) + i);
 }
 
 template <bool BF16P>
 __device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x) {
-  if constexpr (BF16P) static_cast<uint16_t*>(d.p)[i] = (uint16_t)f32_to_bf16_rne(x);
-  else static_cast<float*>(d.p)[i] = x;
+  if constexpr (BF16P) st_global<uint16_t>(static_cast<uint16_t*>(d.p) + i, (uint16_t)f32_to_bf16_rne(x));
+  else st_global<float>(static_cast<float*>(d.p) + i, x);
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -255,13 +273,13 @@ __device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x
 template <int MF, int VF>
 __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ chunk_tid,
-                                                   uint2* __restrict__ partial, StepConsts c) {
+                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2) {
   const int tid = chunk_tid[blockIdx.x];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) * kChunk;
-  const int64_t end = min(start + kChunk, d.numel);
+  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) << chunk_log2;
+  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
   const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
-  const float sm = *d.sm, sv = *d.sv;
+  const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
   uint32_t am = 0, av = 0;
 
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
@@ -288,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
   // ragged tail (< 4 elements at the end of a tensor)
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = __uint_as_float((uint32_t)d.g[i] << 16);
+    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
     float m1, v1;
-    moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, m1, v1);
+    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     am = max(am, abs_bits(m1));
     av = max(av, abs_bits(v1));
   }
@@ -311,10 +329,11 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
                                                            const uint2* __restrict__ partial,
                                                            uint32_t* __restrict__ amax,
                                                            float* __restrict__ old_scale,
-                                                           unsigned long long* __restrict__ counters) {
+                                                           unsigned long long* __restrict__ counters,
+                                                           int chunk_log2) {
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
-  const int64_t nc = (d.numel + kChunk - 1) / kChunk;
+  const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
   uint32_t am = 0, av = 0;
   for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) {
     const uint2 pv = partial[d.chunk0 + k];
@@ -338,13 +357,13 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
     amax[2 * t] = am;
     amax[2 * t + 1] = av;
     if (d.numel > 0) {
-      old_scale[2 * t] = *d.sm;
-      old_scale[2 * t + 1] = *d.sv;
+      old_scale[2 * t] = ld_global<float>(d.sm);
+      old_scale[2 * t + 1] = ld_global<float>(d.sv);
       float s, inv;
       choose_scale<MF, SMODE>(am, s, inv);
-      *d.sm = s;
+      st_global<float>(d.sm, s);
       choose_scale<VF, SMODE>(av, s, inv);
-      *d.sv = s;
+      st_global<float>(d.sv, s);
     }
   }
   if constexpr (STATS) {
@@ -359,11 +378,13 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
                                                      const int32_t* __restrict__ chunk_tid,
                                                      const uint32_t* __restrict__ amax,
                                                      const float* __restrict__ old_scale, StepConsts c,
-                                                     unsigned long long* __restrict__ counters) {
-  const int64_t chunk = blockIdx.x / kSplit;
+                                                     unsigned long long* __restrict__ counters, int chunk_log2) {
+  const int split_log2 = chunk_log2 - kPartLog2;
+  const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
   const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = (chunk - d.chunk0) * kChunk + (int64_t)(blockIdx.x % kSplit) * kPart;
+  const int64_t start = ((chunk - d.chunk0) << chunk_log2) +
+                        ((int64_t)(blockIdx.x & ((1u << split_log2) - 1u)) << kPartLog2);
   const int64_t end = min(start + kPart, d.numel);
   if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
@@ -408,16 +429,16 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = __uint_as_float((uint32_t)d.g[i] << 16);
+    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
     float m1, v1;
-    moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, m1, v1);
+    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     const float p = param_update(c, load_p1<BF16P>(d, i), m1, v1);
     const float qm = m1 * ism, qv = v1 * isv;
     const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
     store_p1<BF16P>(d, i, p);
-    d.m[i] = (uint8_t)cm;
-    d.v[i] = (uint8_t)cv;
+    st_global<uint8_t>(d.m + i, (uint8_t)cm);
+    st_global<uint8_t>(d.v + i, (uint8_t)cv);
   }
   flush_counters<STATS>(counters, tid, cnt);
 }
@@ -443,11 +464,13 @@ template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
                                                     const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                     unsigned long long* __restrict__ counters,
-                                                    uint32_t* __restrict__ amax) {
-  const int64_t chunk = blockIdx.x / kSplit;
+                                                    uint32_t* __restrict__ amax, int chunk_log2) {
+  const int split_log2 = chunk_log2 - kPartLog2;
+  const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
   const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = (chunk - d.chunk0) * kChunk + (int64_t)(blockIdx.x % kSplit) * kPart;
+  const int64_t start = ((chunk - d.chunk0) << chunk_log2) +
+                        ((int64_t)(blockIdx.x & ((1u << split_log2) - 1u)) << kPartLog2);
   const int64_t end = min(start + kPart, d.numel);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & 7, bw = lane >> 3;
@@ -462,8 +485,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
     const int64_t blk = b0 / kBlock;
     float sm = 1.0f, sv = 1.0f;
     if (exists) {
-      sm = d.sm[blk];
-      sv = d.sv[blk];
+      sm = ld_global<float>(d.sm + blk);
+      sv = ld_global<float>(d.sv + blk);
     }
     float m1[16], v1[16], p[16];
     Group G[4];
@@ -490,8 +513,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
           const int64_t i = b0 + 32 * j + 4 * sub + r;
           float a = 0.0f, b = 0.0f, q = 0.0f;
           if (exists && i < end) {
-            const float g = __uint_as_float((uint32_t)d.g[i] << 16);
-            moment_update(c, g, decode1<MF>(d.m[i]) * sm, decode1<VF>(d.v[i]) * sv, a, b);
+            const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, a, b);
             q = load_p1<BF16P>(d, i);
           }
           m1[4 * j + r] = a;
@@ -556,15 +579,15 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
             const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
             count_element<MF, VF, STATS>(cnt, m1[k], v1[k], qm, qv, cm, cv);
             store_p1<BF16P>(d, i, p[k]);
-            d.m[i] = (uint8_t)cm;
-            d.v[i] = (uint8_t)cv;
+            st_global<uint8_t>(d.m + i, (uint8_t)cm);
+            st_global<uint8_t>(d.v + i, (uint8_t)cv);
           }
         }
       }
     }
     if (exists && sub == 0) {
-      d.sm[blk] = nsm;
-      d.sv[blk] = nsv;
+      st_global<float>(d.sm + blk, nsm);
+      st_global<float>(d.sv + blk, nsv);
     }
   }
   if constexpr (STATS) {
@@ -654,6 +677,7 @@ struct fp8adam_ctx {
   fp8adam_config cfg{};
   int32_t n = 0;
   int64_t nchunks = 0;
+  int chunk_log2 = kMaxChunkLog2;  // elements per chunk = 2^chunk_log2
   TensorDesc* d_desc = nullptr;
   int32_t* d_chunk_tid = nullptr;
   uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
@@ -708,25 +732,26 @@ int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
 template <int MF, int VF>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, c->d_desc,
-                     c->d_chunk_tid, c->d_partial, k);
+                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2);
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
 void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
   hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s, c->d_desc,
-                     c->d_partial, c->d_amax, c->d_old_scale, c->d_counters);
+                     c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks * kSplit)), dim3(kThreads), 0, s,
-                     c->d_desc, c->d_chunk_tid, c->d_amax, c->d_old_scale, k, c->d_counters);
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks << (c->chunk_log2 - kPartLog2))),
+                     dim3(kThreads), 0, s, c->d_desc, c->d_chunk_tid, c->d_amax, c->d_old_scale, k, c->d_counters,
+                     c->chunk_log2);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks * kSplit)), dim3(kThreads), 0, s,
-                     c->d_desc, c->d_chunk_tid, k, c->d_counters, c->d_amax);
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks << (c->chunk_log2 - kPartLog2))),
+                     dim3(kThreads), 0, s, c->d_desc, c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
@@ -826,6 +851,14 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (cfg->master != FP8ADAM_MASTER_FP32 && cfg->master != FP8ADAM_MASTER_BF16)
       return fail(FP8ADAM_EINVAL, "bad master dtype");
 
+    // Chunk size: the largest power of two in [kPart, 2^kMaxChunkLog2] that still
+    // gives the amax pass at least kMinAmaxGroups work-groups.
+    int64_t total = 0;
+    for (int32_t t = 0; t < n; t++) total += tensors[t].numel > 0 ? tensors[t].numel : 0;
+    int chunk_log2 = kMaxChunkLog2;
+    while (chunk_log2 > kPartLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
+    const int64_t chunk = (int64_t)1 << chunk_log2;
+
     std::vector<TensorDesc> desc((size_t)n);
     std::vector<int32_t> chunk_tid;
     int64_t nchunks = 0;
@@ -842,10 +875,11 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         if (!T.m_scale || ((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
           return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
       }
-      const int64_t nc = (T.numel + kChunk - 1) / kChunk;
+      const int64_t nc = (T.numel + chunk - 1) / chunk;
       desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
                            T.numel, nchunks};
-      if ((nchunks + nc) * kSplit > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "too many elements for one context");
+      if (((nchunks + nc) << (chunk_log2 - kPartLog2)) > (int64_t)INT32_MAX)
+        return fail(FP8ADAM_EINVAL, "too many elements for one context");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
       nchunks += nc;
     }
@@ -855,6 +889,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->cfg = *cfg;
     c->n = n;
     c->nchunks = nchunks;
+    c->chunk_log2 = chunk_log2;
     hipError_t e = hipGetDevice(&c->device);
     const size_t namax = (size_t)n * 4;
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * (size_t)n);

@@ -237,3 +237,36 @@ def test_llama2_13b_bf16_master_full_size():
     n = len(w.shapes)
     sample = _layer_indices(40, [0]) + [n - 2, n - 1]
     run_full(w, steps=5, sample=sample)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("sizes,chunk", [([1_048_576], 4096), ([9_000_001, 11_000_003], 8192),
+                                          ([30_000_005, 5_000_000, 3], 16384), ([70_000_000], 32768)])
+def test_chunk_size_choice_and_parity(sizes, chunk):
+    """The context picks the largest chunk (4096..32768) that still gives at
+    least 2048 amax-pass work-groups; each choice is checked against the oracle."""
+    dev = torch.device("cuda")
+    params = [torch.randn(n, device=dev) * 0.02 for n in sizes]
+    grads = [random_grad(n, 77 + i, dev) for i, n in enumerate(sizes)]
+    host = [OracleState(np_host(p), np.zeros(n, np.uint8), np.zeros(n, np.uint8), np.ones(1, np.float32),
+                        np.ones(1, np.float32)) for p, n in zip(params, sizes)]
+    opt = pk.FP8AdamW(params, grads, collect_stats=True)
+    assert opt.num_chunks == sum(-(-n // chunk) for n in sizes)
+    try:
+        for t in (1, 2):
+            opt.step(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            torch.cuda.synchronize()
+            cfg = oracle_config(oracle.Hyper(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t),
+                                "e4m3", "e5m2", "tensor", "pow2", "fp32")
+            gstats = opt.stats()
+
+            def check(i):
+                host[i].step(cfg, np_host(grads[i]))
+                compare_tensor(f"tensor {i} step {t}", host[i], np_host(params[i]), np_host(opt.m[i]),
+                               np_host(opt.v[i]), np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), "fp32")
+                _compare_stats(f"tensor {i} step {t}", gstats[i], host[i].stats, "tensor")
+                upload_params(params[i], host[i])
+
+            run_pool(check, list(range(len(sizes))))
+    finally:
+        opt.close()
