@@ -1,15 +1,21 @@
 """Benchmark of the FP8-moment AdamW step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2_7b]
+                    [--schedule two_pass|speculative]
 
 Times K whole optimizer steps (every tensor of the list, one fp8adam_step
 each) after W warm-up steps, with inputs resident in HBM, and prints one JSON
 line: params updated/s, the roofline of the dominant kernel (algorithmic
 bytes / its HIP-event duration, against 8 TB/s), and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Every step gets a fresh gradient draw
+(generated into the bound gradient buffers between steps, outside the timed
+events), so the moments and their scales evolve as in training.
 
 Other modes (used to make the committed profiles):
     --calibrate-copy   a plain device copy of 2 GiB, for HBM counter scaling
+    --same-grad        reuse step 1's gradient every step (profiler runs: drawing
+                       fresh gradients under counter collection is very slow; the
+                       optimizer kernels do the same work either way)
     --no-cpu-baseline  skip the oracle timing
 """
 from __future__ import annotations
@@ -107,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_7b",
                     choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_13b_bf16"])
+    ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
+    ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -133,50 +141,69 @@ def main():
     params = [workloads.make_param(w, i, s, dev) for i, (_, s) in enumerate(shapes)]
     grads = [workloads.make_grad(w, i, s, 1, dev) for i, (_, s) in enumerate(shapes)]
     torch.cuda.synchronize()
-    opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity)
+    schedule = args.schedule if w.granularity == "tensor" else "two_pass"
+    opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
+                      schedule=schedule)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
-    log(f"context: {opt.num_chunks} chunks; warmup {args.warmup} steps")
+    stream = torch.cuda.current_stream()
+
+    def load_grads(t):
+        if args.same_grad:
+            return
+        for i, (_, shp) in enumerate(shapes):
+            grads[i].copy_(workloads.make_grad(w, i, shp, t, dev))
+
+    log(f"context: {opt.num_chunks} chunks, schedule {schedule}; warmup {args.warmup} steps")
     t = 0
     for _ in range(args.warmup):
         t += 1
+        load_grads(t)
         opt.step(step=t, **hp)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        log(f"warm-up step {t} done")
 
     opt.set_timing(True)
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    evs = []
     wall0 = time.perf_counter()
-    ev0.record(stream)
     for _ in range(args.steps):
         t += 1
+        load_grads(t)  # not timed
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         opt.step(step=t, **hp)
-    ev1.record(stream)
+        e1.record(stream)
+        evs.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = sum(a.elapsed_time(b) for a, b in evs)
     ktimes = opt.kernel_times()
     opt.set_timing(False)
     ms_per_step = ms_total / args.steps
     value = total / (ms_per_step / 1e3)
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall incl. gradient generation {wall / args.steps * 1e3:.3f} ms/step)")
     for k, (tot, cnt) in ktimes.items():
         if cnt:
             log(f"  {k}: {cnt} launches, avg {tot / cnt * 1e3:.1f} us")
 
-    kernel = "block128_pass" if w.granularity == "block128" else "update_pass"
+    kernel = "block128_pass" if w.granularity == "block128" else (
+        "spec_pass" if schedule == "speculative" else "update_pass")
     ktot, kcnt = ktimes[kernel]
     kavg_s = ktot / kcnt / 1e3
     bpp = BYTES_PER_PARAM[(w.granularity, w.master)]
     alg_bytes = bpp * total
     achieved = alg_bytes / kavg_s / 1e9
     traffic = load_traffic(w.name, kernel)
-    step_bytes = alg_bytes + (4.0 * total if w.granularity == "tensor" else 0.0)  # + amax pass reads g, m, v
+    # bytes the whole step moved: + the amax pass (g, m, v) in the two-pass schedule,
+    # + the fix-up (g, m, v read, m, v written) of re-quantized tensors in the speculative one
+    fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
+    step_bytes = alg_bytes + (4.0 * total if (w.granularity == "tensor" and schedule == "two_pass") else 0.0)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
                 "bytes_per_param": bpp,
-                "whole_step_GBps_design_bytes": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1)}
+                "whole_step_GBps_excluding_fixup": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1)}
+    if schedule == "speculative":
+        roofline["fixup_avg_us"] = round(fix_ms / max(fix_n, 1) * 1e3, 2)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -202,8 +229,10 @@ def main():
         "dtype": "f32" if w.master == "fp32" else "bf16-master/f32-math",
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(shapes), "params": total, "m_format": w.m_fmt,
-                   "v_format": w.v_fmt, "scale": w.granularity, "master": w.master, "grad": "bf16",
-                   "weight_decay": w.weight_decay, "parallelism": "single GPU"},
+                   "v_format": w.v_fmt, "scale": w.granularity, "master": w.master,
+                   "weight_decay": w.weight_decay, "schedule": schedule,
+                   "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

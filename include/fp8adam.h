@@ -63,6 +63,15 @@ typedef enum { FP8ADAM_SCALE_TENSOR = 0, FP8ADAM_SCALE_BLOCK128 = 1 } fp8adam_gr
 typedef enum { FP8ADAM_SCALE_POW2 = 0, FP8ADAM_SCALE_AMAX = 1 } fp8adam_scale_mode;
 /* Master weights: fp32, or bf16 (the update is rounded to nearest-even bf16). */
 typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master;
+/* How a per-tensor-scaled step is scheduled on the device.  Both give bit-identical results.
+ * TWO_PASS: an amax pass over (g, m, v), then the update pass (18 bytes per fp32 parameter).
+ * SPECULATIVE: one update pass that quantizes with the power-of-two scale the tensor had
+ *   before the step and writes the codes into the other of two code buffers (m/v and
+ *   m_alt/v_alt, alternating every step); a per-tensor check then re-quantizes, from the old
+ *   codes, only the tensors whose true scale differs (14 bytes per fp32 parameter plus 6 per
+ *   re-quantized one).  Needs per-tensor POW2 scales and m_alt/v_alt; steps with
+ *   t < speculate_from_step run TWO_PASS in place on the current buffer. */
+typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 } fp8adam_schedule;
 
 typedef struct {
     int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
@@ -71,6 +80,8 @@ typedef struct {
     int32_t scale_mode;    /* fp8adam_scale_mode */
     int32_t master;        /* fp8adam_master */
     int32_t collect_stats; /* nonzero: count underflow / saturation / non-finite per tensor */
+    int32_t schedule;      /* fp8adam_schedule (block granularity is always one pass) */
+    int32_t speculate_from_step; /* first t of the speculative schedule; <= 0 means 4 */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,
@@ -80,6 +91,9 @@ typedef struct {
  *   m, v    : numel FP8 codes of the moments, updated in place
  *   m_scale : 1 float (tensor granularity) or ceil(numel/128) floats (block), in place
  *   v_scale : same as m_scale, for v
+ *   m_alt, v_alt : numel bytes each, the second code buffers of the speculative
+ *             schedule (ignored, may be NULL, otherwise); fp8adam_current_buffer
+ *             tells which pair holds the moments after a step
  * The state before the first step is all-zero codes with scales 1.0. */
 typedef struct {
     void *param;
@@ -89,6 +103,8 @@ typedef struct {
     float *m_scale;
     float *v_scale;
     int64_t numel;
+    uint8_t *m_alt;
+    uint8_t *v_alt;
 } fp8adam_tensor;
 
 /* Hyperparameters of one step.  step is the 1-based t used for bias correction. */
@@ -107,6 +123,8 @@ typedef struct {
     int64_t underflow_m, underflow_v; /* nonzero moment stored as a +-0 code */
     int64_t saturated_m, saturated_v; /* |x * inv_s| > FMAX before clamping */
     int64_t nonfinite;                /* elements with a non-finite m' or v' */
+    int64_t requantized;              /* speculative schedule: elements re-quantized because the
+                                         tensor's scale changed (numel or 0); else 0 */
 } fp8adam_stats_t;
 
 typedef struct fp8adam_ctx fp8adam_ctx;
@@ -155,15 +173,20 @@ int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 
 /* Per-kernel timing since the last call (or since timing was enabled):
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
- * 3 = block-scaled single pass, 4 = stats reset), total_ms[k] and count[k].
+ * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
+ * 6 = speculative scale check, 7 = re-quantization fix-up), total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);
 
 /* HIP runtime version the library runs on (hipRuntimeGetVersion), in *version. */
 int fp8adam_runtime_version(int32_t *version);
 
-/* Number of chunks (work-groups of the streaming passes) of the context. */
+/* Number of chunks (work-groups of the amax pass) of the context; -1 for NULL. */
 int64_t fp8adam_num_chunks(const fp8adam_ctx *ctx);
+
+/* Which code buffers hold the moments once the steps enqueued so far have run:
+ * 0 = m/v, 1 = m_alt/v_alt (only the speculative schedule alternates); -1 for NULL. */
+int32_t fp8adam_current_buffer(const fp8adam_ctx *ctx);
 
 #ifdef __cplusplus
 }

@@ -20,18 +20,21 @@ E4M3, E5M2 = 0, 1
 SCALE_TENSOR, SCALE_BLOCK128 = 0, 1
 SCALE_POW2, SCALE_AMAX = 0, 1
 MASTER_FP32, MASTER_BF16 = 0, 1
+SCHEDULE_TWO_PASS, SCHEDULE_SPECULATIVE = 0, 1
 BLOCK = 128
 
 _FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
 _GRAN = {"tensor": SCALE_TENSOR, "block128": SCALE_BLOCK128}
 _SMODE = {"pow2": SCALE_POW2, "amax": SCALE_AMAX}
+_SCHED = {"two_pass": SCHEDULE_TWO_PASS, "speculative": SCHEDULE_SPECULATIVE}
 
-KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset")
+KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
+                "spec_check", "fixup")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
-           "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks")
+           "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer")
 
 
 class Fp8AdamError(RuntimeError):
@@ -43,13 +46,14 @@ class Fp8AdamError(RuntimeError):
 class TensorArg(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("m_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("numel", ctypes.c_int64)]
+                ("numel", ctypes.c_int64), ("m_alt", ctypes.c_void_p), ("v_alt", ctypes.c_void_p)]
 
 
 class ConfigArg(ctypes.Structure):
     _fields_ = [("m_format", ctypes.c_int32), ("v_format", ctypes.c_int32),
                 ("granularity", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
-                ("master", ctypes.c_int32), ("collect_stats", ctypes.c_int32)]
+                ("master", ctypes.c_int32), ("collect_stats", ctypes.c_int32),
+                ("schedule", ctypes.c_int32), ("speculate_from_step", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -62,7 +66,7 @@ class StatsArg(ctypes.Structure):
                 ("scale_m", ctypes.c_float), ("scale_v", ctypes.c_float),
                 ("underflow_m", ctypes.c_int64), ("underflow_v", ctypes.c_int64),
                 ("saturated_m", ctypes.c_int64), ("saturated_v", ctypes.c_int64),
-                ("nonfinite", ctypes.c_int64)]
+                ("nonfinite", ctypes.c_int64), ("requantized", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -94,6 +98,8 @@ def load() -> ctypes.CDLL:
     L.fp8adam_runtime_version.argtypes = [ctypes.POINTER(i32)]
     L.fp8adam_num_chunks.argtypes = [vp]
     L.fp8adam_num_chunks.restype = i64
+    L.fp8adam_current_buffer.argtypes = [vp]
+    L.fp8adam_current_buffer.restype = i32
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
                  "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
                  "fp8adam_runtime_version"):
@@ -186,6 +192,10 @@ def fp8adam_num_chunks(ctx: int) -> int:
     return load().fp8adam_num_chunks(ctx)
 
 
+def fp8adam_current_buffer(ctx: int) -> int:
+    return load().fp8adam_current_buffer(ctx)
+
+
 # ------------------------------------------------------------ torch wrapper
 
 class FP8AdamW:
@@ -194,13 +204,16 @@ class FP8AdamW:
     params: fp32 or bf16 master weights (all the same dtype); grads: bf16, same
     numel as their parameter.  The moment codes (uint8) and scales (fp32) are
     allocated here, zero codes with unit scales, unless ``state`` supplies
-    (m, v, m_scale, v_scale) lists.  Every tensor must be contiguous and
-    16-byte aligned on the same device, and must stay alive with the same
-    storage while this object exists.
+    (m, v, m_scale, v_scale) lists.  With ``schedule="speculative"`` a second
+    pair of code buffers is allocated and the moments alternate between the two;
+    ``m`` and ``v`` always return the pair that holds them.  Every tensor must be
+    contiguous and 16-byte aligned on the same device, and must stay alive with
+    the same storage while this object exists.
     """
 
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
-                 scale_mode="pow2", collect_stats=False, state=None):
+                 scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
+                 speculate_from_step=0):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
@@ -215,18 +228,24 @@ class FP8AdamW:
             ms = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             vs = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             state = (m, v, ms, vs)
-        self.m, self.v, self.m_scale, self.v_scale = [list(x) for x in state]
+        m, v, self.m_scale, self.v_scale = [list(x) for x in state]
+        spec = _SCHED[schedule] == SCHEDULE_SPECULATIVE
+        m_alt = [torch.empty_like(x) for x in m] if spec else [None] * len(m)
+        v_alt = [torch.empty_like(x) for x in v] if spec else [None] * len(v)
+        self._m, self._v = (m, m_alt), (v, v_alt)
         args = []
         for i, (p, g) in enumerate(zip(params, grads)):
             if p.dtype != master or g.dtype != torch.bfloat16 or p.numel() != g.numel():
                 raise ValueError(f"tensor {i}: dtype or size mismatch")
-            for t in (p, g, self.m[i], self.v[i], self.m_scale[i], self.v_scale[i]):
+            for t in (p, g, m[i], v[i], self.m_scale[i], self.v_scale[i]):
                 if not t.is_contiguous() or t.device != p.device:
                     raise ValueError(f"tensor {i}: every buffer must be contiguous on one device")
-            args.append(TensorArg(p.data_ptr(), g.data_ptr(), self.m[i].data_ptr(), self.v[i].data_ptr(),
-                                  self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel()))
+            args.append(TensorArg(p.data_ptr(), g.data_ptr(), m[i].data_ptr(), v[i].data_ptr(),
+                                  self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel(),
+                                  _ptr(m_alt[i]), _ptr(v_alt[i])))
         self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
-                             MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats))
+                             MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
+                             _SCHED[schedule], int(speculate_from_step))
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):
@@ -234,6 +253,20 @@ class FP8AdamW:
 
     def num_scales(self, numel: int) -> int:
         return 1 if self.granularity == SCALE_TENSOR else max(1, -(-numel // BLOCK))
+
+    @property
+    def current_buffer(self) -> int:
+        if getattr(self, "_ctx", None):
+            self._last_cur = fp8adam_current_buffer(self._ctx)
+        return getattr(self, "_last_cur", 0)
+
+    @property
+    def m(self) -> list:
+        return self._m[self.current_buffer]
+
+    @property
+    def v(self) -> list:
+        return self._v[self.current_buffer]
 
     def step(self, *, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
              weight_decay: float = 0.0, step: int) -> None:
@@ -256,6 +289,7 @@ class FP8AdamW:
 
     def close(self) -> None:
         if getattr(self, "_ctx", None):
+            _ = self.current_buffer  # remember where the moments are
             torch.cuda.synchronize(self.device)
             fp8adam_destroy(self._ctx)
             self._ctx = None

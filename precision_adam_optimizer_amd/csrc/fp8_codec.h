@@ -125,6 +125,7 @@ struct StepConsts {
   float step_size;     // lr / (1 - beta1^t)
   float inv_bc2;       // 1 / (1 - beta2^t)
   float eps;
+  float grow_m, grow_v; // speculative schedule: expected amax growth (1-beta^t)/(1-beta^(t-1))
 };
 
 // Moment update (daoxuan.cc explainer, "Adam's update makes the needs

@@ -16,6 +16,15 @@
 //                 caller's slots (and clear the tensor's stats counters)
 //     k_update  : recompute m', v' with the staged old scales; update p;
 //                 requantize m', v' with the new scales and saturation
+//   per-tensor scales, speculative schedule (opt-in; bit-identical results)
+//     k_update<SPEC> : one streaming pass that quantizes with the scale the
+//                 tensor had before the step (the prediction), writes the
+//                 codes into the other code buffer (ping-pong), updates p
+//                 and records per-part amax partials
+//     k_spec_reduce : per tensor, the true scale from the partials; where it
+//                 differs from the prediction the tensor is flagged
+//     k_fixup   : flagged tensors only: recompute m', v' from the old codes
+//                 (still intact in the source buffer) and requantize
 //   per-128-element scales (one streaming pass)
 //     k_block   : eight lanes own one 128-element block; the block amax is a
 //                 3-step DPP max, then update and requantize as above
@@ -268,6 +277,30 @@ __device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x
   else st_global<float>(static_cast<float*>(d.p) + i, x);
 }
 
+// Speculative schedule: the predicted scale is the POW2 scale of the previous
+// step's amax times the growth a stationary gradient would give the moving
+// average, (1-beta^t)/(1-beta^(t-1)).  Without a usable previous amax (zero or
+// non-finite) it is the power of two with the exponent of the tensor's current
+// scale (1 if that is zero, subnormal, Inf or NaN).  The update pass and the
+// check evaluate exactly the same expression, so they agree on the prediction.
+__device__ __forceinline__ uint32_t exponent_scale_bits(float s_old) {
+  const uint32_t e = (__float_as_uint(s_old) >> 23) & 0xFFu;
+  if (e == 0u || e == 255u) return 0x3F800000u;
+  return e << 23;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t predicted_scale_bits(uint32_t amax_prev, float s_old, float growth) {
+  if (amax_prev == 0u || (amax_prev >> 23) >= 255u) return exponent_scale_bits(s_old);
+  float s, inv;
+  choose_scale<FMT, 0>(__float_as_uint(__uint_as_float(amax_prev) * growth) & 0x7FFFFFFFu, s, inv);
+  return __float_as_uint(s);
+}
+
+__device__ __forceinline__ float inverse_pow2(uint32_t pow2_bits) {
+  return __uint_as_float((254u - (pow2_bits >> 23)) << 23);
+}
+
 // ------------------------------------------------------------------ pass 1
 
 template <int MF, int VF>
@@ -330,7 +363,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
                                                            uint32_t* __restrict__ amax,
                                                            float* __restrict__ old_scale,
                                                            unsigned long long* __restrict__ counters,
-                                                           int chunk_log2) {
+                                                           int chunk_log2, int32_t* __restrict__ flags) {
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
   const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
@@ -356,6 +389,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
     }
     amax[2 * t] = am;
     amax[2 * t + 1] = av;
+    flags[t] = 0;
     if (d.numel > 0) {
       old_scale[2 * t] = ld_global<float>(d.sm);
       old_scale[2 * t + 1] = ld_global<float>(d.sv);
@@ -373,12 +407,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
 
 // ------------------------------------------------------------------ pass 2
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC>
 __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
+                                                     const TensorDesc* __restrict__ dst_descs,
                                                      const int32_t* __restrict__ chunk_tid,
                                                      const uint32_t* __restrict__ amax,
                                                      const float* __restrict__ old_scale, StepConsts c,
-                                                     unsigned long long* __restrict__ counters, int chunk_log2) {
+                                                     unsigned long long* __restrict__ counters, int chunk_log2,
+                                                     uint2* __restrict__ part_amax) {
   const int split_log2 = chunk_log2 - kPartLog2;
   const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
   const int tid = chunk_tid[chunk];
@@ -388,10 +424,23 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   const int64_t end = min(start + kPart, d.numel);
   if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
-  const float sm = old_scale[2 * tid], sv = old_scale[2 * tid + 1];
-  float nsm, ism, nsv, isv;
-  choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
-  choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
+  // codes go back in place (two-pass) or into the other buffer (speculative)
+  uint8_t* const dm = SPEC ? dst_descs[tid].m : d.m;
+  uint8_t* const dv = SPEC ? dst_descs[tid].v : d.v;
+  float sm, sv, ism, isv;
+  if constexpr (SPEC) {
+    sm = ld_global<float>(d.sm);
+    sv = ld_global<float>(d.sv);
+    ism = inverse_pow2(predicted_scale_bits<MF>(amax[2 * tid], sm, c.grow_m));
+    isv = inverse_pow2(predicted_scale_bits<VF>(amax[2 * tid + 1], sv, c.grow_v));
+  } else {
+    float nsm, nsv;
+    sm = old_scale[2 * tid];
+    sv = old_scale[2 * tid + 1];
+    choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
+    choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
+  }
+  uint32_t am = 0, av = 0;  // speculative: this part's amax
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
 
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUpdUnroll) {
@@ -413,6 +462,10 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
           p[j] = param_update(c, p[j], m1[j], v1[j]);
           qm[j] = m1[j] * ism;
           qv[j] = v1[j] * isv;
+          if constexpr (SPEC) {
+            am = max(am, abs_bits(m1[j]));
+            av = max(av, abs_bits(v1[j]));
+          }
         }
         const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
         const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
@@ -422,8 +475,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
             count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
         }
         store_p4<BF16P, FP8ADAM_NT_UPDATE_ST != 0>(d, i, p);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(d.m + i, wm);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(d.v + i, wv);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dm + i, wm);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dv + i, wv);
       }
     }
   }
@@ -436,9 +489,187 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     const float qm = m1 * ism, qv = v1 * isv;
     const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
+    if constexpr (SPEC) {
+      am = max(am, abs_bits(m1));
+      av = max(av, abs_bits(v1));
+    }
     store_p1<BF16P>(d, i, p);
-    st_global<uint8_t>(d.m + i, (uint8_t)cm);
-    st_global<uint8_t>(d.v + i, (uint8_t)cv);
+    st_global<uint8_t>(dm + i, (uint8_t)cm);
+    st_global<uint8_t>(dv + i, (uint8_t)cv);
+  }
+  flush_counters<STATS>(counters, tid, cnt);
+  if constexpr (SPEC) {
+    block_max2(am, av);
+    if (threadIdx.x == 0) part_amax[blockIdx.x] = make_uint2(am, av);
+  }
+}
+
+// ------------------------------------------------- speculative: verify, fix up
+//
+// One work-group per tensor: the true amax from the per-part partials, the
+// true POW2 scales, and a comparison with the predicted ones.  The old scales
+// are staged for the fix-up, the true scales committed; a flagged tensor's
+// stats counters are cleared (the fix-up recounts them).
+
+template <int MF, int VF, bool STATS>
+__global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc* __restrict__ descs,
+                                                                const uint2* __restrict__ part_amax,
+                                                                uint32_t* __restrict__ amax,
+                                                                float* __restrict__ old_scale,
+                                                                int32_t* __restrict__ flags,
+                                                                unsigned long long* __restrict__ counters,
+                                                                int chunk_log2, float grow_m, float grow_v) {
+  const int t = blockIdx.x;
+  const TensorDesc d = descs[t];
+  const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
+  const int64_t part0 = d.chunk0 << (chunk_log2 - kPartLog2);
+  uint32_t am = 0, av = 0;
+  for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
+    const uint2 pv = part_amax[part0 + k];
+    am = max(am, pv.x);
+    av = max(av, pv.y);
+  }
+  __shared__ uint32_t red[2][kReduceThreads / 64];
+  __shared__ int32_t flag;
+  am = wave_max(am);
+  av = wave_max(av);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    red[0][wave] = am;
+    red[1][wave] = av;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kReduceThreads / 64; w++) {
+      am = max(am, red[0][w]);
+      av = max(av, red[1][w]);
+    }
+    int32_t f = 0;
+    if (d.numel > 0) {
+      const float so_m = ld_global<float>(d.sm), so_v = ld_global<float>(d.sv);
+      // the prediction the update pass used: from the previous amax, read before it is replaced
+      const uint32_t pm = predicted_scale_bits<MF>(amax[2 * t], so_m, grow_m);
+      const uint32_t pv = predicted_scale_bits<VF>(amax[2 * t + 1], so_v, grow_v);
+      float s_m, s_v, inv;
+      choose_scale<MF, 0>(am, s_m, inv);
+      choose_scale<VF, 0>(av, s_v, inv);
+      f = (__float_as_uint(s_m) != pm ? 1 : 0) | (__float_as_uint(s_v) != pv ? 2 : 0);
+      old_scale[2 * t] = so_m;
+      old_scale[2 * t + 1] = so_v;
+      st_global<float>(d.sm, s_m);
+      st_global<float>(d.sv, s_v);
+    }
+    amax[2 * t] = am;
+    amax[2 * t + 1] = av;
+    flags[t] = f;
+    flag = f;
+  }
+  __syncthreads();
+  if constexpr (STATS) {
+    // the fix-up recounts the underflow / saturation counts of a re-quantized moment
+    if (threadIdx.x == 0 && (flag & 1)) {
+      counters[(int64_t)t * kStatsPerTensor + kUnderM] = 0ull;
+      counters[(int64_t)t * kStatsPerTensor + kSatM] = 0ull;
+    }
+    if (threadIdx.x == 0 && (flag & 2)) {
+      counters[(int64_t)t * kStatsPerTensor + kUnderV] = 0ull;
+      counters[(int64_t)t * kStatsPerTensor + kSatV] = 0ull;
+    }
+  }
+}
+
+// One work-group per chunk of a flagged tensor (the others return at once):
+// recompute the mispredicted moment(s) from the gradient and the old codes in
+// the source buffer and requantize them with the true scales into the
+// destination buffer.  p is not touched: its update does not depend on the
+// scales.  Flag bit 0: m, bit 1: v.
+template <int FMT, bool STATS, bool IS_V>
+__device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDesc& d, uint8_t* dst,
+                                             int64_t start, int64_t end, float s_old, float inv_new,
+                                             uint32_t& under, uint32_t& sat) {
+  const uint8_t* src = IS_V ? d.v : d.m;
+  const int64_t gend = start + ((end - start) & ~(int64_t)3);
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
+    vu2 gg[kAmaxUnroll];
+    uint32_t cc[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) {
+        gg[u] = ld_stream<vu2, FP8ADAM_NT_AMAX != 0>(d.g + i);
+        cc[u] = ld_stream<uint32_t, FP8ADAM_NT_AMAX != 0>(src + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) {
+        const float g[4] = {bf16_lo(gg[u].x), bf16_hi(gg[u].x), bf16_lo(gg[u].y), bf16_hi(gg[u].y)};
+        float x[4], q[4];
+        decode4<FMT>(cc[u], x);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          float m1, v1;
+          // moment_update computes both moments; only the one being fixed is used
+          moment_update(c, g[j], x[j] * s_old, x[j] * s_old, m1, v1);
+          x[j] = IS_V ? v1 : m1;
+          q[j] = x[j] * inv_new;
+        }
+        const uint32_t w = encode4<FMT>(q[0], q[1], q[2], q[3]);
+        if constexpr (STATS) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            under += (x[j] != 0.0f && ((w >> (8 * j)) & 0x7Fu) == 0u);
+            sat += (fabsf(q[j]) > Format<FMT>::kMax);
+          }
+        }
+        st_global<uint32_t>(dst + i, w);
+      }
+    }
+  }
+  if (gend + threadIdx.x < end) {
+    const int64_t i = gend + threadIdx.x;
+    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+    const float x0 = decode1<FMT>(ld_global<uint8_t>(src + i)) * s_old;
+    float m1, v1;
+    moment_update(c, g, x0, x0, m1, v1);
+    const float x = IS_V ? v1 : m1;
+    const float q = x * inv_new;
+    const uint32_t code = encode1<FMT>(q);
+    if constexpr (STATS) {
+      under += (x != 0.0f && (code & 0x7Fu) == 0u);
+      sat += (fabsf(q) > Format<FMT>::kMax);
+    }
+    st_global<uint8_t>(dst + i, (uint8_t)code);
+  }
+}
+
+template <int MF, int VF, bool STATS>
+__global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict__ descs,
+                                                    const TensorDesc* __restrict__ dst_descs,
+                                                    const int32_t* __restrict__ chunk_tid,
+                                                    const uint32_t* __restrict__ amax,
+                                                    const float* __restrict__ old_scale,
+                                                    const int32_t* __restrict__ flags, StepConsts c,
+                                                    unsigned long long* __restrict__ counters, int chunk_log2) {
+  const int tid = chunk_tid[blockIdx.x];
+  const int32_t f = flags[tid];
+  if (!f) return;  // uniform for the work-group
+  const TensorDesc d = descs[tid];
+  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) << chunk_log2;
+  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
+  if (f & 1) {
+    float s, inv;
+    choose_scale<MF, 0>(amax[2 * tid], s, inv);
+    fixup_moment<MF, STATS, false>(c, d, dst_descs[tid].m, start, end, old_scale[2 * tid], inv, cnt[kUnderM],
+                                   cnt[kSatM]);
+  }
+  if (f & 2) {
+    float s, inv;
+    choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
+    fixup_moment<VF, STATS, true>(c, d, dst_descs[tid].v, start, end, old_scale[2 * tid + 1], inv, cnt[kUnderV],
+                                  cnt[kSatV]);
   }
   flush_counters<STATS>(counters, tid, cnt);
 }
@@ -678,11 +909,16 @@ struct fp8adam_ctx {
   int32_t n = 0;
   int64_t nchunks = 0;
   int chunk_log2 = kMaxChunkLog2;  // elements per chunk = 2^chunk_log2
-  TensorDesc* d_desc = nullptr;
+  int speculate_from = 4;          // first step t that runs the speculative schedule
+  int cur = 0;                     // code buffer holding the moments: 0 = m/v, 1 = m_alt/v_alt
+  int64_t nparts = 0;              // update / block work-groups
+  TensorDesc* d_desc = nullptr;    // [2][n]: descriptors with m/v, then with m_alt/v_alt
   int32_t* d_chunk_tid = nullptr;
   uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
   uint2* d_partial = nullptr;       // tensor mode: [nchunks] per-chunk amax of m', v'
+  uint2* d_part_amax = nullptr;     // speculative: [nparts] per-part amax of m', v'
   float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
+  int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   unsigned long long* d_counters = nullptr;  // [n][5]
   bool timing = false;
   std::vector<hipEvent_t> ev;  // pairs
@@ -706,6 +942,8 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_chunk_tid) (void)hipFree(c->d_chunk_tid);
   if (c->d_amax) (void)hipFree(c->d_amax);
   if (c->d_partial) (void)hipFree(c->d_partial);
+  if (c->d_part_amax) (void)hipFree(c->d_part_amax);
+  if (c->d_flags) (void)hipFree(c->d_flags);
   if (c->d_old_scale) (void)hipFree(c->d_old_scale);
   if (c->d_counters) (void)hipFree(c->d_counters);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
@@ -729,89 +967,108 @@ int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
 
 // ---- kernel dispatch over the template parameters ----
 
+const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d_desc + (size_t)which * c->n; }
+
 template <int MF, int VF>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, c->d_desc,
+  hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      c->d_chunk_tid, c->d_partial, k, c->chunk_log2);
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
 void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s, c->d_desc,
-                     c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2);
+  hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
+                     descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
+                     c->d_flags);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks << (c->chunk_log2 - kPartLog2))),
-                     dim3(kThreads), 0, s, c->d_desc, c->d_chunk_tid, c->d_amax, c->d_old_scale, k, c->d_counters,
-                     c->chunk_log2);
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC>), dim3((unsigned)c->nparts), dim3(kThreads), 0, s,
+                     descs_of(c, c->cur), descs_of(c, SPEC ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
+                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax);
+}
+
+template <int MF, int VF, bool STATS>
+void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
+                     descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
+                     c->chunk_log2, k.grow_m, k.grow_v);
+}
+
+template <int MF, int VF, bool STATS>
+void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_fixup<MF, VF, STATS>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, descs_of(c, c->cur),
+                     descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
+                     c->d_counters, c->chunk_log2);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)(c->nchunks << (c->chunk_log2 - kPartLog2))),
-                     dim3(kThreads), 0, s, c->d_desc, c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2);
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nparts), dim3(kThreads), 0, s,
+                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2);
+}
+
+// Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
+// 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up.
+#define TIMED(kind, call)                              \
+  do {                                                 \
+    int slot_;                                         \
+    if (int r_ = timed_begin(c, (kind), s, &slot_)) return r_; \
+    call;                                              \
+    if (int r_ = timed_end(c, slot_, s)) return r_;    \
+  } while (0)
+
+void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
+  hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
+                     dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
-int run_step_t(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  int slot;
+int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
-    if (STATS) {
-      if (int r = timed_begin(c, 4, s, &slot)) return r;
-      hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
-                         dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax,
-                         4 * (int64_t)c->n);
-      if (int r = timed_end(c, slot, s)) return r;
-    }
-    if (c->nchunks > 0) {
-      if (int r = timed_begin(c, 3, s, &slot)) return r;
-      launch_block<MF, VF, BF16P, STATS, SMODE>(c, k, s);
-      if (int r = timed_end(c, slot, s)) return r;
-    }
+    if (STATS) TIMED(4, launch_reset(c, 4 * (int64_t)c->n, s));
+    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE>(c, k, s)));
+  } else if (SMODE == 0 && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
+    if (STATS) TIMED(4, launch_reset(c, 0, s));
+    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, true>(c, k, s)));
+    TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
+    if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS>(c, k, s)));
+    c->cur = 1 - c->cur;
   } else {
-    if (c->nchunks > 0) {
-      if (int r = timed_begin(c, 0, s, &slot)) return r;
-      launch_amax<MF, VF>(c, k, s);
-      if (int r = timed_end(c, slot, s)) return r;
-    }
+    if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
-    if (int r = timed_begin(c, 2, s, &slot)) return r;
-    launch_reduce<MF, VF, SMODE, STATS>(c, s);
-    if (int r = timed_end(c, slot, s)) return r;
-    if (c->nchunks > 0) {
-      if (int r = timed_begin(c, 1, s, &slot)) return r;
-      launch_update<MF, VF, BF16P, STATS, SMODE>(c, k, s);
-      if (int r = timed_end(c, slot, s)) return r;
-    }
+    TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, s)));
+    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, false>(c, k, s)));
   }
   HIP_TRY(hipGetLastError());
   return 0;
 }
 
 template <int MF, int VF, bool BF16P, bool STATS>
-int run_step_s(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_t<MF, VF, BF16P, STATS, 0>(c, k, s)
-                                                 : run_step_t<MF, VF, BF16P, STATS, 1>(c, k, s);
+int run_step_s(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_t<MF, VF, BF16P, STATS, 0>(c, k, t, s)
+                                                 : run_step_t<MF, VF, BF16P, STATS, 1>(c, k, t, s);
 }
 
 template <int MF, int VF, bool BF16P>
-int run_step_b(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  return c->cfg.collect_stats ? run_step_s<MF, VF, BF16P, true>(c, k, s) : run_step_s<MF, VF, BF16P, false>(c, k, s);
+int run_step_b(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  return c->cfg.collect_stats ? run_step_s<MF, VF, BF16P, true>(c, k, t, s)
+                              : run_step_s<MF, VF, BF16P, false>(c, k, t, s);
 }
 
 template <int MF, int VF>
-int run_step_f(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  return c->cfg.master == FP8ADAM_MASTER_BF16 ? run_step_b<MF, VF, true>(c, k, s) : run_step_b<MF, VF, false>(c, k, s);
+int run_step_f(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  return c->cfg.master == FP8ADAM_MASTER_BF16 ? run_step_b<MF, VF, true>(c, k, t, s)
+                                              : run_step_b<MF, VF, false>(c, k, t, s);
 }
 
-int run_step(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+int run_step(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   const int mf = c->cfg.m_format, vf = c->cfg.v_format;
-  if (mf == 0 && vf == 1) return run_step_f<0, 1>(c, k, s);
-  if (mf == 1 && vf == 1) return run_step_f<1, 1>(c, k, s);
-  if (mf == 1 && vf == 0) return run_step_f<1, 0>(c, k, s);
-  return run_step_f<0, 0>(c, k, s);
+  if (mf == 0 && vf == 1) return run_step_f<0, 1>(c, k, t, s);
+  if (mf == 1 && vf == 1) return run_step_f<1, 1>(c, k, t, s);
+  if (mf == 1 && vf == 0) return run_step_f<1, 0>(c, k, t, s);
+  return run_step_f<0, 0>(c, k, t, s);
 }
 
 unsigned probe_grid(int64_t n, int per_thread) {
@@ -850,6 +1107,11 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       return fail(FP8ADAM_EINVAL, "bad scale_mode");
     if (cfg->master != FP8ADAM_MASTER_FP32 && cfg->master != FP8ADAM_MASTER_BF16)
       return fail(FP8ADAM_EINVAL, "bad master dtype");
+    if (cfg->schedule != FP8ADAM_SCHEDULE_TWO_PASS && cfg->schedule != FP8ADAM_SCHEDULE_SPECULATIVE)
+      return fail(FP8ADAM_EINVAL, "bad schedule");
+    const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
+    if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
+      return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
 
     // Chunk size: the largest power of two in [kPart, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
@@ -859,7 +1121,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     while (chunk_log2 > kPartLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
     const int64_t chunk = (int64_t)1 << chunk_log2;
 
-    std::vector<TensorDesc> desc((size_t)n);
+    std::vector<TensorDesc> desc(2 * (size_t)n);  // [m/v set][m_alt/v_alt set]
     std::vector<int32_t> chunk_tid;
     int64_t nchunks = 0;
     for (int32_t t = 0; t < n; t++) {
@@ -872,12 +1134,23 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         if (int r = check_aligned(T.grad, "grad", t)) return r;
         if (int r = check_aligned(T.m, "m", t)) return r;
         if (int r = check_aligned(T.v, "v", t)) return r;
-        if (!T.m_scale || ((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
+        if (((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
           return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
+        if (spec) {
+          if (!T.m_alt || !T.v_alt)
+            return fail(FP8ADAM_EINVAL, "the speculative schedule needs m_alt and v_alt (tensor " + std::to_string(t) + ")");
+          if (int r = check_aligned(T.m_alt, "m_alt", t)) return r;
+          if (int r = check_aligned(T.v_alt, "v_alt", t)) return r;
+        }
       }
       const int64_t nc = (T.numel + chunk - 1) / chunk;
       desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
                            T.numel, nchunks};
+      desc[(size_t)n + t] = desc[t];
+      if (spec) {
+        desc[(size_t)n + t].m = T.m_alt;
+        desc[(size_t)n + t].v = T.v_alt;
+      }
       if (((nchunks + nc) << (chunk_log2 - kPartLog2)) > (int64_t)INT32_MAX)
         return fail(FP8ADAM_EINVAL, "too many elements for one context");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
@@ -890,16 +1163,21 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->n = n;
     c->nchunks = nchunks;
     c->chunk_log2 = chunk_log2;
+    c->nparts = nchunks << (chunk_log2 - kPartLog2);
+    c->speculate_from = cfg->speculate_from_step > 0 ? cfg->speculate_from_step : 4;
     hipError_t e = hipGetDevice(&c->device);
     const size_t namax = (size_t)n * 4;
-    if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * (size_t)n);
+    if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * 2 * (size_t)n);
+    if (e == hipSuccess && spec) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nparts));
+    if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 2 * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
     if (e == hipSuccess)
-      e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * (size_t)n, hipMemcpyHostToDevice, stream);
+      e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * 2 * (size_t)n, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->d_flags, 0, sizeof(int32_t) * (size_t)n, stream);
     if (e == hipSuccess && nchunks > 0)
       e = hipMemcpyAsync(c->d_chunk_tid, chunk_tid.data(), sizeof(int32_t) * (size_t)nchunks, hipMemcpyHostToDevice,
                          stream);
@@ -940,7 +1218,13 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
     k.step_size = (float)((double)hp->lr / bc1);
     k.inv_bc2 = (float)(1.0 / bc2);
     k.eps = hp->eps;
-    return run_step(ctx, k, stream);
+    // growth of a moving average's bias (1 - beta^t) from step t-1 to t: the
+    // speculative schedule's prediction of how the amax moves
+    const double bc1_prev = 1.0 - pow((double)hp->beta1, (double)(hp->step - 1));
+    const double bc2_prev = 1.0 - pow((double)hp->beta2, (double)(hp->step - 1));
+    k.grow_m = bc1_prev > 0.0 ? (float)(bc1 / bc1_prev) : 1.0f;
+    k.grow_v = bc2_prev > 0.0 ? (float)(bc2 / bc2_prev) : 1.0f;
+    return run_step(ctx, k, hp->step, stream);
   } catch (...) {
     return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step");
   }
@@ -953,7 +1237,9 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
     std::vector<uint32_t> amax((size_t)n * 4, 0u);
     std::vector<unsigned long long> cnt((size_t)n * kStatsPerTensor, 0ull);
     std::vector<TensorDesc> desc((size_t)n);
+    std::vector<int32_t> flags((size_t)n, 0);
     const bool block = ctx->cfg.granularity == FP8ADAM_SCALE_BLOCK128;
+    HIP_TRY(hipMemcpyAsync(flags.data(), ctx->d_flags, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipMemcpyAsync(amax.data(), ctx->d_amax,
                            sizeof(uint32_t) * (size_t)n * (block ? 4 : 2), hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipMemcpyAsync(cnt.data(), ctx->d_counters, sizeof(unsigned long long) * cnt.size(),
@@ -991,6 +1277,7 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
       o.saturated_m = (int64_t)cnt[kStatsPerTensor * t + kSatM];
       o.saturated_v = (int64_t)cnt[kStatsPerTensor * t + kSatV];
       o.nonfinite = (int64_t)cnt[kStatsPerTensor * t + kNonFinite];
+      o.requantized = (int64_t)(((flags[t] & 1) ? 1 : 0) + ((flags[t] & 2) ? 1 : 0)) * desc[t].numel;
     }
     return 0;
   } catch (...) {
@@ -1001,6 +1288,8 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
 void fp8adam_destroy(fp8adam_ctx* ctx) { free_ctx(ctx); }
 
 int64_t fp8adam_num_chunks(const fp8adam_ctx* ctx) { return ctx ? ctx->nchunks : -1; }
+
+int32_t fp8adam_current_buffer(const fp8adam_ctx* ctx) { return ctx ? ctx->cur : -1; }
 
 int fp8adam_set_timing(fp8adam_ctx* ctx, int32_t enable) {
   try {

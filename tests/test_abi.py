@@ -76,3 +76,22 @@ def test_product_path_does_not_import_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "liboracle" not in text and "fp8adam_oracle" not in text, path
+
+
+def test_speculative_schedule_argument_errors():
+    """The speculative schedule needs per-tensor POW2 scales and both code
+    buffers; these are rejected before any device work."""
+    L = pk.load()
+    h = ctypes.c_void_p()
+    no_alt = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, None, None))
+    alt = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, 112, 128))
+    cfg = pk.ConfigArg(0, 1, 0, 0, 0, 0, pk.SCHEDULE_SPECULATIVE, 0)
+    assert L.fp8adam_init(ctypes.byref(h), no_alt, 1, ctypes.byref(cfg), None) == -1
+    assert "m_alt" in pk.fp8adam_last_error()
+    for bad in (pk.ConfigArg(0, 1, pk.SCALE_BLOCK128, 0, 0, 0, pk.SCHEDULE_SPECULATIVE, 0),
+                pk.ConfigArg(0, 1, 0, pk.SCALE_AMAX, 0, 0, pk.SCHEDULE_SPECULATIVE, 0),
+                pk.ConfigArg(0, 1, 0, 0, 0, 0, 7, 0)):
+        assert L.fp8adam_init(ctypes.byref(h), alt, 1, ctypes.byref(bad), None) == -1
+    misaligned = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, 113, 128))
+    assert L.fp8adam_init(ctypes.byref(h), misaligned, 1, ctypes.byref(cfg), None) == -2
+    assert L.fp8adam_current_buffer(None) == -1

@@ -1,0 +1,122 @@
+"""The speculative schedule (one update pass quantizing with the previous
+power-of-two scale into the other code buffer, then a per-tensor check and a
+re-quantization of the tensors whose scale changed) against the two-pass
+schedule (bit for bit) and against the CPU oracle."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import precision_adam_optimizer_amd as pk
+import workloads
+from tests.gpu_util import np_host, random_grad
+from tests.test_gpu_parity import FORMATS, SIZES, run_full, run_small
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def drifting_grad(n, seed, t, i, dev):
+    """Gradient whose tensor-level scale jumps by a random power of two (-2..+2
+    binades) from step to step, so the per-tensor scales both keep and change."""
+    g = torch.Generator()
+    g.manual_seed(seed * 1000 + t * 31 + i)
+    shift = int(torch.randint(-2, 3, (1,), generator=g))
+    return (random_grad(n, seed * 7 + t * 13 + i, dev).float() * 2.0 ** shift).to(torch.bfloat16)
+
+
+def _run(schedule, sizes, steps, seed, master=torch.float32, spec_from=2):
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    params = [(torch.randn(n, generator=gen, device=dev) * 0.02).to(master) for n in sizes]
+    grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in sizes]
+    opt = pk.FP8AdamW(params, grads, collect_stats=True, schedule=schedule, speculate_from_step=spec_from)
+    hist = []
+    for t in range(1, steps + 1):
+        for i, n in enumerate(sizes):
+            grads[i].copy_(drifting_grad(n, seed, t, i, dev))
+        opt.step(step=t, **HP)
+        torch.cuda.synchronize()
+        st = opt.stats()
+        hist.append(([np_host(p) for p in params], [np_host(m) for m in opt.m], [np_host(v) for v in opt.v],
+                     [np_host(s) for s in opt.m_scale], [np_host(s) for s in opt.v_scale], st))
+    opt.close()
+    return hist
+
+
+@pytest.mark.parametrize("master", [torch.float32, torch.bfloat16])
+def test_speculative_equals_two_pass_bitwise(master):
+    sizes = SIZES + [300_001]
+    a = _run("two_pass", sizes, 10, seed=3, master=master)
+    b = _run("speculative", sizes, 10, seed=3, master=master)
+    requant_steps, clean_steps = 0, 0
+    for t, (x, y) in enumerate(zip(a, b), start=1):
+        for kind, xs, ys in zip(("p", "m", "v", "m_scale", "v_scale"), x[:5], y[:5]):
+            for i, (u, w) in enumerate(zip(xs, ys)):
+                assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), f"step {t}: {kind} of tensor {i} differs"
+        for i, (sa, sb) in enumerate(zip(x[5], y[5])):
+            for k in ("amax_m", "amax_v", "scale_m", "scale_v", "underflow_m", "underflow_v", "saturated_m",
+                      "saturated_v", "nonfinite"):
+                assert np.float64(sa[k]) == np.float64(sb[k]) or (np.isnan(sa[k]) and np.isnan(sb[k])), \
+                    f"step {t} tensor {i}: stat {k} {sa[k]} vs {sb[k]}"
+            assert sa["requantized"] == 0
+        rq = sum(s["requantized"] for s in y[5])
+        if t >= 2:
+            requant_steps += rq > 0
+            clean_steps += rq < 2 * sum(sizes)  # (element, moment) pairs
+    # both paths of the speculative schedule ran
+    assert requant_steps > 0 and clean_steps > 0
+
+
+SPEC_COMBOS = list(itertools.product(FORMATS, ["fp32", "bf16"]))
+
+
+@pytest.mark.parametrize("combo", SPEC_COMBOS, ids=[f"{a}-{b}_{m}" for (a, b), m in SPEC_COMBOS])
+def test_speculative_vs_oracle_ragged(combo):
+    fmts, master = combo
+    k = SPEC_COMBOS.index(combo)
+    # random mid-training state (predictions mostly wrong) and zero state (mixed)
+    rq = run_small(fmts, "tensor", "pow2", master, collect_stats=True, random_init=(k % 2 == 0), steps=5,
+                   seed=40 + k, schedule="speculative", speculate_from_step=2)
+    assert rq > 0
+
+
+def test_speculative_resume_is_bit_exact():
+    sizes = [50_001, 4096, 3]
+    ref = _run("speculative", sizes, 7, seed=5)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    params = [torch.randn(n, generator=gen, device=dev) * 0.02 for n in sizes]
+    grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in sizes]
+    opt = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2)
+    for t in range(1, 5):
+        for i, n in enumerate(sizes):
+            grads[i].copy_(drifting_grad(n, 5, t, i, dev))
+        opt.step(step=t, **HP)
+    torch.cuda.synchronize()
+    state = ([m.clone() for m in opt.m], [v.clone() for v in opt.v], [s.clone() for s in opt.m_scale],
+             [s.clone() for s in opt.v_scale])
+    opt.close()
+    opt2 = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2, state=state)
+    for t in range(5, 8):
+        for i, n in enumerate(sizes):
+            grads[i].copy_(drifting_grad(n, 5, t, i, dev))
+        opt2.step(step=t, **HP)
+    torch.cuda.synchronize()
+    final = ([np_host(p) for p in params], [np_host(m) for m in opt2.m], [np_host(v) for v in opt2.v])
+    opt2.close()
+    for xs, ys in zip(ref[-1][:3], final):
+        for u, w in zip(xs, ys):
+            assert np.array_equal(u.view(np.uint8), w.view(np.uint8))
+
+
+@pytest.mark.timeout(900)
+def test_llama2_7b_speculative_full_size():
+    w = workloads.llama2_7b()
+    n = len(w.shapes)
+    sample = [0] + list(range(1 + 9 * 31, 1 + 9 * 32)) + [n - 2, n - 1]
+    run_full(w, steps=4, sample=sample, collect_stats=True, schedule="speculative", speculate_from_step=2)

@@ -161,7 +161,7 @@ def make_grad(w: Workload, tidx: int, shape, step: int, device, base_seed: int =
         c = torch.randn(3, n, generator=g, device=device, dtype=torch.float32)
         z = z / torch.sqrt((c * c).sum(0) / 3.0)
     lo, hi = math.log10(w.grad_scale[0]), math.log10(w.grad_scale[1])
-    gs = _gen(device, seed_for(base_seed, tidx, step, "gscale"))
+    gs = _gen(device, seed_for(base_seed, tidx, 0, "gscale"))  # a property of the tensor, fixed across steps
     if w.grad_scale_per == "row" and len(shape) == 2:
         rows = shape[0]
         sc = 10.0 ** (lo + (hi - lo) * torch.rand(rows, generator=gs, device=device, dtype=torch.float64))
