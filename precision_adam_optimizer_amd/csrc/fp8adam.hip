@@ -26,8 +26,8 @@
 //     k_fixup   : flagged tensors only: recompute m', v' from the old codes
 //                 (still intact in the source buffer) and requantize
 //   per-128-element scales (one streaming pass)
-//     k_block   : eight lanes own one 128-element block; the block amax is a
-//                 3-step DPP max, then update and requantize as above
+//     k_block   : 32 lanes own one 128-element block; the block amax is a
+//                 5-step DPP/swizzle max, then update and requantize as above
 // The chunk table (built once at init) cuts every tensor into chunks of
 // 2^chunk_log2 elements (4096..32768, chosen per context so that even small
 // lists give a few thousand work-groups); an amax-pass work-group owns one
@@ -76,10 +76,10 @@ namespace {
 #define FP8ADAM_NT_UPDATE_ST 1
 #endif
 #ifndef FP8ADAM_NT_BLOCK_LD
-#define FP8ADAM_NT_BLOCK_LD 0
+#define FP8ADAM_NT_BLOCK_LD 1
 #endif
 #ifndef FP8ADAM_NT_BLOCK_ST
-#define FP8ADAM_NT_BLOCK_ST 0
+#define FP8ADAM_NT_BLOCK_ST 1
 #endif
 
 constexpr int kThreads = 256;                     // 4 waves of 64
@@ -121,15 +121,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
-  return x;
-}
-
-// Max over each group of 8 consecutive lanes with DPP (quad swaps, then the
-// half-row mirror); every lane of the group ends with the group max.
-__device__ __forceinline__ uint32_t group8_max(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
   return x;
 }
 
@@ -685,17 +676,27 @@ __global__ __launch_bounds__(kThreads) void k_reset(unsigned long long* __restri
 
 // ------------------------------------------------------------ block-128 mode
 //
-// Wave layout: lanes 8b..8b+7 own block b of the wave's 8 consecutive blocks
-// (1024 elements).  Lane l of a block touches elements 32*j + 4*l .. +3 for
-// j = 0..3, so each access of the wave covers 32 contiguous elements of every
-// block.  The block amax is the max of the lane's 16 values, then a DPP max
-// over the 8 lanes.
+// 32 lanes own one 128-element block, each lane 4
+// consecutive elements per access, so every access of the wave covers two
+// whole blocks (a full 128-byte line of codes per block and moment; a layout
+// with 8 lanes x 16 elements per block wrote 32-byte pieces of each line and
+// ran ~4% slower).  The block amax is a 5-step max over the 32 lanes (DPP
+// within 16 lanes, then a swizzle across the two 16-lane rows).
+
+__device__ __forceinline__ uint32_t group32_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F));                          // lane ^ 16
+  return x;
+}
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
-                                                    const int32_t* __restrict__ chunk_tid, StepConsts c,
-                                                    unsigned long long* __restrict__ counters,
-                                                    uint32_t* __restrict__ amax, int chunk_log2) {
+                                                      const int32_t* __restrict__ chunk_tid, StepConsts c,
+                                                      unsigned long long* __restrict__ counters,
+                                                      uint32_t* __restrict__ amax, int chunk_log2) {
   const int split_log2 = chunk_log2 - kPartLog2;
   const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
   const int tid = chunk_tid[chunk];
@@ -704,130 +705,112 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
                         ((int64_t)(blockIdx.x & ((1u << split_log2) - 1u)) << kPartLog2);
   const int64_t end = min(start + kPart, d.numel);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane & 7, bw = lane >> 3;
+  const int half = lane >> 5, hl = lane & 31;
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
-  uint32_t tam = 0, tav = 0;  // tensor-wide amax, for stats
+  uint32_t tam = 0, tav = 0;
   float tsm = 0.0f, tsv = 0.0f;
 
   for (int64_t tile = start; tile < end; tile += (int64_t)kBlock * 32) {
-    const int64_t b0 = tile + (int64_t)(wave * 8 + bw) * kBlock;  // this lane's block start
-    const bool exists = b0 < end;
-    const bool full = b0 + kBlock <= end;
-    const int64_t blk = b0 / kBlock;
-    float sm = 1.0f, sv = 1.0f;
-    if (exists) {
-      sm = ld_global<float>(d.sm + blk);
-      sv = ld_global<float>(d.sv + blk);
-    }
-    float m1[16], v1[16], p[16];
+    int64_t b0[4];
+    bool ex[4], full[4];
+    float sm[4], sv[4];
     Group G[4];
-    if (full) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0 + 32 * j + 4 * sub, G[j], true);
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        float a[4], b[4], q[4];
-        fresh_moments<MF, VF>(c, G[j], sm, sv, a, b);
-        unpack_p<BF16P>(G[j], q);
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          m1[4 * j + r] = a[r];
-          v1[4 * j + r] = b[r];
-          p[4 * j + r] = q[r];
-        }
+    for (int j = 0; j < 4; j++) {
+      b0[j] = tile + (int64_t)(wave * 8 + 2 * j + half) * kBlock;
+      ex[j] = b0[j] < end;
+      full[j] = b0[j] + kBlock <= end;
+      sm[j] = 1.0f;
+      sv[j] = 1.0f;
+      if (ex[j]) {
+        sm[j] = ld_global<float>(d.sm + b0[j] / kBlock);
+        sv[j] = ld_global<float>(d.sv + b0[j] / kBlock);
       }
-    } else {
+      if (full[j]) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0[j] + 4 * hl, G[j], true);
+    }
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < 4; j++) {
+      float m1[4], v1[4], p[4];
+      const int64_t i0 = b0[j] + 4 * hl;
+      if (full[j]) {
+        fresh_moments<MF, VF>(c, G[j], sm[j], sv[j], m1, v1);
+        unpack_p<BF16P>(G[j], p);
+      } else {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int64_t i = b0 + 32 * j + 4 * sub + r;
+          const int64_t i = i0 + r;
           float a = 0.0f, b = 0.0f, q = 0.0f;
-          if (exists && i < end) {
+          if (ex[j] && i < end) {
             const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
-            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, a, b);
+            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm[j],
+                          decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv[j], a, b);
             q = load_p1<BF16P>(d, i);
           }
-          m1[4 * j + r] = a;
-          v1[4 * j + r] = b;
-          p[4 * j + r] = q;
+          m1[r] = a;
+          v1[r] = b;
+          p[r] = q;
         }
       }
-    }
-    uint32_t am = 0, av = 0;
+      uint32_t am = 0, av = 0;
 #pragma unroll
-    for (int k = 0; k < 16; k++) {
-      am = max(am, abs_bits(m1[k]));
-      av = max(av, abs_bits(v1[k]));
-    }
-    am = group8_max(am);
-    av = group8_max(av);
-    float nsm, ism, nsv, isv;
-    choose_scale<MF, SMODE>(am, nsm, ism);
-    choose_scale<VF, SMODE>(av, nsv, isv);
-    if constexpr (STATS) {
-      if (exists) {
-        tam = max(tam, am);
-        tav = max(tav, av);
-        tsm = fmaxf(tsm, nsm);
-        tsv = fmaxf(tsv, nsv);
+      for (int r = 0; r < 4; r++) {
+        am = max(am, abs_bits(m1[r]));
+        av = max(av, abs_bits(v1[r]));
       }
-    }
-#pragma unroll
-    for (int k = 0; k < 16; k++) p[k] = param_update(c, p[k], m1[k], v1[k]);
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        float qm[4], qv[4], pj[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          qm[r] = m1[4 * j + r] * ism;
-          qv[r] = v1[4 * j + r] * isv;
-          pj[r] = p[4 * j + r];
+      am = group32_max(am);
+      av = group32_max(av);
+      float nsm, ism, nsv, isv;
+      choose_scale<MF, SMODE>(am, nsm, ism);
+      choose_scale<VF, SMODE>(av, nsv, isv);
+      if constexpr (STATS) {
+        if (ex[j]) {
+          tam = max(tam, am);
+          tav = max(tav, av);
+          tsm = fmaxf(tsm, nsm);
+          tsv = fmaxf(tsv, nsv);
         }
+      }
+      float qm[4], qv[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        p[r] = param_update(c, p[r], m1[r], v1[r]);
+        qm[r] = m1[r] * ism;
+        qv[r] = v1[r] * isv;
+      }
+      if (full[j]) {
         const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
         const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
         if constexpr (STATS) {
 #pragma unroll
           for (int r = 0; r < 4; r++)
-            count_element<MF, VF, STATS>(cnt, m1[4 * j + r], v1[4 * j + r], qm[r], qv[r], wm >> (8 * r),
-                                         wv >> (8 * r));
+            count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], wm >> (8 * r), wv >> (8 * r));
         }
-        const int64_t i = b0 + 32 * j + 4 * sub;
-        store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i, pj);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i, wm);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i, wv);
-      }
-    } else if (exists) {
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
+        store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i0, p);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i0, wm);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i0, wv);
+      } else if (ex[j]) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-          const int64_t i = b0 + 32 * j + 4 * sub + r;
+          const int64_t i = i0 + r;
           if (i < end) {
-            const int k = 4 * j + r;
-            const float qm = m1[k] * ism, qv = v1[k] * isv;
-            const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
-            count_element<MF, VF, STATS>(cnt, m1[k], v1[k], qm, qv, cm, cv);
-            store_p1<BF16P>(d, i, p[k]);
+            const uint32_t cm = encode1<MF>(qm[r]), cv = encode1<VF>(qv[r]);
+            count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], cm, cv);
+            store_p1<BF16P>(d, i, p[r]);
             st_global<uint8_t>(d.m + i, (uint8_t)cm);
             st_global<uint8_t>(d.v + i, (uint8_t)cv);
           }
         }
       }
-    }
-    if (exists && sub == 0) {
-      st_global<float>(d.sm + blk, nsm);
-      st_global<float>(d.sv + blk, nsv);
+      if (ex[j] && hl == 0) {
+        st_global<float>(d.sm + b0[j] / kBlock, nsm);
+        st_global<float>(d.sv + b0[j] / kBlock, nsv);
+      }
     }
   }
   if constexpr (STATS) {
     flush_counters<STATS>(counters, tid, cnt);
-    // tensor-wide amax for the stats (scales follow from it); non-negative floats order as u32
     uint32_t sa = __float_as_uint(tsm), sb = __float_as_uint(tsv);
-    uint32_t a = tam, b = tav;
-    a = wave_max(a);
-    b = wave_max(b);
+    uint32_t a = wave_max(tam), b = wave_max(tav);
     sa = wave_max(sa);
     sb = wave_max(sb);
     if (lane == 0) {
