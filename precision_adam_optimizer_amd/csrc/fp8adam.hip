@@ -78,6 +78,9 @@ namespace {
 #ifndef FP8ADAM_NT_BLOCK_LD
 #define FP8ADAM_NT_BLOCK_LD 1
 #endif
+#ifndef FP8ADAM_XCD_ORDER
+#define FP8ADAM_XCD_ORDER 1  // update / block passes: each XCD walks its own contiguous eighth
+#endif
 #ifndef FP8ADAM_NT_BLOCK_ST
 #define FP8ADAM_NT_BLOCK_ST 1
 #endif
@@ -123,6 +126,33 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
   return x;
 }
+
+// Logical work item (chunk or part) of this work-group.  Work-groups are
+// dispatched round-robin over the 8 XCDs (work-group b runs on XCD b % 8).
+// In XCD order, work-group b takes item (b % 8) * ceil(n/8) + b / 8, so each
+// XCD streams through its own contiguous eighth of the list (measured: update
+// pass -3%, block pass -5%); the grid is then 8 * ceil(n/8) and a surplus
+// work-group gets -1 (returns at once).  The amax pass and the fix-up keep
+// the linear order (XCD order measured +4% there, and it would put a flagged
+// tensor's chunks on few XCDs).
+template <bool XCD>
+__device__ __forceinline__ int64_t work_index(int64_t n) {
+  if constexpr (XCD) {
+    const int64_t per = (n + 7) >> 3;
+    const int64_t w = (int64_t)(blockIdx.x & 7u) * per + (int64_t)(blockIdx.x >> 3);
+    return w < n ? w : -1;
+  } else {
+    (void)n;
+    return (int64_t)blockIdx.x;
+  }
+}
+
+template <bool XCD>
+inline unsigned grid_for(int64_t n) {
+  return XCD ? (unsigned)(((n + 7) >> 3) << 3) : (unsigned)n;
+}
+
+constexpr bool kXcdStreams = FP8ADAM_XCD_ORDER != 0;  // update and block passes
 
 // Work-group max of two values; result valid in thread 0.
 __device__ __forceinline__ void block_max2(uint32_t& a, uint32_t& b) {
@@ -297,10 +327,13 @@ __device__ __forceinline__ float inverse_pow2(uint32_t pow2_bits) {
 template <int MF, int VF>
 __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ chunk_tid,
-                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2) {
-  const int tid = chunk_tid[blockIdx.x];
+                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2,
+                                                   int64_t nwork) {
+  const int64_t w = work_index<false>(nwork);
+  if (w < 0) return;
+  const int tid = chunk_tid[w];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) << chunk_log2;
+  const int64_t start = (w - d.chunk0) << chunk_log2;
   const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
   const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
   const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
@@ -337,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
     av = max(av, abs_bits(v1));
   }
   block_max2(am, av);
-  if (threadIdx.x == 0) partial[blockIdx.x] = make_uint2(am, av);
+  if (threadIdx.x == 0) partial[w] = make_uint2(am, av);
 }
 
 // ------------------------------------------------------------------ reduce
@@ -405,13 +438,14 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
                                                      const uint32_t* __restrict__ amax,
                                                      const float* __restrict__ old_scale, StepConsts c,
                                                      unsigned long long* __restrict__ counters, int chunk_log2,
-                                                     uint2* __restrict__ part_amax) {
+                                                     uint2* __restrict__ part_amax, int64_t nwork) {
+  const int64_t w = work_index<kXcdStreams>(nwork);
+  if (w < 0) return;
   const int split_log2 = chunk_log2 - kPartLog2;
-  const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
+  const int64_t chunk = w >> split_log2;
   const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((chunk - d.chunk0) << chunk_log2) +
-                        ((int64_t)(blockIdx.x & ((1u << split_log2) - 1u)) << kPartLog2);
+  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << kPartLog2);
   const int64_t end = min(start + kPart, d.numel);
   if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
@@ -491,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   flush_counters<STATS>(counters, tid, cnt);
   if constexpr (SPEC) {
     block_max2(am, av);
-    if (threadIdx.x == 0) part_amax[blockIdx.x] = make_uint2(am, av);
+    if (threadIdx.x == 0) part_amax[w] = make_uint2(am, av);
   }
 }
 
@@ -642,12 +676,15 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
                                                     const uint32_t* __restrict__ amax,
                                                     const float* __restrict__ old_scale,
                                                     const int32_t* __restrict__ flags, StepConsts c,
-                                                    unsigned long long* __restrict__ counters, int chunk_log2) {
-  const int tid = chunk_tid[blockIdx.x];
+                                                    unsigned long long* __restrict__ counters, int chunk_log2,
+                                                    int64_t nwork) {
+  const int64_t w = work_index<false>(nwork);
+  if (w < 0) return;
+  const int tid = chunk_tid[w];
   const int32_t f = flags[tid];
   if (!f) return;  // uniform for the work-group
   const TensorDesc d = descs[tid];
-  const int64_t start = ((int64_t)blockIdx.x - d.chunk0) << chunk_log2;
+  const int64_t start = (w - d.chunk0) << chunk_log2;
   const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
   if (f & 1) {
@@ -696,13 +733,14 @@ template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
                                                       const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                       unsigned long long* __restrict__ counters,
-                                                      uint32_t* __restrict__ amax, int chunk_log2) {
+                                                      uint32_t* __restrict__ amax, int chunk_log2, int64_t nwork) {
+  const int64_t w = work_index<kXcdStreams>(nwork);
+  if (w < 0) return;
   const int split_log2 = chunk_log2 - kPartLog2;
-  const int64_t chunk = (int64_t)blockIdx.x >> split_log2;
+  const int64_t chunk = w >> split_log2;
   const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((chunk - d.chunk0) << chunk_log2) +
-                        ((int64_t)(blockIdx.x & ((1u << split_log2) - 1u)) << kPartLog2);
+  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << kPartLog2);
   const int64_t end = min(start + kPart, d.numel);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, hl = lane & 31;
@@ -954,8 +992,8 @@ const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d_desc +
 
 template <int MF, int VF>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_amax<MF, VF>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2);
+  hipLaunchKernelGGL((k_amax<MF, VF>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
+                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks);
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
@@ -967,9 +1005,9 @@ void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC>), dim3((unsigned)c->nparts), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, SPEC ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax);
+                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts);
 }
 
 template <int MF, int VF, bool STATS>
@@ -981,15 +1019,15 @@ void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 
 template <int MF, int VF, bool STATS>
 void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_fixup<MF, VF, STATS>), dim3((unsigned)c->nchunks), dim3(kThreads), 0, s, descs_of(c, c->cur),
+  hipLaunchKernelGGL((k_fixup<MF, VF, STATS>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
-                     c->d_counters, c->chunk_log2);
+                     c->d_counters, c->chunk_log2, c->nchunks);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3((unsigned)c->nparts), dim3(kThreads), 0, s,
-                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2);
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts);
 }
 
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
