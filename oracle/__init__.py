@@ -47,6 +47,7 @@ class Config(ctypes.Structure):
         ("step", ctypes.c_int64),
         ("m_fmt", ctypes.c_int), ("v_fmt", ctypes.c_int),
         ("block", ctypes.c_int), ("scale_mode", ctypes.c_int), ("master_bf16", ctypes.c_int),
+        ("l2_coupled", ctypes.c_int),
     ]
 
 
@@ -156,9 +157,9 @@ class Hyper:
 
 
 def make_config(h: Hyper, m_fmt=E4M3, v_fmt=E5M2, block: int = 0,
-                scale_mode: int = SCALE_POW2, master_bf16: bool = False) -> Config:
+                scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False) -> Config:
     return Config(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step,
-                  fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16))
+                  fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled))
 
 
 def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,

@@ -47,7 +47,12 @@
  *    v' = fma(b2, v, (1-b2)*(g*g)).
  *  - Bias correction 1 - beta^t with the caller's 1-based t; weight decay is
  *    decoupled (AdamW) and applied to the old p; p is updated from the fresh
- *    (unquantized) m', v'.  The parameter update is evaluated in fp64 and
+ *    (unquantized) m', v'.
+ *  - Coupled-L2 variant (l2_coupled): the L2 term of an L2-regularised loss
+ *    enters the gradient instead, g_eff = fma(wd, p, g) in fp32 with the old
+ *    p, and there is no decoupled decay.  [P1] "Why the SwiGLU weights align",
+ *    Theorem 1 set-up: the training objective (Eq. 1) is the loss plus an L2
+ *    penalty on the weights.  The parameter update is evaluated in fp64 and
  *    rounded once to the master dtype (fp32, or bf16 round-to-nearest-even).
  *
  * Build: plain C11, no SIMD intrinsics, -ffp-contract=off.
@@ -224,6 +229,7 @@ typedef struct {
     int block;        /* 0: one scale per tensor; else block length (128) */
     int scale_mode;   /* REF_SCALE_POW2 / REF_SCALE_AMAX */
     int master_bf16;  /* 0: p is fp32; 1: p is bf16 bits */
+    int l2_coupled;   /* 0: decoupled decay (AdamW); 1: wd * p added to the gradient */
 } ref_config;
 
 typedef struct {
@@ -238,6 +244,7 @@ typedef struct {
  * (fp32 values, widened exactly). */
 typedef struct {
     float b1, b2, omb1, omb2;     /* fp32, for the moment update */
+    float l2;                     /* coupled-L2 coefficient (0 when decoupled) */
     double decay, step_size, bc2, eps;
 } ref_consts;
 
@@ -250,7 +257,8 @@ static ref_consts make_consts(const ref_config *c)
     k.omb2 = 1.0f - c->beta2;
     double bc1 = 1.0 - pow((double)c->beta1, (double)c->step);
     k.bc2 = 1.0 - pow((double)c->beta2, (double)c->step);
-    k.decay = 1.0 - (double)c->lr * (double)c->weight_decay;
+    k.l2 = c->l2_coupled ? c->weight_decay : 0.0f;
+    k.decay = c->l2_coupled ? 1.0 : 1.0 - (double)c->lr * (double)c->weight_decay;
     k.step_size = (double)c->lr / bc1;
     k.eps = (double)c->eps;
     return k;
@@ -264,6 +272,13 @@ static double param_update(const ref_consts *k, double p, float m1, float v1)
     double mhat_num = (double)m1;
     double denom = sqrt((double)v1 / k->bc2) + k->eps;
     return p * k->decay - k->step_size * mhat_num / denom;
+}
+
+/* Gradient seen by the moments: g itself, or g + wd * p in the coupled-L2
+ * variant (one fp32 rounding). */
+static float effective_grad(const ref_consts *k, float g, float p)
+{
+    return k->l2 != 0.0f ? fmaf(k->l2, p, g) : g;
 }
 
 /* [P1 "Adam's update makes the needs asymmetric"]  m moving average of g,
@@ -317,7 +332,8 @@ int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
         /* 1. dequantize and update the moments; track the block's amax */
         float am = 0.0f, av = 0.0f;
         for (int64_t i = lo; i < hi; i++) {
-            float gi = bf16_to_f32(g[i]);
+            float pi = c->master_bf16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+            float gi = effective_grad(&k, bf16_to_f32(g[i]), pi);
             float mi = ref_decode(c->m_fmt, cm[i]) * old_sm;
             float vi = ref_decode(c->v_fmt, cv[i]) * old_sv;
             moment_update(&k, gi, mi, vi, &m1[i], &v1[i]);
@@ -382,7 +398,7 @@ int ref_step_fp32_moments(const ref_config *c, int64_t n, float *p, const uint16
     ref_consts k = make_consts(c);
     for (int64_t i = 0; i < n; i++) {
         float m1, v1;
-        moment_update(&k, bf16_to_f32(g[i]), m[i], v[i], &m1, &v1);
+        moment_update(&k, effective_grad(&k, bf16_to_f32(g[i]), p[i]), m[i], v[i], &m1, &v1);
         p[i] = (float)param_update(&k, (double)p[i], m1, v1);
         m[i] = m1;
         v[i] = v1;

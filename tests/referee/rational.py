@@ -11,6 +11,8 @@ The step it computes is the one the oracle documents: dequantize (code times
 scale), m' = b1*m + (1-b1)*g and v' = b2*v + (1-b2)*g*g in fp32 with one
 rounding for the multiply-add, new scale from the amax of m' / v', requantize
 with x * inv_scale, and p' = p*(1 - lr*wd) - lr/(1-b1^t) * m' / (sqrt(v'/(1-b2^t)) + eps).
+With l2_coupled the gradient is g + wd*p (one fp32 rounding) and there is no
+decoupled decay.
 """
 from __future__ import annotations
 
@@ -168,7 +170,7 @@ def param_update(p: float, m1: float, v1: float, lr: float, b1: float, b2: float
 def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[float],
          sv: list[float], *, lr: float, b1: float, b2: float, eps: float, wd: float, t: int,
          m_fmt: int = 0, v_fmt: int = 1, block: int = 0, amax_mode: bool = False,
-         master_bf16: bool = False):
+         master_bf16: bool = False, l2_coupled: bool = False):
     """Returns new (p, cm, cv, sm, sv). All floats are values already exact in
     their storage type (fp32, or bf16 for g and a bf16 master)."""
     n = len(p)
@@ -185,8 +187,9 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
         for i in range(lo, hi):
             m = mul32(dequant(m_fmt, cm[i]), sm[si])
             v = mul32(dequant(v_fmt, cv[i]), sv[si])
-            m1 = fma32(b1, m, mul32(omb1, g[i]))
-            v1 = fma32(b2, v, mul32(omb2, mul32(g[i], g[i])))
+            gi = fma32(wd, p[i], g[i]) if l2_coupled else g[i]
+            m1 = fma32(b1, m, mul32(omb1, gi))
+            v1 = fma32(b2, v, mul32(omb2, mul32(gi, gi)))
             m1s.append(m1)
             v1s.append(v1)
         am = max((abs(x) for x in m1s), default=0.0)
@@ -196,7 +199,7 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
         for j, i in enumerate(range(lo, hi)):
             cm2[i] = quantize(m_fmt, mul32(m1s[j], nism))
             cv2[i] = quantize(v_fmt, mul32(v1s[j], nisv))
-            exact = param_update(p[i], m1s[j], v1s[j], lr, b1, b2, eps, wd, t)
+            exact = param_update(p[i], m1s[j], v1s[j], lr, b1, b2, eps, 0.0 if l2_coupled else wd, t)
             p2[i] = round_bf16(exact) if master_bf16 else round_f32(exact)
         sm2[si], sv2[si] = nsm, nsv
     return p2, cm2, cv2, sm2, sv2

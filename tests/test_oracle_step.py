@@ -94,6 +94,38 @@ def test_fp32_moments_match_torch_adamw():
     assert np.allclose(p, ref, rtol=1e-6, atol=1e-6 * f32(h.lr))
 
 
+def test_fp32_moments_coupled_l2_match_torch_adam():
+    """Coupled L2 (the L2-regularised objective): torch.optim.Adam's weight_decay
+    adds wd*p to the gradient, as the oracle's l2_coupled variant does."""
+    n = 300
+    rng = np.random.default_rng(2)
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    tp = torch.tensor(p0.astype(np.float64), requires_grad=True)
+    opt = torch.optim.Adam([tp], lr=f32(h.lr), betas=(f32(h.beta1), f32(h.beta2)), eps=f32(h.eps),
+                           weight_decay=f32(h.weight_decay))
+    p = p0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    for t in range(1, 11):
+        g = bf16_bits(rng.standard_normal(n) * 10.0 ** rng.uniform(-5, -1, n))
+        h.step = t
+        oracle.step_fp32_moments(oracle.make_config(h, l2_coupled=True), p, g, m, v)
+        tp.grad = torch.tensor(bf16_vals(g).astype(np.float64))
+        opt.step()
+    ref = tp.detach().numpy()
+    assert np.allclose(p, ref, rtol=1e-5, atol=1e-6 * f32(h.lr))
+    # and it is not the decoupled update
+    p2, m2, v2 = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rng = np.random.default_rng(2)
+    rng.standard_normal(n)
+    for t in range(1, 11):
+        g = bf16_bits(rng.standard_normal(n) * 10.0 ** rng.uniform(-5, -1, n))
+        h.step = t
+        oracle.step_fp32_moments(oracle.make_config(h), p2, g, m2, v2)
+    assert not np.allclose(p2, ref, rtol=1e-5, atol=1e-6 * f32(h.lr))
+
+
 def test_exact_fp8_trajectory_dyadic():
     """g = 1, beta1 = beta2 = 0.5: the fresh moments are 1 - 2^-t exactly and the
     power-of-two scale puts them just under the format maximum.
@@ -166,12 +198,15 @@ CASES = [
     (200, 0, 1, 0, True, False, 2),
     (150, 0, 1, 128, True, False, 2),
     (96, 0, 1, 0, False, True, 2),
+    (140, 0, 1, 0, False, False, 3, True),
+    (130, 0, 1, 128, False, True, 2, True),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"n{c[0]}_m{c[1]}v{c[2]}_b{c[3]}_{'amax' if c[4] else 'pow2'}_{'bf16' if c[5] else 'f32'}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"n{c[0]}_m{c[1]}v{c[2]}_b{c[3]}_{'amax' if c[4] else 'pow2'}_{'bf16' if c[5] else 'f32'}{'_l2' if len(c) > 7 else ''}" for c in CASES])
 def test_oracle_equals_rational_referee(case):
-    n, m_fmt, v_fmt, block, amax_mode, bf16_master, steps = case
+    n, m_fmt, v_fmt, block, amax_mode, bf16_master, steps = case[:7]
+    l2 = len(case) > 7 and case[7]
     p, g0, cm, cv, sm, sv = _rand_case(n, 11 + n, m_fmt, v_fmt, block, amax_mode, bf16_master)
     h = oracle.Hyper(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
     rp = [float(x) for x in (bf16_vals(p) if bf16_master else p)]
@@ -183,13 +218,13 @@ def test_oracle_equals_rational_referee(case):
         h.step = t
         cfg = oracle.make_config(h, m_fmt, v_fmt, block=block,
                                  scale_mode=oracle.SCALE_AMAX if amax_mode else oracle.SCALE_POW2,
-                                 master_bf16=bf16_master)
+                                 master_bf16=bf16_master, l2_coupled=l2)
         oracle.step(cfg, p, g, cm, cv, sm, sv)
         rp, rcm, rcv, rsm, rsv = rational.step(
             rp, [float(x) for x in bf16_vals(g)], rcm, rcv, rsm, rsv,
             lr=f32(h.lr), b1=f32(h.beta1), b2=f32(h.beta2), eps=f32(h.eps),
             wd=f32(h.weight_decay), t=t, m_fmt=m_fmt, v_fmt=v_fmt, block=block,
-            amax_mode=amax_mode, master_bf16=bf16_master)
+            amax_mode=amax_mode, master_bf16=bf16_master, l2_coupled=l2)
         assert list(cm) == rcm, f"m codes differ at step {t}"
         assert list(cv) == rcv, f"v codes differ at step {t}"
         assert list(sm) == rsm and list(sv) == rsv, f"scales differ at step {t}"
