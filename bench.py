@@ -89,7 +89,8 @@ def cpu_baseline(w, shapes, idx):
     total, elapsed = 0, 0.0
     h = oracle.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=1)
     cfg = oracle.make_config(h, 0 if w.m_fmt == "e4m3" else 1, 0 if w.v_fmt == "e4m3" else 1,
-                             block=128 if w.granularity == "block128" else 0, master_bf16=(w.master == "bf16"))
+                             block=128 if w.granularity == "block128" else 0, master_bf16=(w.master == "bf16"),
+                             l2_coupled=(w.decay_mode == "l2"))
     for i in idx:
         name, s = shapes[i]
         n = workloads.numel(s)
@@ -112,7 +113,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_7b",
-                    choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_13b_bf16"])
+                    choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_7b_l2",
+                             "llama2_13b_bf16"])
     ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
     ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -141,9 +143,10 @@ def main():
     params = [workloads.make_param(w, i, s, dev) for i, (_, s) in enumerate(shapes)]
     grads = [workloads.make_grad(w, i, s, 1, dev) for i, (_, s) in enumerate(shapes)]
     torch.cuda.synchronize()
-    schedule = args.schedule if w.granularity == "tensor" else "two_pass"
+    # one-pass block scales; coupled L2 needs the old p in the amax pass, so two passes
+    schedule = args.schedule if (w.granularity == "tensor" and w.decay_mode == "decoupled") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
-                      schedule=schedule)
+                      schedule=schedule, decay_mode=w.decay_mode)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
@@ -193,10 +196,12 @@ def main():
     alg_bytes = bpp * total
     achieved = alg_bytes / kavg_s / 1e9
     traffic = load_traffic(w.name, kernel)
-    # bytes the whole step moved: + the amax pass (g, m, v) in the two-pass schedule,
-    # + the fix-up (g, m, v read, m, v written) of re-quantized tensors in the speculative one
+    # bytes the whole step moved: + the amax pass (g, m, v; and p with coupled L2) in the
+    # two-pass schedule, + the fix-up (g, m, v read, m, v written) of re-quantized tensors
+    # in the speculative one
     fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
-    step_bytes = alg_bytes + (4.0 * total if (w.granularity == "tensor" and schedule == "two_pass") else 0.0)
+    amax_bpp = 4.0 + ((4.0 if w.master == "fp32" else 2.0) if w.decay_mode == "l2" else 0.0)
+    step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass") else 0.0)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
@@ -230,7 +235,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(shapes), "params": total, "m_format": w.m_fmt,
                    "v_format": w.v_fmt, "scale": w.granularity, "master": w.master,
-                   "weight_decay": w.weight_decay, "schedule": schedule,
+                   "weight_decay": w.weight_decay, "decay_mode": w.decay_mode, "schedule": schedule,
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,

@@ -21,6 +21,7 @@
  *   m  = decode(c_m) * s_m            v  = decode(c_v) * s_v
  *   m' = fma(b1, m, (1-b1)*g)         v' = fma(b2, v, (1-b2)*(g*g))
  *   p' = p*(1 - lr*wd) - lr/(1-b1^t) * m' / (sqrt(v'/(1-b2^t)) + eps)
+ *   (decay_mode L2: g is replaced by fma(wd, p, g) and the factor (1 - lr*wd) by 1)
  *   s_m', s_v' chosen from max|m'| and max v' over the tensor (or over each
  *   128-element block);  c_m' = encode(m' / s_m'),  c_v' = encode(v' / s_v')
  * Encoding is OCP E4M3FN / E5M2, round-to-nearest-even, saturating at the
@@ -69,9 +70,18 @@ typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master
  *   before the step and writes the codes into the other of two code buffers (m/v and
  *   m_alt/v_alt, alternating every step); a per-tensor check then re-quantizes, from the old
  *   codes, only the tensors whose true scale differs (14 bytes per fp32 parameter plus 6 per
- *   re-quantized one).  Needs per-tensor POW2 scales and m_alt/v_alt; steps with
- *   t < speculate_from_step run TWO_PASS in place on the current buffer. */
+ *   re-quantized one).  Needs per-tensor POW2 scales, decoupled decay (the re-quantization
+ *   recomputes moments after p is overwritten, and coupled L2 would need the old p) and
+ *   m_alt/v_alt; steps with t < speculate_from_step run TWO_PASS in place on the current
+ *   buffer. */
 typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 } fp8adam_schedule;
+/* How weight_decay enters the step.
+ * DECOUPLED (AdamW, the zyxy.net code example): p' = p*(1 - lr*wd) - (Adam update).
+ * L2 (Adam on an L2-regularised loss: the training objective in the set-up of Theorem 1,
+ *   daoxuan.cc explainer, section on why the two SwiGLU weight vectors align): the
+ *   moments see g_eff = fma(wd, p, g) in fp32 with the old p, and p is not decayed
+ *   separately.  With wd = 0 both are plain Adam. */
+typedef enum { FP8ADAM_DECAY_DECOUPLED = 0, FP8ADAM_DECAY_L2 = 1 } fp8adam_decay_mode;
 
 typedef struct {
     int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
@@ -82,6 +92,7 @@ typedef struct {
     int32_t collect_stats; /* nonzero: count underflow / saturation / non-finite per tensor */
     int32_t schedule;      /* fp8adam_schedule (block granularity is always one pass) */
     int32_t speculate_from_step; /* first t of the speculative schedule; <= 0 means 4 */
+    int32_t decay_mode;    /* fp8adam_decay_mode */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,

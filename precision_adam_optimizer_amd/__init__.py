@@ -27,6 +27,8 @@ _FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
 _GRAN = {"tensor": SCALE_TENSOR, "block128": SCALE_BLOCK128}
 _SMODE = {"pow2": SCALE_POW2, "amax": SCALE_AMAX}
 _SCHED = {"two_pass": SCHEDULE_TWO_PASS, "speculative": SCHEDULE_SPECULATIVE}
+DECAY_DECOUPLED, DECAY_L2 = 0, 1
+_DECAY = {"decoupled": DECAY_DECOUPLED, "l2": DECAY_L2}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
                 "spec_check", "fixup")
@@ -53,7 +55,8 @@ class ConfigArg(ctypes.Structure):
     _fields_ = [("m_format", ctypes.c_int32), ("v_format", ctypes.c_int32),
                 ("granularity", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
                 ("master", ctypes.c_int32), ("collect_stats", ctypes.c_int32),
-                ("schedule", ctypes.c_int32), ("speculate_from_step", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("speculate_from_step", ctypes.c_int32),
+                ("decay_mode", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -206,14 +209,17 @@ class FP8AdamW:
     allocated here, zero codes with unit scales, unless ``state`` supplies
     (m, v, m_scale, v_scale) lists.  With ``schedule="speculative"`` a second
     pair of code buffers is allocated and the moments alternate between the two;
-    ``m`` and ``v`` always return the pair that holds them.  Every tensor must be
+    ``m`` and ``v`` always return the pair that holds them.  ``decay_mode="l2"``
+    adds weight_decay * p to the gradient instead of decaying p (Adam on an
+    L2-regularised loss); it cannot be combined with the speculative schedule.
+    Every tensor must be
     contiguous and 16-byte aligned on the same device, and must stay alive with
     the same storage while this object exists.
     """
 
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
-                 speculate_from_step=0):
+                 speculate_from_step=0, decay_mode="decoupled"):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
@@ -245,7 +251,7 @@ class FP8AdamW:
                                   _ptr(m_alt[i]), _ptr(v_alt[i])))
         self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
-                             _SCHED[schedule], int(speculate_from_step))
+                             _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode])
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):

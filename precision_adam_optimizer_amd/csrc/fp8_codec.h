@@ -121,7 +121,8 @@ __device__ __forceinline__ void choose_scale(uint32_t amax_bits, float& s, float
 struct StepConsts {
   float b1, b2;        // beta1, beta2
   float omb1, omb2;    // 1 - beta (fp32)
-  float decay;         // 1 - lr * weight_decay
+  float decay;         // 1 - lr * weight_decay (1 with coupled L2)
+  float l2;            // coupled L2: weight_decay, added to the gradient as l2 * p
   float step_size;     // lr / (1 - beta1^t)
   float inv_bc2;       // 1 / (1 - beta2^t)
   float eps;
@@ -140,6 +141,16 @@ __device__ __forceinline__ void moment_update(const StepConsts& c, float g, floa
   const float gv = c.omb2 * gg;
   m1 = __builtin_fmaf(c.b1, m, gm);
   v1 = __builtin_fmaf(c.b2, v, gv);
+}
+
+// Gradient the moments see: g, or with coupled L2 g + l2 * p (one fp32
+// rounding, the parameter before the step).  The L2-regularised loss is the
+// objective of Theorem 1's set-up in the daoxuan.cc explainer (section on why
+// the two SwiGLU weight vectors align).
+template <bool L2>
+__device__ __forceinline__ float grad_eff(const StepConsts& c, float g, float p) {
+  if constexpr (L2) return __builtin_fmaf(c.l2, p, g);
+  else return g;
 }
 
 // AdamW parameter update from the fresh moments: m in the numerator times the

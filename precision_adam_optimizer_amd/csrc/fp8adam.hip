@@ -255,16 +255,17 @@ __device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group
   }
 }
 
-// Unpack 4 grads, 4 dequantized moments, and the fresh moments.
-template <int MF, int VF>
-__device__ __forceinline__ void fresh_moments(const StepConsts& c, const Group& G, float sm, float sv,
-                                              float (&m1)[4], float (&v1)[4]) {
-  float g[4] = {bf16_lo(G.g.x), bf16_hi(G.g.x), bf16_lo(G.g.y), bf16_hi(G.g.y)};
+// Unpack 4 grads, 4 dequantized moments, and the fresh moments.  p (the
+// parameters before the step) is read only with coupled L2.
+template <int MF, int VF, bool L2>
+__device__ __forceinline__ void fresh_moments(const StepConsts& c, const Group& G, const float (&p)[4], float sm,
+                                              float sv, float (&m1)[4], float (&v1)[4]) {
+  const float g[4] = {bf16_lo(G.g.x), bf16_hi(G.g.x), bf16_lo(G.g.y), bf16_hi(G.g.y)};
   float m[4], v[4];
   decode4<MF>(G.cm, m);
   decode4<VF>(G.cv, v);
 #pragma unroll
-  for (int j = 0; j < 4; j++) moment_update(c, g[j], m[j] * sm, v[j] * sv, m1[j], v1[j]);
+  for (int j = 0; j < 4; j++) moment_update(c, grad_eff<L2>(c, g[j], p[j]), m[j] * sm, v[j] * sv, m1[j], v1[j]);
 }
 
 template <bool BF16P>
@@ -290,6 +291,10 @@ template <bool BF16P>
 __device__ __forceinline__ float load_p1(const TensorDesc& d, int64_t i) {
   if constexpr (BF16P) return __uint_as_float((uint32_t)ld_global<uint16_t>(static_cast<const uint16_t*>(d.p) + i) << 16);
   else return ld_global<float>(static_cast<const float*>(d.p) + i);
+}
+
+__device__ __forceinline__ float load_g1(const TensorDesc& d, int64_t i) {
+  return __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
 }
 
 template <bool BF16P>
@@ -324,7 +329,7 @@ __device__ __forceinline__ float inverse_pow2(uint32_t pow2_bits) {
 
 // ------------------------------------------------------------------ pass 1
 
-template <int MF, int VF>
+template <int MF, int VF, bool BF16P, bool L2>
 __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ chunk_tid,
                                                    uint2* __restrict__ partial, StepConsts c, int chunk_log2,
@@ -344,14 +349,15 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<false, FP8ADAM_NT_AMAX != 0>(d, i, G[u], false);
+      if (i < gend) load_group<BF16P, FP8ADAM_NT_AMAX != 0>(d, i, G[u], L2);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
       if (i < gend) {
-        float m1[4], v1[4];
-        fresh_moments<MF, VF>(c, G[u], sm, sv, m1, v1);
+        float m1[4], v1[4], p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (L2) unpack_p<BF16P>(G[u], p);
+        fresh_moments<MF, VF, L2>(c, G[u], p, sm, sv, m1, v1);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           am = max(am, abs_bits(m1[j]));
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
   // ragged tail (< 4 elements at the end of a tensor)
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+    const float g = grad_eff<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
     float m1, v1;
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     am = max(am, abs_bits(m1));
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
 
 // ------------------------------------------------------------------ pass 2
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC, bool L2>
 __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
                                                      const TensorDesc* __restrict__ dst_descs,
                                                      const int32_t* __restrict__ chunk_tid,
@@ -480,8 +486,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
       const int64_t i = base + (int64_t)u * kSubTile;
       if (i < gend) {
         float m1[4], v1[4], p[4], qm[4], qv[4];
-        fresh_moments<MF, VF>(c, G[u], sm, sv, m1, v1);
         unpack_p<BF16P>(G[u], p);
+        fresh_moments<MF, VF, L2>(c, G[u], p, sm, sv, m1, v1);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           p[j] = param_update(c, p[j], m1[j], v1[j]);
@@ -507,10 +513,11 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+    const float p0 = load_p1<BF16P>(d, i);
+    const float g = grad_eff<L2>(c, load_g1(d, i), p0);
     float m1, v1;
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
-    const float p = param_update(c, load_p1<BF16P>(d, i), m1, v1);
+    const float p = param_update(c, p0, m1, v1);
     const float qm = m1 * ism, qv = v1 * isv;
     const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
@@ -654,7 +661,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+    const float g = load_g1(d, i);
     const float x0 = decode1<FMT>(ld_global<uint8_t>(src + i)) * s_old;
     float m1, v1;
     moment_update(c, g, x0, x0, m1, v1);
@@ -729,7 +736,7 @@ __device__ __forceinline__ uint32_t group32_max(uint32_t x) {
   return x;
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
                                                       const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                       unsigned long long* __restrict__ counters,
@@ -771,18 +778,18 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
       float m1[4], v1[4], p[4];
       const int64_t i0 = b0[j] + 4 * hl;
       if (full[j]) {
-        fresh_moments<MF, VF>(c, G[j], sm[j], sv[j], m1, v1);
         unpack_p<BF16P>(G[j], p);
+        fresh_moments<MF, VF, L2>(c, G[j], p, sm[j], sv[j], m1, v1);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
           const int64_t i = i0 + r;
           float a = 0.0f, b = 0.0f, q = 0.0f;
           if (ex[j] && i < end) {
-            const float g = __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
+            q = load_p1<BF16P>(d, i);
+            const float g = grad_eff<L2>(c, load_g1(d, i), q);
             moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm[j],
                           decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv[j], a, b);
-            q = load_p1<BF16P>(d, i);
           }
           m1[r] = a;
           v1[r] = b;
@@ -990,9 +997,9 @@ int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
 
 const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d_desc + (size_t)which * c->n; }
 
-template <int MF, int VF>
+template <int MF, int VF, bool BF16P, bool L2>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_amax<MF, VF>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
+  hipLaunchKernelGGL((k_amax<MF, VF, BF16P && L2, L2>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks);
 }
 
@@ -1003,9 +1010,9 @@ void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
                      c->d_flags);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC, bool L2>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, SPEC ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts);
 }
@@ -1024,9 +1031,9 @@ void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
                      c->d_counters, c->chunk_log2, c->nchunks);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts);
 }
 
@@ -1045,31 +1052,41 @@ void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
                      dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
 int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
     if (STATS) TIMED(4, launch_reset(c, 4 * (int64_t)c->n, s));
-    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE>(c, k, s)));
-  } else if (SMODE == 0 && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
+    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE, L2>(c, k, s)));
+  } else if (!L2 && SMODE == 0 && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
+    // (fp8adam_init refuses the speculative schedule with coupled L2: the fix-up
+    // recomputes moments after p has been overwritten, and g_eff needs the old p)
     if (STATS) TIMED(4, launch_reset(c, 0, s));
-    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, true>(c, k, s)));
+    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, true, false>(c, k, s)));
     TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
     if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS>(c, k, s)));
     c->cur = 1 - c->cur;
   } else {
-    if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF>(c, k, s)));
+    if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
     TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, s)));
-    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, false>(c, k, s)));
+    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, false, L2>(c, k, s)));
   }
   HIP_TRY(hipGetLastError());
   return 0;
 }
 
+// Coupled L2 with weight_decay 0 is plain Adam: it runs the kernels without
+// the extra term (which would also turn a -0 gradient into +0).
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
+int run_step_l(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  return k.l2 != 0.0f ? run_step_t<MF, VF, BF16P, STATS, SMODE, true>(c, k, t, s)
+                      : run_step_t<MF, VF, BF16P, STATS, SMODE, false>(c, k, t, s);
+}
+
 template <int MF, int VF, bool BF16P, bool STATS>
 int run_step_s(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_t<MF, VF, BF16P, STATS, 0>(c, k, t, s)
-                                                 : run_step_t<MF, VF, BF16P, STATS, 1>(c, k, t, s);
+  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_l<MF, VF, BF16P, STATS, 0>(c, k, t, s)
+                                                 : run_step_l<MF, VF, BF16P, STATS, 1>(c, k, t, s);
 }
 
 template <int MF, int VF, bool BF16P>
@@ -1130,9 +1147,13 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       return fail(FP8ADAM_EINVAL, "bad master dtype");
     if (cfg->schedule != FP8ADAM_SCHEDULE_TWO_PASS && cfg->schedule != FP8ADAM_SCHEDULE_SPECULATIVE)
       return fail(FP8ADAM_EINVAL, "bad schedule");
+    if (cfg->decay_mode != FP8ADAM_DECAY_DECOUPLED && cfg->decay_mode != FP8ADAM_DECAY_L2)
+      return fail(FP8ADAM_EINVAL, "bad decay_mode");
     const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
     if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
       return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
+    if (spec && cfg->decay_mode == FP8ADAM_DECAY_L2)
+      return fail(FP8ADAM_EINVAL, "the speculative schedule cannot be combined with coupled L2 decay");
 
     // Chunk size: the largest power of two in [kPart, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
@@ -1235,7 +1256,9 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
     k.b2 = hp->beta2;
     k.omb1 = 1.0f - hp->beta1;
     k.omb2 = 1.0f - hp->beta2;
-    k.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+    const bool l2 = ctx->cfg.decay_mode == FP8ADAM_DECAY_L2;
+    k.decay = l2 ? 1.0f : (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+    k.l2 = l2 ? hp->weight_decay : 0.0f;
     k.step_size = (float)((double)hp->lr / bc1);
     k.inv_bc2 = (float)(1.0 / bc2);
     k.eps = hp->eps;

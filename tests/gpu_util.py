@@ -61,10 +61,10 @@ class OracleState:
 
 
 def oracle_config(h: oracle.Hyper, m_fmt: str, v_fmt: str, granularity: str, scale_mode: str,
-                  master: str) -> oracle.Config:
+                  master: str, decay_mode: str = "decoupled") -> oracle.Config:
     return oracle.make_config(h, FMT_ID[m_fmt], FMT_ID[v_fmt], block=128 if granularity == "block128" else 0,
                               scale_mode=oracle.SCALE_AMAX if scale_mode == "amax" else oracle.SCALE_POW2,
-                              master_bf16=(master == "bf16"))
+                              master_bf16=(master == "bf16"), l2_coupled=(decay_mode == "l2"))
 
 
 def compare_tensor(name: str, st: OracleState, p_gpu: np.ndarray, cm_gpu: np.ndarray, cv_gpu: np.ndarray,

@@ -92,6 +92,12 @@ def test_speculative_schedule_argument_errors():
                 pk.ConfigArg(0, 1, 0, pk.SCALE_AMAX, 0, 0, pk.SCHEDULE_SPECULATIVE, 0),
                 pk.ConfigArg(0, 1, 0, 0, 0, 0, 7, 0)):
         assert L.fp8adam_init(ctypes.byref(h), alt, 1, ctypes.byref(bad), None) == -1
+    l2 = pk.ConfigArg(0, 1, 0, 0, 0, 0, pk.SCHEDULE_SPECULATIVE, 0, pk.DECAY_L2)
+    assert L.fp8adam_init(ctypes.byref(h), alt, 1, ctypes.byref(l2), None) == -1
+    assert "coupled L2" in pk.fp8adam_last_error()
+    bad_decay = pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 5)
+    assert L.fp8adam_init(ctypes.byref(h), alt, 1, ctypes.byref(bad_decay), None) == -1
+    assert "decay_mode" in pk.fp8adam_last_error()
     misaligned = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, 113, 128))
     assert L.fp8adam_init(ctypes.byref(h), misaligned, 1, ctypes.byref(cfg), None) == -2
     assert L.fp8adam_current_buffer(None) == -1

@@ -43,7 +43,7 @@ def _compare_stats(name, got: dict, want: dict, granularity: str):
 
 
 def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init, sizes=SIZES, steps=3,
-              lr=3e-4, seed=0, schedule="two_pass", speculate_from_step=0):
+              lr=3e-4, seed=0, schedule="two_pass", speculate_from_step=0, decay_mode="decoupled", wd=0.1):
     m_fmt, v_fmt = fmts
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
@@ -68,16 +68,16 @@ def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init,
                         np_host(state[3][i])) for i in range(len(sizes))]
     opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, granularity=granularity,
                       scale_mode=scale_mode, collect_stats=collect_stats, state=state, schedule=schedule,
-                      speculate_from_step=speculate_from_step)
+                      speculate_from_step=speculate_from_step, decay_mode=decay_mode)
     requantized = 0
     try:
         for t in range(1, steps + 1):
             for i, n in enumerate(sizes):
                 grads[i].copy_(random_grad(n, seed * 7919 + t * 101 + i, dev))
-            opt.step(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            opt.step(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=wd, step=t)
             torch.cuda.synchronize()
-            h = oracle.Hyper(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
-            cfg = oracle_config(h, m_fmt, v_fmt, granularity, scale_mode, master)
+            h = oracle.Hyper(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=wd, step=t)
+            cfg = oracle_config(h, m_fmt, v_fmt, granularity, scale_mode, master, decay_mode)
             gstats = opt.stats() if collect_stats else None
             for i, n in enumerate(sizes):
                 host[i].step(cfg, np_host(grads[i]))
@@ -109,6 +109,27 @@ def test_small_large_learning_rate_and_stats(gran):
     """Big updates (lr 1e-2) from a random mid-training state, stats on."""
     run_small(("e4m3", "e5m2"), gran, "pow2", "fp32", collect_stats=True, random_init=True, lr=1e-2,
               steps=4, seed=99)
+
+
+L2_COMBOS = list(itertools.product(["tensor", "block128"], ["pow2", "amax"], ["fp32", "bf16"]))
+
+
+@pytest.mark.parametrize("combo", L2_COMBOS, ids=[f"{g}_{s}_{m}" for g, s, m in L2_COMBOS])
+def test_small_coupled_l2(combo):
+    """Coupled L2 (weight_decay * p added to the gradient, no separate decay):
+    wd = 0.1 with |p| ~ 0.02 makes the L2 term dominate the smaller gradients."""
+    gran, smode, master = combo
+    k = L2_COMBOS.index(combo)
+    run_small(("e4m3", "e5m2"), gran, smode, master, collect_stats=(k % 2 == 0), random_init=(k % 4 < 2),
+              seed=200 + k, decay_mode="l2")
+
+
+def test_small_coupled_l2_other_formats_and_zero_decay():
+    run_small(("e5m2", "e4m3"), "tensor", "pow2", "fp32", collect_stats=True, random_init=True, seed=211,
+              decay_mode="l2", wd=0.5)
+    # weight_decay 0 is plain Adam in both modes (a -0 gradient stays -0)
+    run_small(("e4m3", "e5m2"), "block128", "pow2", "bf16", collect_stats=True, random_init=False, seed=212,
+              decay_mode="l2", wd=0.0)
 
 
 def test_zero_sized_tensor_in_list():
@@ -150,7 +171,8 @@ def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0
         host[i] = OracleState(np_host(params[i]), np.zeros(n, np.uint8), np.zeros(n, np.uint8),
                               np.ones(nb, np.float32), np.ones(nb, np.float32))
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
-                      collect_stats=collect_stats, schedule=schedule, speculate_from_step=speculate_from_step)
+                      collect_stats=collect_stats, schedule=schedule, speculate_from_step=speculate_from_step,
+                      decay_mode=w.decay_mode)
     top_m, top_v = _top_code(w.m_fmt), _top_code(w.v_fmt)
     all_stats = []
     try:
@@ -160,7 +182,7 @@ def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0
             opt.step(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
             torch.cuda.synchronize()
             h = oracle.Hyper(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
-            cfg = oracle_config(h, w.m_fmt, w.v_fmt, w.granularity, "pow2", w.master)
+            cfg = oracle_config(h, w.m_fmt, w.v_fmt, w.granularity, "pow2", w.master, w.decay_mode)
 
             def check(i):
                 st = host[i]
@@ -228,6 +250,14 @@ def test_llama2_7b_per_tensor_full_size():
     n = len(w.shapes)
     sample = _layer_indices(32, [0, 17, 31]) + [n - 2, n - 1]
     run_full(w, steps=2, sample=sample)
+
+
+@pytest.mark.timeout(900)
+def test_llama2_7b_coupled_l2_full_size():
+    w = workloads.llama2_7b_l2()
+    n = len(w.shapes)
+    sample = _layer_indices(32, [0, 31]) + [n - 2, n - 1]
+    run_full(w, steps=2, sample=sample, collect_stats=True)
 
 
 @pytest.mark.timeout(900)

@@ -60,6 +60,7 @@ class Workload:
     beta2: float = 0.95
     eps: float = 1e-8
     weight_decay: float = 0.0
+    decay_mode: str = "decoupled"  # "decoupled" (AdamW) or "l2" (wd * p added to the gradient)
     steps: int = 10
     param_std: float = 0.02
     extra: dict = field(default_factory=dict)
@@ -103,6 +104,15 @@ def llama2_7b_block128() -> Workload:
                     weight_decay=0.1, steps=20)
 
 
+def llama2_7b_l2() -> Workload:
+    """The 7B per-tensor list with coupled L2 (wd=0.1 enters the gradient)
+    instead of AdamW's decoupled decay."""
+    w = llama2_7b()
+    w.name = "llama2_7b_pertensor_l2"
+    w.decay_mode = "l2"
+    return w
+
+
 def llama2_13b_bf16() -> Workload:
     """Llama-2-13B-shaped list (363 tensors, 13.0B params) with bf16 master
     weights, gradient scales in [1e-7, 1], Adam as for the 1M case, 5 steps."""
@@ -122,6 +132,7 @@ WORKLOADS = {
     "llama2_100m": llama2_100m,
     "llama2_7b": llama2_7b,
     "llama2_7b_block128": llama2_7b_block128,
+    "llama2_7b_l2": llama2_7b_l2,
     "llama2_13b_bf16": llama2_13b_bf16,
 }
 
