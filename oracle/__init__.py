@@ -48,6 +48,7 @@ class Config(ctypes.Structure):
         ("m_fmt", ctypes.c_int), ("v_fmt", ctypes.c_int),
         ("block", ctypes.c_int), ("scale_mode", ctypes.c_int), ("master_bf16", ctypes.c_int),
         ("l2_coupled", ctypes.c_int),
+        ("history_len", ctypes.c_int), ("margin", ctypes.c_int), ("delayed_from", ctypes.c_int64),
     ]
 
 
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
         L.ref_step.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, P, u16p, u8p, u8p,
                                f32p, f32p, ctypes.POINTER(Stats)]
         L.ref_step.restype = ctypes.c_int
+        L.ref_step_hist.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, P, u16p, u8p, u8p,
+                                    f32p, f32p, f32p, ctypes.POINTER(Stats)]
+        L.ref_step_hist.restype = ctypes.c_int
         L.ref_step_fp32_moments.argtypes = [ctypes.POINTER(Config), ctypes.c_int64, f32p, u16p,
                                             f32p, f32p]
         L.ref_step_fp32_moments.restype = ctypes.c_int
@@ -157,9 +161,12 @@ class Hyper:
 
 
 def make_config(h: Hyper, m_fmt=E4M3, v_fmt=E5M2, block: int = 0,
-                scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False) -> Config:
+                scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False,
+                history_len: int = 0, margin: int = 0, delayed_from: int = 2) -> Config:
+    """history_len > 0 selects delayed scaling (per-tensor scales only)."""
     return Config(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step,
-                  fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled))
+                  fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled),
+                  history_len, margin, delayed_from)
 
 
 def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,
@@ -181,6 +188,24 @@ def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.
                         _ptr(sm), _ptr(sv), ctypes.byref(st))
     if rc != 0:
         raise ValueError("oracle ref_step rejected its arguments")
+    return st.as_dict()
+
+
+def step_hist(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,
+              sm: np.ndarray, sv: np.ndarray, hist: np.ndarray) -> dict:
+    """A step with delayed scaling: as ``step``, plus hist (float32, 2 * history_len:
+    the amax history of m then v), read for the scale and updated in place."""
+    n = p.size
+    assert cfg.history_len > 0 and hist.dtype == np.float32 and hist.size == 2 * cfg.history_len
+    assert g_bits.dtype == np.uint16 and g_bits.size == n
+    assert cm.dtype == np.uint8 and cv.dtype == np.uint8 and cm.size == n and cv.size == n
+    assert sm.dtype == np.float32 and sv.dtype == np.float32 and sm.size >= 1 and sv.size >= 1
+    assert p.dtype == (np.uint16 if cfg.master_bf16 else np.float32)
+    st = Stats()
+    rc = lib().ref_step_hist(ctypes.byref(cfg), n, _ptr(p), _ptr(g_bits), _ptr(cm), _ptr(cv),
+                             _ptr(sm), _ptr(sv), _ptr(hist), ctypes.byref(st))
+    if rc != 0:
+        raise ValueError("oracle ref_step_hist rejected its arguments")
     return st.as_dict()
 
 

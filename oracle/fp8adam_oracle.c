@@ -48,6 +48,13 @@
  *  - Bias correction 1 - beta^t with the caller's 1-based t; weight decay is
  *    decoupled (AdamW) and applied to the old p; p is updated from the fresh
  *    (unquantized) m', v'.
+ *  - Delayed scaling (history_len > 0, per-tensor scales): the scale of step t
+ *    comes from the largest amax recorded over the previous H steps (times
+ *    2^margin) instead of this step's amax; values beyond the format maximum
+ *    saturate.  [P3 "Strategies" (track the max-abs value) and the code
+ *    example's delayed-scaling recipe: history of 16, margin 0, interval 1,
+ *    MAX of the history.]  Steps t < delayed_from are just in time, so the
+ *    first step has a history to start from.
  *  - Coupled-L2 variant (l2_coupled): the L2 term of an L2-regularised loss
  *    enters the gradient instead, g_eff = fma(wd, p, g) in fp32 with the old
  *    p, and there is no decoupled decay.  [P1] "Why the SwiGLU weights align",
@@ -230,6 +237,9 @@ typedef struct {
     int scale_mode;   /* REF_SCALE_POW2 / REF_SCALE_AMAX */
     int master_bf16;  /* 0: p is fp32; 1: p is bf16 bits */
     int l2_coupled;   /* 0: decoupled decay (AdamW); 1: wd * p added to the gradient */
+    int history_len;  /* 0: just-in-time scales; H >= 1: delayed scaling over an amax history of H steps */
+    int margin;       /* delayed: the scale is chosen for amax_ref * 2^margin (0..64) */
+    int64_t delayed_from; /* delayed: steps t < delayed_from choose the scale just in time */
 } ref_config;
 
 typedef struct {
@@ -297,24 +307,45 @@ static float amax_update(float acc, float x)
     return a > acc ? a : acc;
 }
 
+/* [P3 "Strategies"; code example: delayed scaling with an amax history,
+ * margin 0, interval 1, the MAX of the history]  The reference amax of a
+ * delayed step: the largest entry of the history (a non-finite entry makes it
+ * non-finite, which gives scale 1), times 2^margin. */
+static float history_reference(const float *h, int H, int margin)
+{
+    float r = 0.0f;
+    for (int j = 0; j < H; j++) r = amax_update(r, h[j]);
+    return ldexpf(r, margin);
+}
+
 /*
  * One optimizer step for one tensor, in place on host arrays.
  *   p     : n fp32 (or n bf16 bit patterns when master_bf16)
  *   g     : n bf16 bit patterns
  *   cm,cv : n FP8 codes of m and v
  *   sm,sv : scales (1 per tensor, or ceil(n/block) per block), replaced by the new ones
+ *   hist  : delayed scaling only (history_len = H > 0, per-tensor scales): 2H
+ *           floats, the amax history of m then of v.  A delayed step (t >=
+ *           delayed_from) quantizes with the scale of history_reference() and
+ *           saturates what no longer fits; every step (just-in-time ones too)
+ *           then records its amax of m' and v' in slot (t-1) mod H, so the
+ *           history always holds the last H steps.  NULL when H = 0.
  * Returns 0, or -1 on a bad argument / allocation failure.
  */
-int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
-             uint8_t *cm, uint8_t *cv, float *sm, float *sv, ref_stats *st)
+int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
+                  uint8_t *cm, uint8_t *cv, float *sm, float *sv, float *hist, ref_stats *st)
 {
     if (!c || n < 0 || c->step < 1 || c->m_fmt < 0 || c->m_fmt > 1 || c->v_fmt < 0 ||
-        c->v_fmt > 1 || c->block < 0)
+        c->v_fmt > 1 || c->block < 0 || c->history_len < 0)
         return -1;
+    const int H = c->history_len;
+    if (H > 0 && (c->block > 0 || !hist || c->margin < 0 || c->margin > 64)) return -1;
+    const int delayed = H > 0 && c->step >= c->delayed_from;
     ref_consts k = make_consts(c);
     float fmax_m = ref_format_max(c->m_fmt), fmax_v = ref_format_max(c->v_fmt);
     int64_t blen = c->block > 0 ? c->block : (n > 0 ? n : 1);
-    int64_t nblocks = n > 0 ? (n + blen - 1) / blen : 0;
+    /* a per-tensor step always has its one scale (amax 0 for an empty tensor) */
+    int64_t nblocks = c->block > 0 ? (n + blen - 1) / blen : 1;
 
     float *m1 = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
     float *v1 = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
@@ -341,10 +372,13 @@ int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
             av = amax_update(av, v1[i]);
         }
 
-        /* 2. new scales from the amax of the new moments */
+        /* 2. new scales: from the amax of the new moments (just in time), or
+         *    from the history of earlier steps (delayed) */
         float nsm, nism, nsv, nisv;
-        ref_choose_scale(c->m_fmt, c->scale_mode, am, &nsm, &nism);
-        ref_choose_scale(c->v_fmt, c->scale_mode, av, &nsv, &nisv);
+        float ref_m = delayed ? history_reference(hist, H, c->margin) : am;
+        float ref_v = delayed ? history_reference(hist + H, H, c->margin) : av;
+        ref_choose_scale(c->m_fmt, c->scale_mode, ref_m, &nsm, &nism);
+        ref_choose_scale(c->v_fmt, c->scale_mode, ref_v, &nsv, &nisv);
 
         /* 3. requantize the moments and update the parameters */
         for (int64_t i = lo; i < hi; i++) {
@@ -369,6 +403,11 @@ int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
 
         sm[si] = nsm;
         sv[si] = nsv;
+        if (H > 0) {
+            int slot = (int)((c->step - 1) % H);
+            hist[slot] = am;
+            hist[H + slot] = av;
+        }
         s.amax_m = amax_update(s.amax_m, am);
         s.amax_v = amax_update(s.amax_v, av);
         if (c->block > 0) {
@@ -383,6 +422,14 @@ int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
     free(v1);
     if (st) *st = s;
     return 0;
+}
+
+/* Just-in-time step (no history). */
+int ref_step(const ref_config *c, int64_t n, void *p, const uint16_t *g,
+             uint8_t *cm, uint8_t *cv, float *sm, float *sv, ref_stats *st)
+{
+    if (!c || c->history_len != 0) return -1;
+    return ref_step_hist(c, n, p, g, cm, cv, sm, sv, NULL, st);
 }
 
 /*

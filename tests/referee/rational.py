@@ -12,7 +12,8 @@ scale), m' = b1*m + (1-b1)*g and v' = b2*v + (1-b2)*g*g in fp32 with one
 rounding for the multiply-add, new scale from the amax of m' / v', requantize
 with x * inv_scale, and p' = p*(1 - lr*wd) - lr/(1-b1^t) * m' / (sqrt(v'/(1-b2^t)) + eps).
 With l2_coupled the gradient is g + wd*p (one fp32 rounding) and there is no
-decoupled decay.
+decoupled decay.  With scale_amax the scales are chosen from the given amax
+values (delayed scaling) instead of this step's.
 """
 from __future__ import annotations
 
@@ -170,9 +171,12 @@ def param_update(p: float, m1: float, v1: float, lr: float, b1: float, b2: float
 def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[float],
          sv: list[float], *, lr: float, b1: float, b2: float, eps: float, wd: float, t: int,
          m_fmt: int = 0, v_fmt: int = 1, block: int = 0, amax_mode: bool = False,
-         master_bf16: bool = False, l2_coupled: bool = False):
-    """Returns new (p, cm, cv, sm, sv). All floats are values already exact in
-    their storage type (fp32, or bf16 for g and a bf16 master)."""
+         master_bf16: bool = False, l2_coupled: bool = False, scale_amax=None, return_amax: bool = False):
+    """Returns new (p, cm, cv, sm, sv), plus the per-block (amax m', amax v')
+    list with return_amax. All floats are values already exact in their storage
+    type (fp32, or bf16 for g and a bf16 master).  scale_amax: (am, av) to
+    choose a per-tensor step's scales from."""
+    assert scale_amax is None or block == 0
     n = len(p)
     blen = block if block > 0 else max(n, 1)
     omb1 = sub32(1.0, b1)
@@ -180,7 +184,8 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
     p2, cm2, cv2 = list(p), list(cm), list(cv)
     sm2, sv2 = list(sm), list(sv)
     choose = amax_scale if amax_mode else pow2_scale
-    for bi, lo in enumerate(range(0, n, blen)):
+    amaxes = []
+    for bi, lo in enumerate(range(0, n if block > 0 else max(n, 1), blen)):
         hi = min(lo + blen, n)
         si = bi if block > 0 else 0
         m1s, v1s = [], []
@@ -194,6 +199,9 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
             v1s.append(v1)
         am = max((abs(x) for x in m1s), default=0.0)
         av = max((abs(x) for x in v1s), default=0.0)
+        amaxes.append((am, av))
+        if scale_amax is not None:
+            am, av = scale_amax
         nsm, nism = choose(m_fmt, am)
         nsv, nisv = choose(v_fmt, av)
         for j, i in enumerate(range(lo, hi)):
@@ -202,4 +210,6 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
             exact = param_update(p[i], m1s[j], v1s[j], lr, b1, b2, eps, 0.0 if l2_coupled else wd, t)
             p2[i] = round_bf16(exact) if master_bf16 else round_f32(exact)
         sm2[si], sv2[si] = nsm, nsv
+    if return_amax:
+        return p2, cm2, cv2, sm2, sv2, amaxes
     return p2, cm2, cv2, sm2, sv2

@@ -371,3 +371,127 @@ def test_nonfinite_count_closed_form():
     st = oracle.step(oracle.make_config(oracle.Hyper(step=1)), p, g, cm, cv, sm, sv)
     assert st["nonfinite"] == 1
     assert sm[0] == 1.0 and sv[0] == 1.0
+
+
+# ------------------------------------------------------------ delayed scaling
+
+DELAYED = [
+    # H, margin, amax_mode, m_fmt, v_fmt, bf16_master
+    (1, 0, False, 0, 1, False),
+    (3, 0, False, 0, 1, False),
+    (3, 2, False, 0, 1, True),
+    (2, 1, True, 0, 1, False),
+    (4, 0, False, 1, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", DELAYED, ids=[f"H{c[0]}_margin{c[1]}_{'amax' if c[2] else 'pow2'}_m{c[3]}v{c[4]}{'_bf16' if c[5] else ''}" for c in DELAYED])
+def test_delayed_scaling_equals_rational_referee(case):
+    """Delayed scaling over 7 steps, step 1 just in time: the referee is told
+    the reference amax (the max of its own record of the last H amaxes, times
+    2^margin) and must agree with the oracle bit for bit, history included.
+    The gradient grows 30x at step 4 (codes saturate) and shrinks at step 5."""
+    H, margin, amax_mode, m_fmt, v_fmt, bf16_master = case
+    n = 120
+    p, _, cm, cv, sm, sv = _rand_case(n, 500 + H, m_fmt, v_fmt, 0, amax_mode, bf16_master)
+    cm[:], cv[:], sm[:], sv[:] = 0, 0, 1.0, 1.0
+    h = oracle.Hyper(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    hist = np.zeros(2 * H, np.float32)
+    rhist = [0.0] * (2 * H)
+    rp = [float(x) for x in (bf16_vals(p) if bf16_master else p)]
+    rcm, rcv, rsm, rsv = [int(x) for x in cm], [int(x) for x in cv], [1.0], [1.0]
+    rng = np.random.default_rng(H * 10 + margin)
+    scales = [1e-3, 1e-3, 1e-3, 3e-2, 1e-4, 1e-3, 1e-3]
+    saturated = 0
+    for t, gs in enumerate(scales, start=1):
+        g = bf16_bits(rng.standard_normal(n) * gs)
+        h.step = t
+        cfg = oracle.make_config(h, m_fmt, v_fmt, scale_mode=oracle.SCALE_AMAX if amax_mode else oracle.SCALE_POW2,
+                                 master_bf16=bf16_master, history_len=H, margin=margin, delayed_from=2)
+        st = oracle.step_hist(cfg, p, g, cm, cv, sm, sv, hist)
+        saturated += st["saturated_m"] + st["saturated_v"]
+        ref = None if t < 2 else (max(rhist[:H]) * 2.0 ** margin, max(rhist[H:]) * 2.0 ** margin)
+        rp, rcm, rcv, rsm, rsv, am = rational.step(
+            rp, [float(x) for x in bf16_vals(g)], rcm, rcv, rsm, rsv,
+            lr=f32(h.lr), b1=f32(h.beta1), b2=f32(h.beta2), eps=f32(h.eps), wd=f32(h.weight_decay), t=t,
+            m_fmt=m_fmt, v_fmt=v_fmt, amax_mode=amax_mode, master_bf16=bf16_master, scale_amax=ref,
+            return_amax=True)
+        slot = (t - 1) % H
+        rhist[slot], rhist[H + slot] = am[0]
+        assert list(cm) == rcm, f"m codes differ at step {t}"
+        assert list(cv) == rcv, f"v codes differ at step {t}"
+        assert list(sm) == rsm and list(sv) == rsv, f"scales differ at step {t}"
+        assert list(hist) == rhist, f"history differs at step {t}"
+        if bf16_master:
+            assert np.array_equal(bf16_vals(p).view(np.uint32), np.array(rp, np.float32).view(np.uint32))
+        else:
+            assert _ulp_diff_f32(p, np.array(rp, np.float32)).max() <= 1
+        rp = [float(x) for x in (bf16_vals(p) if bf16_master else p)]
+    assert saturated > 0  # the growth step overran the delayed scale
+
+
+def test_delayed_saturation_count_closed_form():
+    """Zero moments, a history holding amax a: m' = (1-b1)*g exactly in fp32,
+    the scale is POW2(a), and the saturated count is the number of |m'|/s above
+    448 (counted here in numpy), the codes of those elements +-448."""
+    n = 64
+    rng = np.random.default_rng(1)
+    g = bf16_bits(rng.standard_normal(n) * 1e-2)
+    gv = bf16_vals(g)
+    omb1 = np.float32(1.0) - np.float32(0.9)
+    m1 = (omb1 * gv).astype(np.float32)
+    a = np.float32(2e-4)
+    k = math.frexp(float(a))[1] - 9 + (1 if math.frexp(float(a))[0] > 0.875 else 0)
+    s = 2.0 ** k
+    want_sat = int(np.sum(np.abs(m1.astype(np.float64)) / s > 448.0))
+    assert 0 < want_sat < n
+    p = np.zeros(n, np.float32)
+    cm, cv = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    sm, sv = np.ones(1, np.float32), np.ones(1, np.float32)
+    hist = np.array([a, 0.0, 1e30, 0.0], np.float32)  # H = 2: m history (a, 0), v history (1e30, 0)
+    cfg = oracle.make_config(oracle.Hyper(step=5, lr=1e-3, weight_decay=0.0), history_len=2, delayed_from=2)
+    st = oracle.step_hist(cfg, p, g, cm, cv, sm, sv, hist)
+    assert st["saturated_m"] == want_sat and st["saturated_v"] == 0
+    assert sm[0] == np.float32(s)
+    top = np.abs(m1.astype(np.float64)) / s > 448.0
+    assert np.all((cm[top] & 0x7F) == 0x7E)  # E4M3 448
+    # slot (5-1) mod 2 = 0 now holds this step's amax, slot 1 is unchanged
+    assert hist[0] == np.max(np.abs(m1)) and hist[1] == 0.0
+
+
+def test_delayed_warmup_steps_are_just_in_time():
+    """Steps before delayed_from equal the just-in-time step and record their
+    amax; a delayed step whose history maximum equals its own amax is the
+    just-in-time step too."""
+    n = 257
+    p, g, cm, cv, sm, sv = _rand_case(n, 77, 0, 1, 0, False, False)
+    args = [x.copy() for x in (p, g, cm, cv, sm, sv)]
+    h = oracle.Hyper(step=1, weight_decay=0.1)
+    st = oracle.step(oracle.make_config(h), *args)
+    hist = np.zeros(6, np.float32)
+    b = [x.copy() for x in (p, g, cm, cv, sm, sv)]
+    oracle.step_hist(oracle.make_config(h, history_len=3, delayed_from=3), *b, hist)
+    for x, y in zip(args, b):
+        assert np.array_equal(x, y)
+    assert hist[0] == np.float32(st["amax_m"]) and hist[3] == np.float32(st["amax_v"])
+    # same inputs at t = 4 (delayed), history preset to that step's own amax
+    h.step = 4
+    jit = [x.copy() for x in (p, g, cm, cv, sm, sv)]
+    st4 = oracle.step(oracle.make_config(h), *jit)
+    hist = np.array([0.0, st4["amax_m"], 0.0, 0.0, st4["amax_v"], 0.0], np.float32)
+    d = [x.copy() for x in (p, g, cm, cv, sm, sv)]
+    std = oracle.step_hist(oracle.make_config(h, history_len=3, delayed_from=2), *d, hist)
+    for x, y in zip(jit, d):
+        assert np.array_equal(x, y)
+    assert std["saturated_m"] == 0 and std["saturated_v"] == 0
+
+
+def test_delayed_rejects_block_mode_and_missing_history():
+    cfg = oracle.make_config(oracle.Hyper(step=2), block=128, history_len=4)
+    z = np.zeros(4, np.float32)
+    with pytest.raises(ValueError):
+        oracle.step_hist(cfg, np.zeros(8, np.float32), np.zeros(8, np.uint16), np.zeros(8, np.uint8),
+                         np.zeros(8, np.uint8), np.ones(1, np.float32), np.ones(1, np.float32), np.zeros(8, np.float32))
+    with pytest.raises(ValueError):
+        oracle.step(oracle.make_config(oracle.Hyper(step=2), history_len=2), np.zeros(4, np.float32),
+                    np.zeros(4, np.uint16), np.zeros(4, np.uint8), np.zeros(4, np.uint8), z[:1] + 1, z[:1] + 1)
