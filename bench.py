@@ -116,6 +116,8 @@ def main():
                     choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_7b_l2",
                              "llama2_13b_bf16"])
     ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
+    ap.add_argument("--scaling", default="just_in_time", choices=["just_in_time", "delayed"],
+                    help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")
     ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -144,9 +146,11 @@ def main():
     grads = [workloads.make_grad(w, i, s, 1, dev) for i, (_, s) in enumerate(shapes)]
     torch.cuda.synchronize()
     # one-pass block scales; coupled L2 needs the old p in the amax pass, so two passes
-    schedule = args.schedule if (w.granularity == "tensor" and w.decay_mode == "decoupled") else "two_pass"
+    scaling = args.scaling if w.granularity == "tensor" else "just_in_time"
+    schedule = args.schedule if (w.granularity == "tensor" and w.decay_mode == "decoupled"
+                                 and scaling == "just_in_time") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
-                      schedule=schedule, decay_mode=w.decay_mode)
+                      schedule=schedule, decay_mode=w.decay_mode, scaling=scaling)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
@@ -156,7 +160,7 @@ def main():
         for i, (_, shp) in enumerate(shapes):
             grads[i].copy_(workloads.make_grad(w, i, shp, t, dev))
 
-    log(f"context: {opt.num_chunks} chunks, schedule {schedule}; warmup {args.warmup} steps")
+    log(f"context: {opt.num_chunks} chunks, schedule {schedule}, scaling {scaling}; warmup {args.warmup} steps")
     t = 0
     for _ in range(args.warmup):
         t += 1
@@ -189,7 +193,7 @@ def main():
             log(f"  {k}: {cnt} launches, avg {tot / cnt * 1e3:.1f} us")
 
     kernel = "block128_pass" if w.granularity == "block128" else (
-        "spec_pass" if schedule == "speculative" else "update_pass")
+        "delayed_pass" if scaling == "delayed" else "spec_pass" if schedule == "speculative" else "update_pass")
     ktot, kcnt = ktimes[kernel]
     kavg_s = ktot / kcnt / 1e3
     bpp = BYTES_PER_PARAM[(w.granularity, w.master)]
@@ -201,7 +205,8 @@ def main():
     # in the speculative one
     fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
     amax_bpp = 4.0 + ((4.0 if w.master == "fp32" else 2.0) if w.decay_mode == "l2" else 0.0)
-    step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass") else 0.0)
+    step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass"
+                                                   and scaling == "just_in_time") else 0.0)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
@@ -236,6 +241,7 @@ def main():
         "config": {"workload": w.name, "tensors": len(shapes), "params": total, "m_format": w.m_fmt,
                    "v_format": w.v_fmt, "scale": w.granularity, "master": w.master,
                    "weight_decay": w.weight_decay, "decay_mode": w.decay_mode, "schedule": schedule,
+                   "scaling": scaling if scaling == "just_in_time" else "delayed (amax history 16, margin 0)",
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,

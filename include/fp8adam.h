@@ -82,6 +82,16 @@ typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 }
  *   moments see g_eff = fma(wd, p, g) in fp32 with the old p, and p is not decayed
  *   separately.  With wd = 0 both are plain Adam. */
 typedef enum { FP8ADAM_DECAY_DECOUPLED = 0, FP8ADAM_DECAY_L2 = 1 } fp8adam_decay_mode;
+/* When the scale is chosen (per-tensor granularity).
+ * JUST_IN_TIME: from this step's amax of m' and v' (codes never saturate under POW2).
+ * DELAYED: delayed scaling as in the zyxy.net article (strategies: track the max-abs value;
+ *   code example: a history of 16 amaxes, margin 0, interval 1, MAX of the history).  Step t
+ *   quantizes with the scale of max(history) * 2^margin, saturating what no longer fits
+ *   (counted as saturated), in one pass over the data (14 bytes per fp32 parameter); each step
+ *   then records its amax of m' and v' in slot (t-1) mod H of the tensor's amax_history.
+ *   Steps with t < delayed_from_step are just in time (two passes) and also record their amax,
+ *   so the history is seeded.  Needs per-tensor scales and the TWO_PASS schedule value. */
+typedef enum { FP8ADAM_SCALING_JUST_IN_TIME = 0, FP8ADAM_SCALING_DELAYED = 1 } fp8adam_scaling;
 
 typedef struct {
     int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
@@ -93,6 +103,10 @@ typedef struct {
     int32_t schedule;      /* fp8adam_schedule (block granularity is always one pass) */
     int32_t speculate_from_step; /* first t of the speculative schedule; <= 0 means 4 */
     int32_t decay_mode;    /* fp8adam_decay_mode */
+    int32_t scaling;       /* fp8adam_scaling */
+    int32_t amax_history_len;  /* DELAYED: H in [1, 1024]; <= 0 means 16 */
+    int32_t margin;            /* DELAYED: scale chosen for max(history) * 2^margin, margin in [0, 64] */
+    int32_t delayed_from_step; /* DELAYED: first t quantized with the delayed scale; <= 0 means 2 */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,
@@ -105,7 +119,10 @@ typedef struct {
  *   m_alt, v_alt : numel bytes each, the second code buffers of the speculative
  *             schedule (ignored, may be NULL, otherwise); fp8adam_current_buffer
  *             tells which pair holds the moments after a step
- * The state before the first step is all-zero codes with scales 1.0. */
+ *   amax_history : DELAYED scaling only (else ignored, may be NULL): 2*H floats, 4-byte
+ *             aligned, the amax history of m (first H) then of v; read and updated by
+ *             every step.  Part of the optimizer state (checkpoint it with the codes).
+ * The state before the first step is all-zero codes with scales 1.0 (and a zero history). */
 typedef struct {
     void *param;
     const void *grad;
@@ -116,6 +133,7 @@ typedef struct {
     int64_t numel;
     uint8_t *m_alt;
     uint8_t *v_alt;
+    float *amax_history;
 } fp8adam_tensor;
 
 /* Hyperparameters of one step.  step is the 1-based t used for bias correction. */
@@ -185,7 +203,8 @@ int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 /* Per-kernel timing since the last call (or since timing was enabled):
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
- * 6 = speculative scale check, 7 = re-quantization fix-up), total_ms[k] and count[k].
+ * 6 = speculative scale check, 7 = re-quantization fix-up, 8 = delayed-scaling pass,
+ * 9 = delayed-scaling commit), total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);
 

@@ -344,8 +344,8 @@ int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
     ref_consts k = make_consts(c);
     float fmax_m = ref_format_max(c->m_fmt), fmax_v = ref_format_max(c->v_fmt);
     int64_t blen = c->block > 0 ? c->block : (n > 0 ? n : 1);
-    /* a per-tensor step always has its one scale (amax 0 for an empty tensor) */
-    int64_t nblocks = c->block > 0 ? (n + blen - 1) / blen : 1;
+    /* an empty tensor has no blocks: its scales (and history) stay as they are */
+    int64_t nblocks = n > 0 ? (n + blen - 1) / blen : 0;
 
     float *m1 = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
     float *v1 = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));

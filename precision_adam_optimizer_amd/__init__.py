@@ -29,9 +29,11 @@ _SMODE = {"pow2": SCALE_POW2, "amax": SCALE_AMAX}
 _SCHED = {"two_pass": SCHEDULE_TWO_PASS, "speculative": SCHEDULE_SPECULATIVE}
 DECAY_DECOUPLED, DECAY_L2 = 0, 1
 _DECAY = {"decoupled": DECAY_DECOUPLED, "l2": DECAY_L2}
+SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
+_SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
-                "spec_check", "fixup")
+                "spec_check", "fixup", "delayed_pass", "delayed_commit")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
@@ -48,7 +50,8 @@ class Fp8AdamError(RuntimeError):
 class TensorArg(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("m_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("numel", ctypes.c_int64), ("m_alt", ctypes.c_void_p), ("v_alt", ctypes.c_void_p)]
+                ("numel", ctypes.c_int64), ("m_alt", ctypes.c_void_p), ("v_alt", ctypes.c_void_p),
+                ("amax_history", ctypes.c_void_p)]
 
 
 class ConfigArg(ctypes.Structure):
@@ -56,7 +59,9 @@ class ConfigArg(ctypes.Structure):
                 ("granularity", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
                 ("master", ctypes.c_int32), ("collect_stats", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("speculate_from_step", ctypes.c_int32),
-                ("decay_mode", ctypes.c_int32)]
+                ("decay_mode", ctypes.c_int32), ("scaling", ctypes.c_int32),
+                ("amax_history_len", ctypes.c_int32), ("margin", ctypes.c_int32),
+                ("delayed_from_step", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -212,6 +217,10 @@ class FP8AdamW:
     ``m`` and ``v`` always return the pair that holds them.  ``decay_mode="l2"``
     adds weight_decay * p to the gradient instead of decaying p (Adam on an
     L2-regularised loss); it cannot be combined with the speculative schedule.
+    ``scaling="delayed"`` quantizes with the scale of the largest amax over the
+    last ``amax_history_len`` steps (times 2^margin) in one pass; each tensor
+    then carries a float32 history of 2 * amax_history_len entries
+    (``amax_history``; a fifth ``state`` list supplies it).
     Every tensor must be
     contiguous and 16-byte aligned on the same device, and must stay alive with
     the same storage while this object exists.
@@ -219,7 +228,8 @@ class FP8AdamW:
 
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
-                 speculate_from_step=0, decay_mode="decoupled"):
+                 speculate_from_step=0, decay_mode="decoupled", scaling="just_in_time",
+                 amax_history_len=16, margin=0, delayed_from_step=0):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
@@ -234,7 +244,15 @@ class FP8AdamW:
             ms = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             vs = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             state = (m, v, ms, vs)
-        m, v, self.m_scale, self.v_scale = [list(x) for x in state]
+        m, v, self.m_scale, self.v_scale = [list(x) for x in state[:4]]
+        delayed = _SCALING[scaling] == SCALING_DELAYED
+        if delayed and len(state) > 4:
+            self.amax_history = list(state[4])
+        elif delayed:
+            self.amax_history = [torch.zeros(2 * amax_history_len, dtype=torch.float32, device=p.device)
+                                 for p in params]
+        else:
+            self.amax_history = [None] * len(params)
         spec = _SCHED[schedule] == SCHEDULE_SPECULATIVE
         m_alt = [torch.empty_like(x) for x in m] if spec else [None] * len(m)
         v_alt = [torch.empty_like(x) for x in v] if spec else [None] * len(v)
@@ -248,10 +266,11 @@ class FP8AdamW:
                     raise ValueError(f"tensor {i}: every buffer must be contiguous on one device")
             args.append(TensorArg(p.data_ptr(), g.data_ptr(), m[i].data_ptr(), v[i].data_ptr(),
                                   self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel(),
-                                  _ptr(m_alt[i]), _ptr(v_alt[i])))
+                                  _ptr(m_alt[i]), _ptr(v_alt[i]), _ptr(self.amax_history[i])))
         self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
-                             _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode])
+                             _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode],
+                             _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step))
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):

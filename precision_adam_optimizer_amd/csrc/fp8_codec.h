@@ -127,6 +127,9 @@ struct StepConsts {
   float inv_bc2;       // 1 / (1 - beta2^t)
   float eps;
   float grow_m, grow_v; // speculative schedule: expected amax growth (1-beta^t)/(1-beta^(t-1))
+  float margin_scale;  // delayed scaling: 2^margin
+  int hist_len;        // delayed scaling: H (0: no history)
+  int hist_slot;       // delayed scaling: (t-1) mod H, the slot this step's amax goes to
 };
 
 // Moment update (daoxuan.cc explainer, "Adam's update makes the needs

@@ -111,7 +111,13 @@ struct TensorDesc {
   float* sv;
   int64_t numel;
   int64_t chunk0;  // index of the tensor's first chunk
+  float* hist;     // delayed scaling: [2][H] amax history of m, v
 };
+
+// Update-pass variants: just-in-time scales known before the pass (two-pass
+// schedule), a predicted scale with codes to the other buffer (speculative),
+// or the delayed scale from the amax history.
+enum UpdateMode { kModeJit = 0, kModeSpec = 1, kModeDelayed = 2 };
 
 enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
 
@@ -327,6 +333,17 @@ __device__ __forceinline__ float inverse_pow2(uint32_t pow2_bits) {
   return __uint_as_float((254u - (pow2_bits >> 23)) << 23);
 }
 
+// Delayed scaling: the scale of the largest entry of a tensor's amax history
+// (H entries, sign bits ignored; a non-finite entry gives scale 1) times
+// 2^margin.  Called by whole waves; every lane gets the same s and inv.
+template <int FMT, int SMODE>
+__device__ __forceinline__ void delayed_scale(const float* h, const StepConsts& c, float& s, float& inv) {
+  uint32_t r = 0;
+  for (int j = threadIdx.x & 63; j < c.hist_len; j += 64) r = max(r, abs_bits(ld_global<float>(h + j)));
+  r = wave_max(r);
+  choose_scale<FMT, SMODE>(abs_bits(__uint_as_float(r) * c.margin_scale), s, inv);
+}
+
 // ------------------------------------------------------------------ pass 1
 
 template <int MF, int VF, bool BF16P, bool L2>
@@ -393,7 +410,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
                                                            uint32_t* __restrict__ amax,
                                                            float* __restrict__ old_scale,
                                                            unsigned long long* __restrict__ counters,
-                                                           int chunk_log2, int32_t* __restrict__ flags) {
+                                                           int chunk_log2, int32_t* __restrict__ flags,
+                                                           int hist_len, int hist_slot) {
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
   const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
@@ -428,6 +446,10 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
       st_global<float>(d.sm, s);
       choose_scale<VF, SMODE>(av, s, inv);
       st_global<float>(d.sv, s);
+      if (hist_len > 0) {  // just-in-time step of delayed scaling: seed the history
+        st_global<float>(d.hist + hist_slot, __uint_as_float(am));
+        st_global<float>(d.hist + hist_len + hist_slot, __uint_as_float(av));
+      }
     }
   }
   if constexpr (STATS) {
@@ -437,7 +459,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
 
 // ------------------------------------------------------------------ pass 2
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2>
 __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
                                                      const TensorDesc* __restrict__ dst_descs,
                                                      const int32_t* __restrict__ chunk_tid,
@@ -445,6 +467,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
                                                      const float* __restrict__ old_scale, StepConsts c,
                                                      unsigned long long* __restrict__ counters, int chunk_log2,
                                                      uint2* __restrict__ part_amax, int64_t nwork) {
+  constexpr bool SPEC = MODE == kModeSpec;
+  constexpr bool PARTS = MODE != kModeJit;  // per-part amax partials for the commit kernel
   const int64_t w = work_index<kXcdStreams>(nwork);
   if (w < 0) return;
   const int split_log2 = chunk_log2 - kPartLog2;
@@ -464,6 +488,12 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     sv = ld_global<float>(d.sv);
     ism = inverse_pow2(predicted_scale_bits<MF>(amax[2 * tid], sm, c.grow_m));
     isv = inverse_pow2(predicted_scale_bits<VF>(amax[2 * tid + 1], sv, c.grow_v));
+  } else if constexpr (MODE == kModeDelayed) {
+    float unused;
+    sm = ld_global<float>(d.sm);
+    sv = ld_global<float>(d.sv);
+    delayed_scale<MF, SMODE>(d.hist, c, unused, ism);
+    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, unused, isv);
   } else {
     float nsm, nsv;
     sm = old_scale[2 * tid];
@@ -471,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
     choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
   }
-  uint32_t am = 0, av = 0;  // speculative: this part's amax
+  uint32_t am = 0, av = 0;  // speculative / delayed: this part's amax
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
 
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUpdUnroll) {
@@ -493,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
           p[j] = param_update(c, p[j], m1[j], v1[j]);
           qm[j] = m1[j] * ism;
           qv[j] = v1[j] * isv;
-          if constexpr (SPEC) {
+          if constexpr (PARTS) {
             am = max(am, abs_bits(m1[j]));
             av = max(av, abs_bits(v1[j]));
           }
@@ -521,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     const float qm = m1 * ism, qv = v1 * isv;
     const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
-    if constexpr (SPEC) {
+    if constexpr (PARTS) {
       am = max(am, abs_bits(m1));
       av = max(av, abs_bits(v1));
     }
@@ -530,9 +560,62 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     st_global<uint8_t>(dv + i, (uint8_t)cv);
   }
   flush_counters<STATS>(counters, tid, cnt);
-  if constexpr (SPEC) {
+  if constexpr (PARTS) {
     block_max2(am, av);
     if (threadIdx.x == 0) part_amax[w] = make_uint2(am, av);
+  }
+}
+
+// ------------------------------------------------------- delayed: commit
+//
+// One work-group per tensor, after the delayed pass: the tensor's amax from the
+// per-part partials; wave 0 recomputes the delayed scales exactly as the pass
+// did (before the history changes), thread 0 commits them and records this
+// step's amax in the history slot.
+
+template <int MF, int VF, int SMODE>
+__global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorDesc* __restrict__ descs,
+                                                                   const uint2* __restrict__ part_amax,
+                                                                   uint32_t* __restrict__ amax, StepConsts c,
+                                                                   int chunk_log2) {
+  const int t = blockIdx.x;
+  const TensorDesc d = descs[t];
+  const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
+  const int64_t part0 = d.chunk0 << (chunk_log2 - kPartLog2);
+  uint32_t am = 0, av = 0;
+  for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
+    const uint2 pv = part_amax[part0 + k];
+    am = max(am, pv.x);
+    av = max(av, pv.y);
+  }
+  __shared__ uint32_t red[2][kReduceThreads / 64];
+  am = wave_max(am);
+  av = wave_max(av);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    red[0][wave] = am;
+    red[1][wave] = av;
+  }
+  __syncthreads();
+  if (wave == 0 && d.numel > 0) {  // uniform: all of wave 0, or none
+    float s_m, s_v, inv;
+    delayed_scale<MF, SMODE>(d.hist, c, s_m, inv);
+    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, s_v, inv);
+    if (lane == 0) {
+      for (int w = 1; w < kReduceThreads / 64; w++) {
+        am = max(am, red[0][w]);
+        av = max(av, red[1][w]);
+      }
+      st_global<float>(d.sm, s_m);
+      st_global<float>(d.sv, s_v);
+      st_global<float>(d.hist + c.hist_slot, __uint_as_float(am));
+      st_global<float>(d.hist + c.hist_len + c.hist_slot, __uint_as_float(av));
+      amax[2 * t] = am;
+      amax[2 * t + 1] = av;
+    }
+  } else if (threadIdx.x == 0) {
+    amax[2 * t] = 0u;
+    amax[2 * t + 1] = 0u;
   }
 }
 
@@ -938,6 +1021,9 @@ struct fp8adam_ctx {
   int64_t nchunks = 0;
   int chunk_log2 = kMaxChunkLog2;  // elements per chunk = 2^chunk_log2
   int speculate_from = 4;          // first step t that runs the speculative schedule
+  int hist_len = 0;                // delayed scaling: amax history length H (0: just in time)
+  int delayed_from = 2;            // delayed scaling: first step t quantized with the delayed scale
+  float margin_scale = 1.0f;       // delayed scaling: 2^margin
   int cur = 0;                     // code buffer holding the moments: 0 = m/v, 1 = m_alt/v_alt
   int64_t nparts = 0;              // update / block work-groups
   TensorDesc* d_desc = nullptr;    // [2][n]: descriptors with m/v, then with m_alt/v_alt
@@ -1004,16 +1090,22 @@ void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
-void launch_reduce(fp8adam_ctx* c, hipStream_t s) {
+void launch_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
                      descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
-                     c->d_flags);
+                     c->d_flags, k.hist_len, k.hist_slot);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool SPEC, bool L2>
+template <int MF, int VF, int SMODE>
+void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
+                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2);
+}
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, SPEC, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
-                     descs_of(c, c->cur), descs_of(c, SPEC ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+                     descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts);
 }
 
@@ -1038,7 +1130,8 @@ void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 }
 
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
-// 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up.
+// 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up,
+// 8 delayed pass, 9 delayed commit.
 #define TIMED(kind, call)                              \
   do {                                                 \
     int slot_;                                         \
@@ -1061,15 +1154,19 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
     // (fp8adam_init refuses the speculative schedule with coupled L2: the fix-up
     // recomputes moments after p has been overwritten, and g_eff needs the old p)
     if (STATS) TIMED(4, launch_reset(c, 0, s));
-    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, true, false>(c, k, s)));
+    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false>(c, k, s)));
     TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
     if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS>(c, k, s)));
     c->cur = 1 - c->cur;
+  } else if (c->hist_len > 0 && t >= c->delayed_from) {
+    if (STATS) TIMED(4, launch_reset(c, 0, s));
+    if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2>(c, k, s)));
+    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, s)));
   } else {
     if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
-    TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, s)));
-    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, false, L2>(c, k, s)));
+    TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, k, s)));
+    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeJit, L2>(c, k, s)));
   }
   HIP_TRY(hipGetLastError());
   return 0;
@@ -1154,6 +1251,16 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
     if (spec && cfg->decay_mode == FP8ADAM_DECAY_L2)
       return fail(FP8ADAM_EINVAL, "the speculative schedule cannot be combined with coupled L2 decay");
+    if (cfg->scaling != FP8ADAM_SCALING_JUST_IN_TIME && cfg->scaling != FP8ADAM_SCALING_DELAYED)
+      return fail(FP8ADAM_EINVAL, "bad scaling");
+    const bool delayed = cfg->scaling == FP8ADAM_SCALING_DELAYED;
+    const int hist_len = cfg->amax_history_len > 0 ? cfg->amax_history_len : 16;
+    if (delayed) {
+      if (cfg->granularity != FP8ADAM_SCALE_TENSOR || spec)
+        return fail(FP8ADAM_EINVAL, "delayed scaling needs per-tensor scales and the TWO_PASS schedule value");
+      if (hist_len > 1024) return fail(FP8ADAM_EINVAL, "amax_history_len must be at most 1024");
+      if (cfg->margin < 0 || cfg->margin > 64) return fail(FP8ADAM_EINVAL, "margin must lie in [0, 64]");
+    }
 
     // Chunk size: the largest power of two in [kPart, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
@@ -1178,6 +1285,12 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         if (int r = check_aligned(T.v, "v", t)) return r;
         if (((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
           return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
+        if (delayed) {
+          if (!T.amax_history)
+            return fail(FP8ADAM_EINVAL, "delayed scaling needs amax_history (tensor " + std::to_string(t) + ")");
+          if ((uintptr_t)T.amax_history & 3u)
+            return fail(FP8ADAM_EALIGN, "amax_history of tensor " + std::to_string(t) + " is not 4-byte aligned");
+        }
         if (spec) {
           if (!T.m_alt || !T.v_alt)
             return fail(FP8ADAM_EINVAL, "the speculative schedule needs m_alt and v_alt (tensor " + std::to_string(t) + ")");
@@ -1187,7 +1300,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       }
       const int64_t nc = (T.numel + chunk - 1) / chunk;
       desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
-                           T.numel, nchunks};
+                           T.numel, nchunks, delayed ? T.amax_history : nullptr};
       desc[(size_t)n + t] = desc[t];
       if (spec) {
         desc[(size_t)n + t].m = T.m_alt;
@@ -1207,10 +1320,13 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->chunk_log2 = chunk_log2;
     c->nparts = nchunks << (chunk_log2 - kPartLog2);
     c->speculate_from = cfg->speculate_from_step > 0 ? cfg->speculate_from_step : 4;
+    c->hist_len = delayed ? hist_len : 0;
+    c->delayed_from = cfg->delayed_from_step > 0 ? cfg->delayed_from_step : 2;
+    c->margin_scale = ldexpf(1.0f, delayed ? cfg->margin : 0);
     hipError_t e = hipGetDevice(&c->device);
     const size_t namax = (size_t)n * 4;
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * 2 * (size_t)n);
-    if (e == hipSuccess && spec) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nparts));
+    if (e == hipSuccess && (spec || delayed)) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nparts));
     if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
@@ -1268,6 +1384,9 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
     const double bc2_prev = 1.0 - pow((double)hp->beta2, (double)(hp->step - 1));
     k.grow_m = bc1_prev > 0.0 ? (float)(bc1 / bc1_prev) : 1.0f;
     k.grow_v = bc2_prev > 0.0 ? (float)(bc2 / bc2_prev) : 1.0f;
+    k.margin_scale = ctx->margin_scale;
+    k.hist_len = ctx->hist_len;
+    k.hist_slot = ctx->hist_len > 0 ? (int)((hp->step - 1) % ctx->hist_len) : 0;
     return run_step(ctx, k, hp->step, stream);
   } catch (...) {
     return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step");

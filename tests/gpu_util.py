@@ -49,22 +49,29 @@ def pool_size() -> int:
 class OracleState:
     """Host copy of one tensor's optimizer state, advanced by the oracle."""
 
-    def __init__(self, p: np.ndarray, cm: np.ndarray, cv: np.ndarray, sm: np.ndarray, sv: np.ndarray):
+    def __init__(self, p: np.ndarray, cm: np.ndarray, cv: np.ndarray, sm: np.ndarray, sv: np.ndarray,
+                 hist: np.ndarray | None = None):
         self.p, self.cm, self.cv, self.sm, self.sv = p, cm, cv, sm, sv
+        self.hist = hist  # delayed scaling: the amax history (2H float32), else None
         self.p_old = p.copy()
         self.stats = None
 
     def step(self, cfg: oracle.Config, g_bits: np.ndarray) -> dict:
         self.p_old = self.p.copy()
-        self.stats = oracle.step(cfg, self.p, g_bits, self.cm, self.cv, self.sm, self.sv)
+        if self.hist is not None:
+            self.stats = oracle.step_hist(cfg, self.p, g_bits, self.cm, self.cv, self.sm, self.sv, self.hist)
+        else:
+            self.stats = oracle.step(cfg, self.p, g_bits, self.cm, self.cv, self.sm, self.sv)
         return self.stats
 
 
 def oracle_config(h: oracle.Hyper, m_fmt: str, v_fmt: str, granularity: str, scale_mode: str,
-                  master: str, decay_mode: str = "decoupled") -> oracle.Config:
+                  master: str, decay_mode: str = "decoupled", history_len: int = 0, margin: int = 0,
+                  delayed_from: int = 2) -> oracle.Config:
     return oracle.make_config(h, FMT_ID[m_fmt], FMT_ID[v_fmt], block=128 if granularity == "block128" else 0,
                               scale_mode=oracle.SCALE_AMAX if scale_mode == "amax" else oracle.SCALE_POW2,
-                              master_bf16=(master == "bf16"), l2_coupled=(decay_mode == "l2"))
+                              master_bf16=(master == "bf16"), l2_coupled=(decay_mode == "l2"),
+                              history_len=history_len, margin=margin, delayed_from=delayed_from)
 
 
 def compare_tensor(name: str, st: OracleState, p_gpu: np.ndarray, cm_gpu: np.ndarray, cv_gpu: np.ndarray,

@@ -185,7 +185,7 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
     sm2, sv2 = list(sm), list(sv)
     choose = amax_scale if amax_mode else pow2_scale
     amaxes = []
-    for bi, lo in enumerate(range(0, n if block > 0 else max(n, 1), blen)):
+    for bi, lo in enumerate(range(0, n, blen)):
         hi = min(lo + blen, n)
         si = bi if block > 0 else 0
         m1s, v1s = [], []

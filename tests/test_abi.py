@@ -98,6 +98,21 @@ def test_speculative_schedule_argument_errors():
     bad_decay = pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 5)
     assert L.fp8adam_init(ctypes.byref(h), alt, 1, ctypes.byref(bad_decay), None) == -1
     assert "decay_mode" in pk.fp8adam_last_error()
+    # delayed scaling: per-tensor scales, no speculative schedule, a history, sane H and margin
+    hist = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, None, None, 112))
+    no_hist = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, None, None, None))
+    odd_hist = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, None, None, 114))
+    D = pk.SCALING_DELAYED
+    for arr, bad, code, text in (
+            (hist, pk.ConfigArg(0, 1, pk.SCALE_BLOCK128, 0, 0, 0, 0, 0, 0, D), -1, "per-tensor"),
+            (alt, pk.ConfigArg(0, 1, 0, 0, 0, 0, pk.SCHEDULE_SPECULATIVE, 0, 0, D), -1, "TWO_PASS"),
+            (hist, pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, D, 2000), -1, "1024"),
+            (hist, pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, D, 16, 65), -1, "margin"),
+            (hist, pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, 9), -1, "scaling"),
+            (no_hist, pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, D), -1, "amax_history"),
+            (odd_hist, pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, D), -2, "amax_history")):
+        assert L.fp8adam_init(ctypes.byref(h), arr, 1, ctypes.byref(bad), None) == code
+        assert text in pk.fp8adam_last_error()
     misaligned = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, 113, 128))
     assert L.fp8adam_init(ctypes.byref(h), misaligned, 1, ctypes.byref(cfg), None) == -2
     assert L.fp8adam_current_buffer(None) == -1
