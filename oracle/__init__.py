@@ -49,7 +49,22 @@ class Config(ctypes.Structure):
         ("block", ctypes.c_int), ("scale_mode", ctypes.c_int), ("master_bf16", ctypes.c_int),
         ("l2_coupled", ctypes.c_int),
         ("history_len", ctypes.c_int), ("margin", ctypes.c_int), ("delayed_from", ctypes.c_int64),
+        ("grad_factor", ctypes.c_float), ("sched_step", ctypes.c_int64),
     ]
+
+
+class AmpConfig(ctypes.Structure):
+    _fields_ = [("max_norm", ctypes.c_float), ("growth_factor", ctypes.c_float),
+                ("backoff_factor", ctypes.c_float), ("growth_interval", ctypes.c_int32)]
+
+
+class AmpState(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("growth_tracker", ctypes.c_int32), ("step", ctypes.c_int64),
+                ("found_inf", ctypes.c_int32), ("grad_norm", ctypes.c_float), ("clip_coef", ctypes.c_float),
+                ("grad_factor", ctypes.c_float)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class Stats(ctypes.Structure):
@@ -100,6 +115,10 @@ def lib() -> ctypes.CDLL:
                                             f32p, f32p]
         L.ref_step_fp32_moments.restype = ctypes.c_int
         L.ref_rounding_is_nearest.restype = ctypes.c_int
+        L.ref_grad_sumsq.argtypes = [u16p, ctypes.c_int64, P, ctypes.POINTER(ctypes.c_int64)]
+        L.ref_sumsq_total.argtypes = [P]
+        L.ref_sumsq_total.restype = ctypes.c_double
+        L.ref_amp_control.argtypes = [P, ctypes.c_int64, ctypes.POINTER(AmpConfig), ctypes.POINTER(AmpState)]
         _lib = L
     return _lib
 
@@ -162,11 +181,14 @@ class Hyper:
 
 def make_config(h: Hyper, m_fmt=E4M3, v_fmt=E5M2, block: int = 0,
                 scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False,
-                history_len: int = 0, margin: int = 0, delayed_from: int = 2) -> Config:
-    """history_len > 0 selects delayed scaling (per-tensor scales only)."""
+                history_len: int = 0, margin: int = 0, delayed_from: int = 2, grad_factor: float = 1.0,
+                sched_step: int = 0) -> Config:
+    """history_len > 0 selects delayed scaling (per-tensor scales only); grad_factor
+    multiplies every gradient first; sched_step (0: h.step) is the step number
+    compared with delayed_from."""
     return Config(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step,
                   fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled),
-                  history_len, margin, delayed_from)
+                  history_len, margin, delayed_from, grad_factor, sched_step)
 
 
 def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,
@@ -216,3 +238,27 @@ def step_fp32_moments(cfg: Config, p: np.ndarray, g_bits: np.ndarray, m: np.ndar
                                      _ptr(m), _ptr(v))
     if rc != 0:
         raise ValueError("oracle ref_step_fp32_moments rejected its arguments")
+
+
+class GradSums:
+    """Exact sum of squares (per-exponent integer buckets) and non-finite count
+    of bf16 gradients, accumulated tensor by tensor."""
+
+    def __init__(self):
+        self.acc = np.zeros(256, np.uint64)
+        self.nonfinite = ctypes.c_int64(0)
+
+    def add(self, g_bits: np.ndarray) -> "GradSums":
+        g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+        lib().ref_grad_sumsq(_ptr(g), g.size, _ptr(self.acc), ctypes.byref(self.nonfinite))
+        return self
+
+    def total(self) -> float:
+        """The exact sum of squares rounded once to double."""
+        return lib().ref_sumsq_total(_ptr(self.acc))
+
+
+def amp_control(sums: GradSums, cfg: AmpConfig, state: AmpState) -> AmpState:
+    """One loss-scaler / clipping decision over the whole list; updates state in place."""
+    lib().ref_amp_control(_ptr(sums.acc), sums.nonfinite.value, ctypes.byref(cfg), ctypes.byref(state))
+    return state

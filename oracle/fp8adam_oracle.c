@@ -240,6 +240,9 @@ typedef struct {
     int history_len;  /* 0: just-in-time scales; H >= 1: delayed scaling over an amax history of H steps */
     int margin;       /* delayed: the scale is chosen for amax_ref * 2^margin (0..64) */
     int64_t delayed_from; /* delayed: steps t < delayed_from choose the scale just in time */
+    float grad_factor;    /* every bf16 gradient is multiplied by this first (1: none; loss-scale
+                             unscaling and norm clipping otherwise) */
+    int64_t sched_step;   /* the step number compared with delayed_from (0: step) */
 } ref_config;
 
 typedef struct {
@@ -340,7 +343,7 @@ int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
         return -1;
     const int H = c->history_len;
     if (H > 0 && (c->block > 0 || !hist || c->margin < 0 || c->margin > 64)) return -1;
-    const int delayed = H > 0 && c->step >= c->delayed_from;
+    const int delayed = H > 0 && (c->sched_step > 0 ? c->sched_step : c->step) >= c->delayed_from;
     ref_consts k = make_consts(c);
     float fmax_m = ref_format_max(c->m_fmt), fmax_v = ref_format_max(c->v_fmt);
     int64_t blen = c->block > 0 ? c->block : (n > 0 ? n : 1);
@@ -364,7 +367,7 @@ int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
         float am = 0.0f, av = 0.0f;
         for (int64_t i = lo; i < hi; i++) {
             float pi = c->master_bf16 ? bf16_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
-            float gi = effective_grad(&k, bf16_to_f32(g[i]), pi);
+            float gi = effective_grad(&k, bf16_to_f32(g[i]) * c->grad_factor, pi);
             float mi = ref_decode(c->m_fmt, cm[i]) * old_sm;
             float vi = ref_decode(c->v_fmt, cv[i]) * old_sv;
             moment_update(&k, gi, mi, vi, &m1[i], &v1[i]);
@@ -445,7 +448,7 @@ int ref_step_fp32_moments(const ref_config *c, int64_t n, float *p, const uint16
     ref_consts k = make_consts(c);
     for (int64_t i = 0; i < n; i++) {
         float m1, v1;
-        moment_update(&k, effective_grad(&k, bf16_to_f32(g[i]), p[i]), m[i], v[i], &m1, &v1);
+        moment_update(&k, effective_grad(&k, bf16_to_f32(g[i]) * c->grad_factor, p[i]), m[i], v[i], &m1, &v1);
         p[i] = (float)param_update(&k, (double)p[i], m1, v1);
         m[i] = m1;
         v[i] = v1;
@@ -455,3 +458,131 @@ int ref_step_fp32_moments(const ref_config *c, int64_t n, float *p, const uint16
 
 /* The library is meant to run in the default rounding mode. */
 int ref_rounding_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* ------------------------------------------------- loss scaling and clipping
+ *
+ * [P3 "Strategies": gradient (loss) scaling that grows the scale after a run of
+ * overflow-free iterations and shrinks it on overflow; gradient clipping.
+ * P3 code example: the gradients are unscaled, clipped to a global norm of
+ * max_norm = 1.0, and the optimizer step is skipped when they overflowed.]
+ * Readings (the page gives the calls, not the arithmetic; these are the
+ * definitions of the library calls it names):
+ *   - unscale: g / S with inv_S = 1/S rounded to fp32;
+ *   - non-finite: any Inf/NaN gradient element skips the whole step (nothing
+ *     changes but the loss scale), S *= backoff and the growth count restarts;
+ *     otherwise the count grows, and reaching growth_interval multiplies S by
+ *     growth (if that stays finite) and restarts it;
+ *   - norm: ||g / S|| over every tensor, from the EXACT sum of squares;
+ *   - clip coefficient c = min(1, max_norm / (norm + 1e-6)) rounded to fp32
+ *     (c = 1 without clipping); every gradient is then multiplied by the one
+ *     fp32 factor c * inv_S (one rounding per element);
+ *   - a skipped step does not count: the Adam step t is the number of steps
+ *     taken, kept with the scaler.
+ */
+
+/* Exact sum of squares of bf16 values, kept per binary exponent: a finite
+ * bf16 value is M * 2^(E - 134) with M = 128 + mantissa for E >= 1 and
+ * M = mantissa (E taken as 1) for subnormals, so its square is
+ * M^2 * 2^(2E - 268) with M^2 < 2^16; acc[E] sums M^2 exactly. */
+void ref_grad_sumsq(const uint16_t *g, int64_t n, uint64_t acc[256], int64_t *nonfinite)
+{
+    for (int64_t i = 0; i < n; i++) {
+        uint32_t b = g[i];
+        uint32_t e = (b >> 7) & 0xFFu, mant = b & 0x7Fu;
+        if (e == 0xFFu) { (*nonfinite)++; continue; }
+        uint32_t m = e ? (0x80u | mant) : mant;
+        if (!e) e = 1;
+        acc[e] += (uint64_t)m * m;
+    }
+}
+
+/* sum_E acc[E] * 2^(2E - 268), exact in a 704-bit integer (bit 0 = 2^-266),
+ * then rounded once to double (round to nearest even). */
+double ref_sumsq_total(const uint64_t acc[256])
+{
+    enum { L = 11 };
+    uint64_t big[L];
+    memset(big, 0, sizeof big);
+    for (int e = 1; e < 255; e++) {
+        if (!acc[e]) continue;
+        int sh = 2 * e - 2;                       /* 2E - 268 - (-266) */
+        int w = sh / 64, b = sh % 64;
+        uint64_t lo = acc[e] << b, hi = b ? acc[e] >> (64 - b) : 0;
+        unsigned __int128 carry = 0;
+        for (int k = w; k < L; k++) {
+            unsigned __int128 add = (k == w ? lo : (k == w + 1 ? hi : 0));
+            unsigned __int128 sum = (unsigned __int128)big[k] + add + carry;
+            big[k] = (uint64_t)sum;
+            carry = sum >> 64;
+            if (k > w + 1 && !carry) break;
+        }
+    }
+    int top = -1;
+    for (int k = L - 1; k >= 0 && top < 0; k--)
+        if (big[k]) top = 64 * k + 63 - __builtin_clzll(big[k]);
+    if (top < 0) return 0.0;
+    /* the 64 bits top..top-63 (zeros below bit 0), and whether anything lies below them */
+    uint64_t hi64 = 0;
+    int sticky = 0;
+    for (int j = 0; j < 64; j++) {
+        int bit = top - j;
+        uint64_t v = bit >= 0 ? (big[bit / 64] >> (bit % 64)) & 1u : 0u;
+        hi64 = (hi64 << 1) | v;
+    }
+    for (int bit = top - 64; bit >= 0 && !sticky; bit--)
+        if ((big[bit / 64] >> (bit % 64)) & 1u) sticky = 1;
+    uint64_t keep = hi64 >> 11, rem = hi64 & 0x7FFu;
+    if (rem > 0x400u || (rem == 0x400u && (sticky || (keep & 1u)))) keep++;
+    return ldexp((double)keep, top - 52 - 266);
+}
+
+typedef struct {
+    float max_norm;         /* <= 0: no clipping */
+    float growth_factor, backoff_factor;
+    int32_t growth_interval;
+} ref_amp_config;
+
+typedef struct {
+    float scale;
+    int32_t growth_tracker;
+    int64_t step;           /* Adam steps taken */
+    int32_t found_inf;
+    float grad_norm, clip_coef, grad_factor;
+} ref_amp_state;
+
+/* One scaler decision from the sums of every tensor's gradients (acc and
+ * nonfinite summed over the list).  Updates st; on success st->step is the t
+ * of the step to run and st->grad_factor the factor for ref_step. */
+void ref_amp_control(const uint64_t acc[256], int64_t nonfinite, const ref_amp_config *cfg,
+                     ref_amp_state *st)
+{
+    float inv = (float)(1.0 / (double)st->scale);
+    if (nonfinite > 0) {
+        st->found_inf = 1;
+        st->grad_norm = NAN;
+        st->clip_coef = 1.0f;
+        st->grad_factor = 0.0f;
+        st->scale = st->scale * cfg->backoff_factor;
+        st->growth_tracker = 0;
+        return;
+    }
+    double norm = sqrt(ref_sumsq_total(acc)) * (double)inv;
+    double c = 1.0;
+    if (cfg->max_norm > 0.0f) {
+        c = (double)cfg->max_norm / (norm + 1e-6);
+        if (c > 1.0) c = 1.0;
+    }
+    st->found_inf = 0;
+    st->grad_norm = (float)norm;
+    st->clip_coef = (float)c;
+    st->grad_factor = st->clip_coef * inv;
+    st->step += 1;
+    int32_t next = st->growth_tracker + 1;
+    if (next == cfg->growth_interval) {
+        float grown = st->scale * cfg->growth_factor;
+        if (isfinite(grown)) st->scale = grown;
+        st->growth_tracker = 0;
+    } else {
+        st->growth_tracker = next;
+    }
+}
