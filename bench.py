@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
     ap.add_argument("--scaling", default="just_in_time", choices=["just_in_time", "delayed"],
                     help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")
+    ap.add_argument("--amp", action="store_true",
+                    help="loss-scaled gradients (scale 2^16) through the fused unscale / Inf-NaN skip / "
+                         "global-norm clip (max_norm 1.0) step")
     ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -154,18 +157,28 @@ def main():
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
+    loss_scale = 2.0 ** 16
+    amp = pk.amp_state(loss_scale, dev) if args.amp else None
+
     def load_grads(t):
-        if args.same_grad:
+        if args.same_grad and t > 1:
             return
         for i, (_, shp) in enumerate(shapes):
-            grads[i].copy_(workloads.make_grad(w, i, shp, t, dev))
+            g = workloads.make_grad(w, i, shp, t, dev)
+            grads[i].copy_((g.float() * loss_scale).to(torch.bfloat16) if args.amp else g)
+
+    def opt_step(t):
+        if args.amp:
+            opt.step_amp(amp, step=t, max_norm=1.0, **hp)
+        else:
+            opt.step(step=t, **hp)
 
     log(f"context: {opt.num_chunks} chunks, schedule {schedule}, scaling {scaling}; warmup {args.warmup} steps")
     t = 0
     for _ in range(args.warmup):
         t += 1
         load_grads(t)
-        opt.step(step=t, **hp)
+        opt_step(t)
         torch.cuda.synchronize()
         log(f"warm-up step {t} done")
 
@@ -177,7 +190,7 @@ def main():
         load_grads(t)  # not timed
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        opt.step(step=t, **hp)
+        opt_step(t)
         e1.record(stream)
         evs.append((e0, e1))
     torch.cuda.synchronize()
@@ -207,6 +220,8 @@ def main():
     amax_bpp = 4.0 + ((4.0 if w.master == "fp32" else 2.0) if w.decay_mode == "l2" else 0.0)
     step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass"
                                                    and scaling == "just_in_time") else 0.0)
+    if args.amp:  # + the gradient-norm pass (g read once)
+        step_bytes += 2.0 * total
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
@@ -242,6 +257,7 @@ def main():
                    "v_format": w.v_fmt, "scale": w.granularity, "master": w.master,
                    "weight_decay": w.weight_decay, "decay_mode": w.decay_mode, "schedule": schedule,
                    "scaling": scaling if scaling == "just_in_time" else "delayed (amax history 16, margin 0)",
+                   "loss_scaling": "scale 2^16, Inf/NaN skip, clip to global norm 1.0" if args.amp else None,
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,

@@ -171,6 +171,48 @@ int fp8adam_init(fp8adam_ctx **out, const fp8adam_tensor *tensors, int32_t n,
  * consistent.  Steps of one context must not overlap. */
 int fp8adam_step(fp8adam_ctx *ctx, const fp8adam_hparams *hp, hipStream_t stream);
 
+/* ---- loss scaling, non-finite skip and global-norm clipping, fused ----
+ * The zyxy.net article's strategies section scales the loss, grows the scale after a
+ * run of overflow-free steps and shrinks it on overflow, and clips gradients; its code
+ * example unscales the gradients, clips them to a global norm of 1.0 and skips the
+ * optimizer step when they overflowed.  fp8adam_step_amp does all of it on the device,
+ * with no host synchronization:
+ *   1. one read of every gradient (2 bytes per parameter): the sum of squares in fp64 and
+ *      the count of Inf/NaN elements, over every tensor of the context;
+ *   2. one work-group takes the decision, like torch.amp.GradScaler with a fused optimizer:
+ *      any Inf/NaN -> the step is skipped (parameters, codes, scales and history unchanged),
+ *      scale *= backoff_factor, growth_tracker = 0; otherwise norm = ||g|| / scale,
+ *      clip_coef = min(1, max_norm / (norm + 1e-6)) in fp32 (1 if max_norm <= 0),
+ *      grad_factor = clip_coef * fp32(1/scale), step += 1 and the growth rule (after
+ *      growth_interval taken steps, scale *= growth_factor if that stays finite);
+ *   3. the step as fp8adam_step, with every bf16 gradient multiplied by grad_factor and the
+ *      bias corrections of t = state.step (skipped steps are not counted); with delayed
+ *      scaling this t also picks the history slot, (t-1) mod H.
+ * The sum of squares is deterministic (fixed reduction order). */
+typedef struct {
+    float scale;             /* in/out: loss scale S (the gradients are those of loss * S) */
+    int32_t growth_tracker;  /* in/out: taken steps since the scale last changed */
+    int64_t step;            /* in/out: Adam steps taken so far (start at 0) */
+    int32_t found_inf;       /* out: 1 if the last call found an Inf/NaN gradient and skipped */
+    float grad_norm;         /* out: ||g|| / S over every tensor (NaN when skipped) */
+    float clip_coef;         /* out: the clip coefficient (1: not clipped) */
+    float grad_factor;       /* out: clip_coef / S, the factor applied to every gradient */
+} fp8adam_amp_state;         /* device memory, caller-owned, 8-byte aligned, 32 bytes */
+
+typedef struct {
+    float max_norm;          /* > 0: clip the global norm to it; <= 0: no clipping */
+    float growth_factor;     /* > 1 (torch's default 2) */
+    float backoff_factor;    /* in (0, 1) (default 0.5) */
+    int32_t growth_interval; /* >= 1 (default 2000) */
+} fp8adam_amp_config;
+
+/* One step with loss scaling and clipping, enqueued on `stream`; state is device memory
+ * read and written by the step.  hp->step is the caller's call count and only chooses the
+ * schedule (speculative / delayed from which call); the bias correction uses state.step.
+ * Returns EINVAL for a bad hp, amp or state (null, misaligned) before enqueuing anything. */
+int fp8adam_step_amp(fp8adam_ctx *ctx, const fp8adam_hparams *hp, const fp8adam_amp_config *amp,
+                     fp8adam_amp_state *state, hipStream_t stream);
+
 /* Copy the diagnostics of the last step into out_host[0..n) (n = the context's
  * tensor count; EINVAL otherwise).  Synchronizes `stream`. */
 int fp8adam_stats(fp8adam_ctx *ctx, fp8adam_stats_t *out_host, int32_t n, hipStream_t stream);
@@ -204,7 +246,8 @@ int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
  * 6 = speculative scale check, 7 = re-quantization fix-up, 8 = delayed-scaling pass,
- * 9 = delayed-scaling commit), total_ms[k] and count[k].
+ * 9 = delayed-scaling commit, 10 = gradient-norm pass, 11 = loss-scale decision),
+ * total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);
 

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,12 +34,13 @@ SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
-                "spec_check", "fixup", "delayed_pass", "delayed_commit")
+                "spec_check", "fixup", "delayed_pass", "delayed_commit", "gradnorm_pass", "amp_decision")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
-           "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer")
+           "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
+           "fp8adam_step_amp")
 
 
 class Fp8AdamError(RuntimeError):
@@ -69,6 +71,16 @@ class HParamsArg(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class AmpConfigArg(ctypes.Structure):
+    _fields_ = [("max_norm", ctypes.c_float), ("growth_factor", ctypes.c_float),
+                ("backoff_factor", ctypes.c_float), ("growth_interval", ctypes.c_int32)]
+
+
+# fp8adam_amp_state, as it lies in device memory (32 bytes)
+AMP_STATE_DTYPE = np.dtype([("scale", "<f4"), ("growth_tracker", "<i4"), ("step", "<i8"), ("found_inf", "<i4"),
+                            ("grad_norm", "<f4"), ("clip_coef", "<f4"), ("grad_factor", "<f4")])
+
+
 class StatsArg(ctypes.Structure):
     _fields_ = [("amax_m", ctypes.c_float), ("amax_v", ctypes.c_float),
                 ("scale_m", ctypes.c_float), ("scale_v", ctypes.c_float),
@@ -95,6 +107,7 @@ def load() -> ctypes.CDLL:
     L.fp8adam_init.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg), vp]
     L.fp8adam_step.argtypes = [vp, ctypes.POINTER(HParamsArg), vp]
     L.fp8adam_stats.argtypes = [vp, ctypes.POINTER(StatsArg), i32, vp]
+    L.fp8adam_step_amp.argtypes = [vp, ctypes.POINTER(HParamsArg), ctypes.POINTER(AmpConfigArg), vp, vp]
     L.fp8adam_destroy.argtypes = [vp]
     L.fp8adam_destroy.restype = None
     L.fp8adam_last_error.restype = ctypes.c_char_p
@@ -141,6 +154,25 @@ def fp8adam_init(tensors: list[TensorArg], cfg: ConfigArg, stream: int | None = 
 
 def fp8adam_step(ctx: int, hp: HParamsArg, stream: int | None = None) -> None:
     _check(load().fp8adam_step(ctx, ctypes.byref(hp), current_stream() if stream is None else stream))
+
+
+def fp8adam_step_amp(ctx: int, hp: HParamsArg, amp: AmpConfigArg, state: int, stream: int | None = None) -> None:
+    _check(load().fp8adam_step_amp(ctx, ctypes.byref(hp), ctypes.byref(amp), state,
+                                   current_stream() if stream is None else stream))
+
+
+def amp_state(init_scale: float = 65536.0, device="cuda") -> torch.Tensor:
+    """A fresh loss-scaler state (fp8adam_amp_state) in device memory: 32 bytes."""
+    rec = np.zeros(1, AMP_STATE_DTYPE)
+    rec["scale"] = init_scale
+    rec["clip_coef"] = 1.0
+    return torch.from_numpy(rec.view(np.uint8).copy()).to(device)
+
+
+def read_amp_state(t: torch.Tensor) -> dict:
+    """The fields of a device-side loss-scaler state (copies to the host)."""
+    rec = t.detach().cpu().numpy().view(AMP_STATE_DTYPE)[0]
+    return {k: rec[k].item() for k in AMP_STATE_DTYPE.names}
 
 
 def fp8adam_stats(ctx: int, n: int, stream: int | None = None) -> list[dict]:
@@ -297,6 +329,20 @@ class FP8AdamW:
              weight_decay: float = 0.0, step: int) -> None:
         with torch.cuda.device(self.device):
             fp8adam_step(self._ctx, HParamsArg(lr, beta1, beta2, eps, weight_decay, step))
+
+    def step_amp(self, amp_state: torch.Tensor, *, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                 eps: float = 1e-8, weight_decay: float = 0.0, step: int, max_norm: float = 0.0,
+                 growth_factor: float = 2.0, backoff_factor: float = 0.5, growth_interval: int = 2000) -> None:
+        """A step on gradients of (loss * scale): unscale, skip on Inf/NaN, clip the
+        global norm to max_norm (if > 0), all on the device (``amp_state`` from
+        ``amp_state()``).  ``step`` counts calls; the bias correction uses the
+        state's count of taken steps."""
+        if amp_state.dtype != torch.uint8 or amp_state.numel() != AMP_STATE_DTYPE.itemsize:
+            raise ValueError("amp_state must be the 32-byte tensor from amp_state()")
+        with torch.cuda.device(self.device):
+            fp8adam_step_amp(self._ctx, HParamsArg(lr, beta1, beta2, eps, weight_decay, step),
+                             AmpConfigArg(max_norm, growth_factor, backoff_factor, growth_interval),
+                             amp_state.data_ptr())
 
     def stats(self) -> list[dict]:
         with torch.cuda.device(self.device):

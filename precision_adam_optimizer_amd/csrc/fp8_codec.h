@@ -127,6 +127,7 @@ struct StepConsts {
   float inv_bc2;       // 1 / (1 - beta2^t)
   float eps;
   float grow_m, grow_v; // speculative schedule: expected amax growth (1-beta^t)/(1-beta^(t-1))
+  float gfac;          // factor applied to every bf16 gradient first (1; loss-scale unscaling and clipping)
   float margin_scale;  // delayed scaling: 2^margin
   int hist_len;        // delayed scaling: H (0: no history)
   int hist_slot;       // delayed scaling: (t-1) mod H, the slot this step's amax goes to
@@ -154,6 +155,13 @@ template <bool L2>
 __device__ __forceinline__ float grad_eff(const StepConsts& c, float g, float p) {
   if constexpr (L2) return __builtin_fmaf(c.l2, p, g);
   else return g;
+}
+
+// The gradient as the moments take it: times the step's gradient factor (exact
+// for 1), then the coupled-L2 term if any.
+template <bool L2>
+__device__ __forceinline__ float grad_in(const StepConsts& c, float g, float p) {
+  return grad_eff<L2>(c, g * c.gfac, p);
 }
 
 // AdamW parameter update from the fresh moments: m in the numerator times the

@@ -119,6 +119,31 @@ struct TensorDesc {
 // or the delayed scale from the amax history.
 enum UpdateMode { kModeJit = 0, kModeSpec = 1, kModeDelayed = 2 };
 
+// Loss-scaling control of the step in flight, written on the device by
+// k_gradctl (library-owned): whether the step is skipped (a non-finite
+// gradient), the gradient factor clip_coef / S, and the bias-correction
+// constants of the device-side step count.
+struct GradCtl {
+  int32_t skip;
+  float gfac;
+  float step_size, inv_bc2, grow_m, grow_v;
+  int32_t hist_slot;  // delayed scaling: (t-1) mod H of the device-side t
+};
+
+// With loss scaling, take the step's gradient factor and bias corrections;
+// true if the step is skipped (the kernel then changes nothing).
+__device__ __forceinline__ bool amp_apply(const GradCtl* gctl, StepConsts& c) {
+  if (gctl == nullptr) return false;
+  if (gctl->skip) return true;
+  c.gfac = gctl->gfac;
+  c.step_size = gctl->step_size;
+  c.inv_bc2 = gctl->inv_bc2;
+  c.grow_m = gctl->grow_m;
+  c.grow_v = gctl->grow_v;
+  c.hist_slot = gctl->hist_slot;
+  return false;
+}
+
 enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
@@ -271,7 +296,7 @@ __device__ __forceinline__ void fresh_moments(const StepConsts& c, const Group& 
   decode4<MF>(G.cm, m);
   decode4<VF>(G.cv, v);
 #pragma unroll
-  for (int j = 0; j < 4; j++) moment_update(c, grad_eff<L2>(c, g[j], p[j]), m[j] * sm, v[j] * sv, m1[j], v1[j]);
+  for (int j = 0; j < 4; j++) moment_update(c, grad_in<L2>(c, g[j], p[j]), m[j] * sm, v[j] * sv, m1[j], v1[j]);
 }
 
 template <bool BF16P>
@@ -350,9 +375,9 @@ template <int MF, int VF, bool BF16P, bool L2>
 __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ chunk_tid,
                                                    uint2* __restrict__ partial, StepConsts c, int chunk_log2,
-                                                   int64_t nwork) {
+                                                   int64_t nwork, const GradCtl* __restrict__ gctl) {
   const int64_t w = work_index<false>(nwork);
-  if (w < 0) return;
+  if (w < 0 || amp_apply(gctl, c)) return;
   const int tid = chunk_tid[w];
   const TensorDesc d = descs[tid];
   const int64_t start = (w - d.chunk0) << chunk_log2;
@@ -386,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
   // ragged tail (< 4 elements at the end of a tensor)
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = grad_eff<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
+    const float g = grad_in<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
     float m1, v1;
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     am = max(am, abs_bits(m1));
@@ -411,8 +436,15 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
                                                            float* __restrict__ old_scale,
                                                            unsigned long long* __restrict__ counters,
                                                            int chunk_log2, int32_t* __restrict__ flags,
-                                                           int hist_len, int hist_slot) {
+                                                           int hist_len, int hist_slot,
+                                                           const GradCtl* __restrict__ gctl) {
   const int t = blockIdx.x;
+  if (gctl != nullptr && gctl->skip) {  // skipped step: scales, amax and history stay
+    if (threadIdx.x == 0) flags[t] = 0;
+    if (STATS && threadIdx.x < kStatsPerTensor) counters[(int64_t)t * kStatsPerTensor + threadIdx.x] = 0ull;
+    return;
+  }
+  if (gctl != nullptr) hist_slot = gctl->hist_slot;
   const TensorDesc d = descs[t];
   const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
   uint32_t am = 0, av = 0;
@@ -466,7 +498,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
                                                      const uint32_t* __restrict__ amax,
                                                      const float* __restrict__ old_scale, StepConsts c,
                                                      unsigned long long* __restrict__ counters, int chunk_log2,
-                                                     uint2* __restrict__ part_amax, int64_t nwork) {
+                                                     uint2* __restrict__ part_amax, int64_t nwork,
+                                                     const GradCtl* __restrict__ gctl) {
   constexpr bool SPEC = MODE == kModeSpec;
   constexpr bool PARTS = MODE != kModeJit;  // per-part amax partials for the commit kernel
   const int64_t w = work_index<kXcdStreams>(nwork);
@@ -482,6 +515,20 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   // codes go back in place (two-pass) or into the other buffer (speculative)
   uint8_t* const dm = SPEC ? dst_descs[tid].m : d.m;
   uint8_t* const dv = SPEC ? dst_descs[tid].v : d.v;
+  if (amp_apply(gctl, c)) {  // skipped step
+    // the speculative schedule switches buffers regardless: carry the codes over
+    if constexpr (SPEC) {
+      for (int64_t i = start + kGroup * threadIdx.x; i < gend; i += kSubTile) {
+        st_global<uint32_t>(dm + i, ld_global<uint32_t>(d.m + i));
+        st_global<uint32_t>(dv + i, ld_global<uint32_t>(d.v + i));
+      }
+      if (gend + threadIdx.x < end) {
+        st_global<uint8_t>(dm + gend + threadIdx.x, ld_global<uint8_t>(d.m + gend + threadIdx.x));
+        st_global<uint8_t>(dv + gend + threadIdx.x, ld_global<uint8_t>(d.v + gend + threadIdx.x));
+      }
+    }
+    return;
+  }
   float sm, sv, ism, isv;
   if constexpr (SPEC) {
     sm = ld_global<float>(d.sm);
@@ -544,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
     const float p0 = load_p1<BF16P>(d, i);
-    const float g = grad_eff<L2>(c, load_g1(d, i), p0);
+    const float g = grad_in<L2>(c, load_g1(d, i), p0);
     float m1, v1;
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     const float p = param_update(c, p0, m1, v1);
@@ -577,7 +624,8 @@ template <int MF, int VF, int SMODE>
 __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorDesc* __restrict__ descs,
                                                                    const uint2* __restrict__ part_amax,
                                                                    uint32_t* __restrict__ amax, StepConsts c,
-                                                                   int chunk_log2) {
+                                                                   int chunk_log2, const GradCtl* __restrict__ gctl) {
+  if (amp_apply(gctl, c)) return;  // skipped step: scales, amax and history stay
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
   const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
@@ -633,8 +681,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
                                                                 float* __restrict__ old_scale,
                                                                 int32_t* __restrict__ flags,
                                                                 unsigned long long* __restrict__ counters,
-                                                                int chunk_log2, float grow_m, float grow_v) {
+                                                                int chunk_log2, StepConsts c,
+                                                                const GradCtl* __restrict__ gctl) {
   const int t = blockIdx.x;
+  if (amp_apply(gctl, c)) {  // skipped step: scales and amax stay, nothing to fix up
+    if (threadIdx.x == 0) flags[t] = 0;
+    return;
+  }
+  const float grow_m = c.grow_m, grow_v = c.grow_v;
   const TensorDesc d = descs[t];
   const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
   const int64_t part0 = d.chunk0 << (chunk_log2 - kPartLog2);
@@ -726,7 +780,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
         for (int j = 0; j < 4; j++) {
           float m1, v1;
           // moment_update computes both moments; only the one being fixed is used
-          moment_update(c, g[j], x[j] * s_old, x[j] * s_old, m1, v1);
+          moment_update(c, g[j] * c.gfac, x[j] * s_old, x[j] * s_old, m1, v1);
           x[j] = IS_V ? v1 : m1;
           q[j] = x[j] * inv_new;
         }
@@ -744,7 +798,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
-    const float g = load_g1(d, i);
+    const float g = load_g1(d, i) * c.gfac;
     const float x0 = decode1<FMT>(ld_global<uint8_t>(src + i)) * s_old;
     float m1, v1;
     moment_update(c, g, x0, x0, m1, v1);
@@ -767,9 +821,9 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
                                                     const float* __restrict__ old_scale,
                                                     const int32_t* __restrict__ flags, StepConsts c,
                                                     unsigned long long* __restrict__ counters, int chunk_log2,
-                                                    int64_t nwork) {
+                                                    int64_t nwork, const GradCtl* __restrict__ gctl) {
   const int64_t w = work_index<false>(nwork);
-  if (w < 0) return;
+  if (w < 0 || amp_apply(gctl, c)) return;
   const int tid = chunk_tid[w];
   const int32_t f = flags[tid];
   if (!f) return;  // uniform for the work-group
@@ -790,6 +844,146 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
                                   cnt[kSatV]);
   }
   flush_counters<STATS>(counters, tid, cnt);
+}
+
+// ------------------------------------------- loss scaling and clipping
+//
+// k_gradnorm: one work-group per chunk reads the bf16 gradients only (2 bytes
+// per parameter) and writes the chunk's sum of squares in fp64 (each square is
+// exact in fp64) and its count of Inf/NaN elements.  k_gradctl (one
+// work-group) sums the partials in a fixed order, so the result is
+// deterministic, and takes the scaler's decision: skip the step (non-finite
+// gradient; the scale backs off) or run it with the gradient factor
+// c / S, c = min(1, max_norm / (||g||/S + 1e-6)), and the bias corrections of
+// the device-side step count, which only a taken step advances.
+
+__global__ __launch_bounds__(kThreads) void k_gradnorm(const TensorDesc* __restrict__ descs,
+                                                       const int32_t* __restrict__ chunk_tid,
+                                                       double* __restrict__ gpart, int chunk_log2, int64_t nwork) {
+  const int64_t w = work_index<false>(nwork);
+  if (w < 0) return;
+  const TensorDesc d = descs[chunk_tid[w]];
+  const int64_t start = (w - d.chunk0) << chunk_log2;
+  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+  const int64_t gend = start + ((end - start) & ~(int64_t)3);
+  double acc = 0.0;
+  uint32_t bad = 0;
+  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
+    vu2 gg[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) gg[u] = ld_stream<vu2, FP8ADAM_NT_AMAX != 0>(d.g + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kSubTile;
+      if (i < gend) {
+        const uint32_t x = gg[u].x, y = gg[u].y;
+        bad += ((x & 0x7F80u) == 0x7F80u) + ((x & 0x7F800000u) == 0x7F800000u) +
+               ((y & 0x7F80u) == 0x7F80u) + ((y & 0x7F800000u) == 0x7F800000u);
+        const double a = bf16_lo(x), b = bf16_hi(x), e = bf16_lo(y), f = bf16_hi(y);
+        acc = __builtin_fma(a, a, acc);
+        acc = __builtin_fma(b, b, acc);
+        acc = __builtin_fma(e, e, acc);
+        acc = __builtin_fma(f, f, acc);
+      }
+    }
+  }
+  if (gend + threadIdx.x < end) {
+    const uint32_t x = ld_global<uint16_t>(d.g + gend + threadIdx.x);
+    bad += (x & 0x7F80u) == 0x7F80u;
+    const double a = bf16_lo(x);
+    acc = __builtin_fma(a, a, acc);
+  }
+  // fixed-order reduction: butterfly within the wave, then waves in order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    acc += __shfl_xor(acc, o);
+    bad += (uint32_t)__shfl_xor((int)bad, o);
+  }
+  __shared__ double sacc[kThreads / 64];
+  __shared__ uint32_t sbad[kThreads / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sacc[wave] = acc;
+    sbad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kThreads / 64; k++) {
+      acc += sacc[k];
+      bad += sbad[k];
+    }
+    st_global<double>(gpart + 2 * w, acc);
+    st_global<double>(gpart + 2 * w + 1, (double)bad);
+  }
+}
+
+__global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __restrict__ gpart, int64_t nchunks,
+                                                           fp8adam_amp_state* __restrict__ st, GradCtl* __restrict__ ctl,
+                                                           fp8adam_amp_config cfg, float lr, float beta1, float beta2,
+                                                           int hist_len) {
+  double acc = 0.0, bad = 0.0;
+  for (int64_t k = threadIdx.x; k < nchunks; k += kReduceThreads) {
+    acc += gpart[2 * k];
+    bad += gpart[2 * k + 1];
+  }
+  __shared__ double sacc[kReduceThreads], sbad[kReduceThreads];
+  sacc[threadIdx.x] = acc;
+  sbad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int h = kReduceThreads / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      sacc[threadIdx.x] += sacc[threadIdx.x + h];
+      sbad[threadIdx.x] += sbad[threadIdx.x + h];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x != 0) return;
+  const float scale = st->scale;
+  const float inv = __double2float_rn(__ddiv_rn(1.0, (double)scale));
+  if (sbad[0] > 0.0) {
+    st_global(&st->found_inf, 1);
+    st_global(&st->grad_norm, __builtin_nanf(""));
+    st_global(&st->clip_coef, 1.0f);
+    st_global(&st->grad_factor, 0.0f);
+    st_global(&st->scale, __fmul_rn(scale, cfg.backoff_factor));
+    st_global(&st->growth_tracker, 0);
+    st_global(&ctl->skip, 1);
+    return;
+  }
+  const double norm = __dmul_rn(__dsqrt_rn(sacc[0]), (double)inv);
+  double cc = 1.0;
+  if (cfg.max_norm > 0.0f) {
+    cc = __ddiv_rn((double)cfg.max_norm, __dadd_rn(norm, 1e-6));
+    if (cc > 1.0) cc = 1.0;
+  }
+  const float c32 = __double2float_rn(cc);
+  const float gfac = __fmul_rn(c32, inv);
+  const int64_t t = st->step + 1;
+  st_global(&st->found_inf, 0);
+  st_global(&st->grad_norm, __double2float_rn(norm));
+  st_global(&st->clip_coef, c32);
+  st_global(&st->grad_factor, gfac);
+  st_global(&st->step, t);
+  const int32_t next = st->growth_tracker + 1;
+  if (next == cfg.growth_interval) {
+    const float grown = __fmul_rn(scale, cfg.growth_factor);
+    if (isfinite(grown)) st_global(&st->scale, grown);
+    st_global(&st->growth_tracker, 0);
+  } else {
+    st_global(&st->growth_tracker, next);
+  }
+  const double bc1 = 1.0 - pow((double)beta1, (double)t), bc2 = 1.0 - pow((double)beta2, (double)t);
+  const double bc1p = 1.0 - pow((double)beta1, (double)(t - 1)), bc2p = 1.0 - pow((double)beta2, (double)(t - 1));
+  st_global(&ctl->skip, 0);
+  st_global(&ctl->gfac, gfac);
+  st_global(&ctl->step_size, (float)((double)lr / bc1));
+  st_global(&ctl->inv_bc2, (float)(1.0 / bc2));
+  st_global(&ctl->grow_m, bc1p > 0.0 ? (float)(bc1 / bc1p) : 1.0f);
+  st_global(&ctl->grow_v, bc2p > 0.0 ? (float)(bc2 / bc2p) : 1.0f);
+  st_global(&ctl->hist_slot, hist_len > 0 ? (int32_t)((t - 1) % hist_len) : 0);
 }
 
 // Zero the stats counters (and, in block mode, the amax used for stats).
@@ -823,9 +1017,10 @@ template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
                                                       const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                       unsigned long long* __restrict__ counters,
-                                                      uint32_t* __restrict__ amax, int chunk_log2, int64_t nwork) {
+                                                      uint32_t* __restrict__ amax, int chunk_log2, int64_t nwork,
+                                                      const GradCtl* __restrict__ gctl) {
   const int64_t w = work_index<kXcdStreams>(nwork);
-  if (w < 0) return;
+  if (w < 0 || amp_apply(gctl, c)) return;
   const int split_log2 = chunk_log2 - kPartLog2;
   const int64_t chunk = w >> split_log2;
   const int tid = chunk_tid[chunk];
@@ -870,7 +1065,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
           float a = 0.0f, b = 0.0f, q = 0.0f;
           if (ex[j] && i < end) {
             q = load_p1<BF16P>(d, i);
-            const float g = grad_eff<L2>(c, load_g1(d, i), q);
+            const float g = grad_in<L2>(c, load_g1(d, i), q);
             moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm[j],
                           decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv[j], a, b);
           }
@@ -1034,6 +1229,9 @@ struct fp8adam_ctx {
   float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   unsigned long long* d_counters = nullptr;  // [n][5]
+  double* d_gpart = nullptr;        // loss scaling: [nchunks][2] sum of squares and Inf/NaN count of g
+  GradCtl* d_gctl = nullptr;        // loss scaling: the decision of the step in flight
+  const GradCtl* gctl = nullptr;    // d_gctl during fp8adam_step_amp, else null
   bool timing = false;
   std::vector<hipEvent_t> ev;  // pairs
   std::vector<int> ev_kind;
@@ -1060,6 +1258,8 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_flags) (void)hipFree(c->d_flags);
   if (c->d_old_scale) (void)hipFree(c->d_old_scale);
   if (c->d_counters) (void)hipFree(c->d_counters);
+  if (c->d_gpart) (void)hipFree(c->d_gpart);
+  if (c->d_gctl) (void)hipFree(c->d_gctl);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   delete c;
 }
@@ -1086,52 +1286,52 @@ const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d_desc +
 template <int MF, int VF, bool BF16P, bool L2>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_amax<MF, VF, BF16P && L2, L2>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks);
+                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks, c->gctl);
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
 void launch_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
                      descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
-                     c->d_flags, k.hist_len, k.hist_slot);
+                     c->d_flags, k.hist_len, k.hist_slot, c->gctl);
 }
 
 template <int MF, int VF, int SMODE>
 void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2);
+                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts);
+                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts, c->gctl);
 }
 
 template <int MF, int VF, bool STATS>
 void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
                      descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, k.grow_m, k.grow_v);
+                     c->chunk_log2, k, c->gctl);
 }
 
 template <int MF, int VF, bool STATS>
 void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_fixup<MF, VF, STATS>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
-                     c->d_counters, c->chunk_log2, c->nchunks);
+                     c->d_counters, c->chunk_log2, c->nchunks, c->gctl);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
-                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts);
+                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts, c->gctl);
 }
 
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
 // 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up,
-// 8 delayed pass, 9 delayed commit.
+// 8 delayed pass, 9 delayed commit, 10 gradient-norm pass, 11 loss-scale decision.
 #define TIMED(kind, call)                              \
   do {                                                 \
     int slot_;                                         \
@@ -1196,6 +1396,17 @@ template <int MF, int VF>
 int run_step_f(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   return c->cfg.master == FP8ADAM_MASTER_BF16 ? run_step_b<MF, VF, true>(c, k, t, s)
                                               : run_step_b<MF, VF, false>(c, k, t, s);
+}
+
+void launch_gradnorm(fp8adam_ctx* c, hipStream_t s) {
+  hipLaunchKernelGGL(k_gradnorm, dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
+                     c->d_chunk_tid, c->d_gpart, c->chunk_log2, c->nchunks);
+}
+
+void launch_gradctl(fp8adam_ctx* c, const fp8adam_amp_config& amp, fp8adam_amp_state* state,
+                    const fp8adam_hparams& hp, hipStream_t s) {
+  hipLaunchKernelGGL(k_gradctl, dim3(1), dim3(kReduceThreads), 0, s, c->d_gpart, c->nchunks, state, c->d_gctl, amp,
+                     hp.lr, hp.beta1, hp.beta2, c->hist_len);
 }
 
 int run_step(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
@@ -1333,6 +1544,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 2 * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
+    if (e == hipSuccess) e = hipMalloc(&c->d_gpart, 2 * sizeof(double) * (size_t)std::max<int64_t>(1, nchunks));
+    if (e == hipSuccess) e = hipMalloc(&c->d_gctl, sizeof(GradCtl));
     if (e == hipSuccess)
       e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * 2 * (size_t)n, hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemsetAsync(c->d_flags, 0, sizeof(int32_t) * (size_t)n, stream);
@@ -1357,8 +1570,10 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
   }
 }
 
-int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream) {
-  try {
+namespace {
+
+// Validate the hyperparameters and fill the per-step constants of step hp->step.
+int step_consts(const fp8adam_ctx* ctx, const fp8adam_hparams* hp, StepConsts& k) {
     if (!ctx || !hp) return fail(FP8ADAM_EINVAL, "ctx or hp is null");
     if (hp->step < 1) return fail(FP8ADAM_EINVAL, "step must be >= 1");
     if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
@@ -1367,7 +1582,6 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
     if (!isfinite(hp->lr) || !isfinite(hp->weight_decay)) return fail(FP8ADAM_EINVAL, "lr and weight_decay must be finite");
     const double bc1 = 1.0 - pow((double)hp->beta1, (double)hp->step);
     const double bc2 = 1.0 - pow((double)hp->beta2, (double)hp->step);
-    StepConsts k;
     k.b1 = hp->beta1;
     k.b2 = hp->beta2;
     k.omb1 = 1.0f - hp->beta1;
@@ -1387,9 +1601,45 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
     k.margin_scale = ctx->margin_scale;
     k.hist_len = ctx->hist_len;
     k.hist_slot = ctx->hist_len > 0 ? (int)((hp->step - 1) % ctx->hist_len) : 0;
+    k.gfac = 1.0f;
+    return 0;
+}
+
+}  // namespace
+
+int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream) {
+  try {
+    StepConsts k;
+    if (int r = step_consts(ctx, hp, k)) return r;
     return run_step(ctx, k, hp->step, stream);
   } catch (...) {
     return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step");
+  }
+}
+
+int fp8adam_step_amp(fp8adam_ctx* ctx, const fp8adam_hparams* hp, const fp8adam_amp_config* amp,
+                     fp8adam_amp_state* state, hipStream_t stream) {
+  try {
+    StepConsts k;
+    if (int r = step_consts(ctx, hp, k)) return r;
+    if (!amp || !state) return fail(FP8ADAM_EINVAL, "amp or state is null");
+    if ((uintptr_t)state & 7u) return fail(FP8ADAM_EINVAL, "state must be 8-byte aligned");
+    if (!(amp->growth_factor > 1.0f) || !isfinite(amp->growth_factor) || !(amp->backoff_factor > 0.0f) ||
+        !(amp->backoff_factor < 1.0f) || amp->growth_interval < 1 || !isfinite(amp->max_norm))
+      return fail(FP8ADAM_EINVAL, "growth_factor must exceed 1, backoff_factor lie in (0, 1), "
+                                  "growth_interval be >= 1 and max_norm be finite");
+    fp8adam_ctx* c = ctx;
+    hipStream_t s = stream;
+    if (c->nchunks > 0) TIMED(10, launch_gradnorm(c, s));
+    TIMED(11, (launch_gradctl(c, *amp, state, *hp, s)));
+    HIP_TRY(hipGetLastError());
+    c->gctl = c->d_gctl;
+    const int r = run_step(c, k, hp->step, s);
+    c->gctl = nullptr;
+    return r;
+  } catch (...) {
+    if (ctx) ctx->gctl = nullptr;
+    return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step_amp");
   }
 }
 
