@@ -232,6 +232,7 @@ __device__ __forceinline__ void count_element(uint32_t (&cnt)[kStatsPerTensor], 
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
+typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
 
 // Streamed loads and stores (optionally non-temporal: the data is touched once per pass).
 // The tensor pointers come from a descriptor in memory, so the compiler cannot
@@ -857,44 +858,53 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
 // c / S, c = min(1, max_norm / (||g||/S + 1e-6)), and the bias corrections of
 // the device-side step count, which only a taken step advances.
 
+// Work-groups of the gradient-norm pass: a fixed grid that strides over the
+// chunks, so the decision kernel sums few partials (and always in one order).
+constexpr int kNormGroups = 2048;
+
+__device__ __forceinline__ void sumsq_bf16x2(uint32_t x, double& acc, uint32_t& bad) {
+  bad += ((x & 0x7F80u) == 0x7F80u) + ((x & 0x7F800000u) == 0x7F800000u);
+  const double a = bf16_lo(x), b = bf16_hi(x);
+  acc = __builtin_fma(a, a, acc);
+  acc = __builtin_fma(b, b, acc);
+}
+
 __global__ __launch_bounds__(kThreads) void k_gradnorm(const TensorDesc* __restrict__ descs,
                                                        const int32_t* __restrict__ chunk_tid,
-                                                       double* __restrict__ gpart, int chunk_log2, int64_t nwork) {
-  const int64_t w = work_index<false>(nwork);
-  if (w < 0) return;
-  const TensorDesc d = descs[chunk_tid[w]];
-  const int64_t start = (w - d.chunk0) << chunk_log2;
-  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
-  const int64_t gend = start + ((end - start) & ~(int64_t)3);
+                                                       double* __restrict__ gpart, int chunk_log2, int64_t nchunks) {
+  constexpr int kU = 4;                         // 16-byte loads in flight per lane
+  constexpr int kStep = kThreads * 8;           // elements per load of the work-group
   double acc = 0.0;
   uint32_t bad = 0;
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
-    vu2 gg[kAmaxUnroll];
+  for (int64_t w = blockIdx.x; w < nchunks; w += gridDim.x) {
+    const TensorDesc d = descs[chunk_tid[w]];
+    const int64_t start = (w - d.chunk0) << chunk_log2;
+    const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+    const int64_t gend = start + ((end - start) & ~(int64_t)7);  // whole groups of 8
+    for (int64_t base = start + 8 * threadIdx.x; base < gend; base += (int64_t)kStep * kU) {
+      vu4 gg[kU];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) gg[u] = ld_stream<vu2, FP8ADAM_NT_AMAX != 0>(d.g + i);
-    }
+      for (int u = 0; u < kU; u++) {
+        const int64_t i = base + (int64_t)u * kStep;
+        if (i < gend) gg[u] = ld_stream<vu4, FP8ADAM_NT_AMAX != 0>(d.g + i);
+      }
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        const uint32_t x = gg[u].x, y = gg[u].y;
-        bad += ((x & 0x7F80u) == 0x7F80u) + ((x & 0x7F800000u) == 0x7F800000u) +
-               ((y & 0x7F80u) == 0x7F80u) + ((y & 0x7F800000u) == 0x7F800000u);
-        const double a = bf16_lo(x), b = bf16_hi(x), e = bf16_lo(y), f = bf16_hi(y);
-        acc = __builtin_fma(a, a, acc);
-        acc = __builtin_fma(b, b, acc);
-        acc = __builtin_fma(e, e, acc);
-        acc = __builtin_fma(f, f, acc);
+      for (int u = 0; u < kU; u++) {
+        const int64_t i = base + (int64_t)u * kStep;
+        if (i < gend) {
+          sumsq_bf16x2(gg[u].x, acc, bad);
+          sumsq_bf16x2(gg[u].y, acc, bad);
+          sumsq_bf16x2(gg[u].z, acc, bad);
+          sumsq_bf16x2(gg[u].w, acc, bad);
+        }
       }
     }
-  }
-  if (gend + threadIdx.x < end) {
-    const uint32_t x = ld_global<uint16_t>(d.g + gend + threadIdx.x);
-    bad += (x & 0x7F80u) == 0x7F80u;
-    const double a = bf16_lo(x);
-    acc = __builtin_fma(a, a, acc);
+    if (gend + threadIdx.x < end) {  // ragged tail (< 8 elements at the end of a tensor)
+      const uint32_t x = ld_global<uint16_t>(d.g + gend + threadIdx.x);
+      bad += (x & 0x7F80u) == 0x7F80u;
+      const double a = bf16_lo(x);
+      acc = __builtin_fma(a, a, acc);
+    }
   }
   // fixed-order reduction: butterfly within the wave, then waves in order
 #pragma unroll
@@ -915,17 +925,17 @@ __global__ __launch_bounds__(kThreads) void k_gradnorm(const TensorDesc* __restr
       acc += sacc[k];
       bad += sbad[k];
     }
-    st_global<double>(gpart + 2 * w, acc);
-    st_global<double>(gpart + 2 * w + 1, (double)bad);
+    st_global<double>(gpart + 2 * blockIdx.x, acc);
+    st_global<double>(gpart + 2 * blockIdx.x + 1, (double)bad);
   }
 }
 
-__global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __restrict__ gpart, int64_t nchunks,
+__global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __restrict__ gpart, int64_t nparts,
                                                            fp8adam_amp_state* __restrict__ st, GradCtl* __restrict__ ctl,
                                                            fp8adam_amp_config cfg, float lr, float beta1, float beta2,
                                                            int hist_len) {
   double acc = 0.0, bad = 0.0;
-  for (int64_t k = threadIdx.x; k < nchunks; k += kReduceThreads) {
+  for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
     acc += gpart[2 * k];
     bad += gpart[2 * k + 1];
   }
@@ -1229,7 +1239,7 @@ struct fp8adam_ctx {
   float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   unsigned long long* d_counters = nullptr;  // [n][5]
-  double* d_gpart = nullptr;        // loss scaling: [nchunks][2] sum of squares and Inf/NaN count of g
+  double* d_gpart = nullptr;        // loss scaling: [norm groups][2] sum of squares and Inf/NaN count of g
   GradCtl* d_gctl = nullptr;        // loss scaling: the decision of the step in flight
   const GradCtl* gctl = nullptr;    // d_gctl during fp8adam_step_amp, else null
   bool timing = false;
@@ -1398,14 +1408,16 @@ int run_step_f(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
                                               : run_step_b<MF, VF, false>(c, k, t, s);
 }
 
+int64_t norm_groups(const fp8adam_ctx* c) { return std::min<int64_t>(c->nchunks, kNormGroups); }
+
 void launch_gradnorm(fp8adam_ctx* c, hipStream_t s) {
-  hipLaunchKernelGGL(k_gradnorm, dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
+  hipLaunchKernelGGL(k_gradnorm, dim3((unsigned)norm_groups(c)), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      c->d_chunk_tid, c->d_gpart, c->chunk_log2, c->nchunks);
 }
 
 void launch_gradctl(fp8adam_ctx* c, const fp8adam_amp_config& amp, fp8adam_amp_state* state,
                     const fp8adam_hparams& hp, hipStream_t s) {
-  hipLaunchKernelGGL(k_gradctl, dim3(1), dim3(kReduceThreads), 0, s, c->d_gpart, c->nchunks, state, c->d_gctl, amp,
+  hipLaunchKernelGGL(k_gradctl, dim3(1), dim3(kReduceThreads), 0, s, c->d_gpart, norm_groups(c), state, c->d_gctl, amp,
                      hp.lr, hp.beta1, hp.beta2, c->hist_len);
 }
 
@@ -1544,7 +1556,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 2 * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
-    if (e == hipSuccess) e = hipMalloc(&c->d_gpart, 2 * sizeof(double) * (size_t)std::max<int64_t>(1, nchunks));
+    if (e == hipSuccess)
+      e = hipMalloc(&c->d_gpart, 2 * sizeof(double) * (size_t)std::max<int64_t>(1, std::min<int64_t>(nchunks, kNormGroups)));
     if (e == hipSuccess) e = hipMalloc(&c->d_gctl, sizeof(GradCtl));
     if (e == hipSuccess)
       e = hipMemcpyAsync(c->d_desc, desc.data(), sizeof(TensorDesc) * 2 * (size_t)n, hipMemcpyHostToDevice, stream);
