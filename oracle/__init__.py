@@ -50,6 +50,7 @@ class Config(ctypes.Structure):
         ("l2_coupled", ctypes.c_int),
         ("history_len", ctypes.c_int), ("margin", ctypes.c_int), ("delayed_from", ctypes.c_int64),
         ("grad_factor", ctypes.c_float), ("sched_step", ctypes.c_int64),
+        ("stochastic", ctypes.c_int), ("tensor_index", ctypes.c_uint32), ("seed", ctypes.c_uint64),
     ]
 
 
@@ -115,6 +116,11 @@ def lib() -> ctypes.CDLL:
                                             f32p, f32p]
         L.ref_step_fp32_moments.restype = ctypes.c_int
         L.ref_rounding_is_nearest.restype = ctypes.c_int
+        L.ref_encode_sr.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_uint32]
+        L.ref_encode_sr.restype = ctypes.c_uint8
+        L.ref_philox4x32_10.argtypes = [P, P, P]
+        L.ref_sr_word.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64]
+        L.ref_sr_word.restype = ctypes.c_uint32
         L.ref_grad_sumsq.argtypes = [u16p, ctypes.c_int64, P, ctypes.POINTER(ctypes.c_int64)]
         L.ref_sumsq_total.argtypes = [P]
         L.ref_sumsq_total.restype = ctypes.c_double
@@ -182,13 +188,13 @@ class Hyper:
 def make_config(h: Hyper, m_fmt=E4M3, v_fmt=E5M2, block: int = 0,
                 scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False,
                 history_len: int = 0, margin: int = 0, delayed_from: int = 2, grad_factor: float = 1.0,
-                sched_step: int = 0) -> Config:
+                sched_step: int = 0, stochastic: bool = False, tensor_index: int = 0, seed: int = 0) -> Config:
     """history_len > 0 selects delayed scaling (per-tensor scales only); grad_factor
     multiplies every gradient first; sched_step (0: h.step) is the step number
     compared with delayed_from."""
     return Config(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step,
                   fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled),
-                  history_len, margin, delayed_from, grad_factor, sched_step)
+                  history_len, margin, delayed_from, grad_factor, sched_step, int(stochastic), tensor_index, seed)
 
 
 def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,
@@ -262,3 +268,20 @@ def amp_control(sums: GradSums, cfg: AmpConfig, state: AmpState) -> AmpState:
     """One loss-scaler / clipping decision over the whole list; updates state in place."""
     lib().ref_amp_control(_ptr(sums.acc), sums.nonfinite.value, ctypes.byref(cfg), ctypes.byref(state))
     return state
+
+
+def encode_sr(fmt, x: float, r16: int) -> int:
+    """Stochastic rounding of one value with 16 random bits."""
+    return lib().ref_encode_sr(fmt_id(fmt), x, r16)
+
+
+def philox4x32_10(ctr, key) -> list:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().ref_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return [int(x) for x in out]
+
+
+def sr_word(seed: int, tensor: int, t: int, i: int) -> int:
+    return lib().ref_sr_word(seed, tensor, t, i)

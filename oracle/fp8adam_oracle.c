@@ -55,6 +55,9 @@
  *    example's delayed-scaling recipe: history of 16, margin 0, interval 1,
  *    MAX of the history.]  Steps t < delayed_from are just in time, so the
  *    first step has a history to start from.
+ *  - Stochastic rounding (stochastic = 1): each moment code rounds up or down
+ *    with probability given by the distance to its two FP8 neighbours, using
+ *    16 bits of a Philox4x32-10 word per element and moment (ref_encode_sr).
  *  - Coupled-L2 variant (l2_coupled): the L2 term of an L2-regularised loss
  *    enters the gradient instead, g_eff = fma(wd, p, g) in fp32 with the old
  *    p, and there is no decoupled decay.  [P1] "Why the SwiGLU weights align",
@@ -177,6 +180,65 @@ void ref_encode_bits_range(int fmt, uint32_t start, int64_t count, uint8_t *out)
     for (int64_t i = 0; i < count; i++) out[i] = ref_encode(fmt, u2f(start + (uint32_t)i));
 }
 
+/* -------------------------------------------------------- stochastic rounding */
+
+/* [P3 "Strategies": stochastic rounding, to cut the rounding error that
+ * accumulates over many updates]  Round x to one of its two FP8 neighbours
+ * lo <= |x| < hi, up with probability equal to its distance from lo, resolved
+ * with 16 random bits: with f = (|x| - lo) / (hi - lo) in [0, 1), round up iff
+ * floor(f * 2^16) + r16 >= 2^16.  Values at or beyond FMAX saturate as in
+ * round-to-nearest; zeros, NaN and exact FP8 values are unchanged. */
+uint8_t ref_encode_sr(int fmt, float x, uint32_t r16)
+{
+    const ref_format *F = &REF_FORMATS[fmt];
+    double a = fabs((double)x);
+    if (isnan(x) || a == 0.0 || a >= (double)ref_format_max(fmt)) return ref_encode(fmt, x);
+    int e;
+    (void)frexp(a, &e);                    /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    int emin = 1 - F->bias;                /* exponent of the smallest normal */
+    if (ex < emin) ex = emin;              /* subnormal range: one fixed spacing */
+    double spacing = ldexp(1.0, ex - F->mbits);
+    double units = a / spacing;            /* exact: division by a power of two */
+    double lo = floor(units);
+    uint32_t d = (uint32_t)floor((units - lo) * 65536.0);
+    double mag = (d + (r16 & 0xFFFFu) >= 65536u ? lo + 1.0 : lo) * spacing;
+    return ref_encode(fmt, (float)copysign(mag, (double)x)); /* an FP8 value: exact */
+}
+
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+ * as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplies with the
+ * round constants below, the key bumped by the Weyl constants between rounds. */
+void ref_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; r++) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The random word of element i of tensor `tensor` at step t: word i mod 4 of
+ * Philox4x32-10 with counter (i/4 low, i/4 high, t, tensor) and the 64-bit
+ * seed as key.  The first moment takes its low 16 bits, the second its high
+ * 16 bits. */
+uint32_t ref_sr_word(uint64_t seed, uint32_t tensor, int64_t t, int64_t i)
+{
+    uint64_t grp = (uint64_t)i >> 2;
+    uint32_t ctr[4] = {(uint32_t)grp, (uint32_t)(grp >> 32), (uint32_t)t, tensor};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    ref_philox4x32_10(ctr, key, out);
+    return out[i & 3];
+}
+
 /* --------------------------------------------------------------- bf16 helpers */
 
 static float bf16_to_f32(uint16_t b) { return u2f((uint32_t)b << 16); }
@@ -243,6 +305,9 @@ typedef struct {
     float grad_factor;    /* every bf16 gradient is multiplied by this first (1: none; loss-scale
                              unscaling and norm clipping otherwise) */
     int64_t sched_step;   /* the step number compared with delayed_from (0: step) */
+    int stochastic;       /* 0: round to nearest even; 1: stochastic rounding of both moments */
+    uint32_t tensor_index;/* stochastic: the tensor's position in its list (part of the counter) */
+    uint64_t seed;        /* stochastic: the generator's key */
 } ref_config;
 
 typedef struct {
@@ -386,8 +451,14 @@ int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
         /* 3. requantize the moments and update the parameters */
         for (int64_t i = lo; i < hi; i++) {
             float qm = m1[i] * nism, qv = v1[i] * nisv;
-            cm[i] = ref_encode(c->m_fmt, qm);
-            cv[i] = ref_encode(c->v_fmt, qv);
+            if (c->stochastic) {
+                uint32_t r = ref_sr_word(c->seed, c->tensor_index, c->step, i);
+                cm[i] = ref_encode_sr(c->m_fmt, qm, r & 0xFFFFu);
+                cv[i] = ref_encode_sr(c->v_fmt, qv, r >> 16);
+            } else {
+                cm[i] = ref_encode(c->m_fmt, qm);
+                cv[i] = ref_encode(c->v_fmt, qv);
+            }
             if (m1[i] != 0.0f && (cm[i] & 0x7F) == 0) s.underflow_m++;
             if (v1[i] != 0.0f && (cv[i] & 0x7F) == 0) s.underflow_v++;
             if (fabsf(qm) > fmax_m) s.saturated_m++;

@@ -126,6 +126,23 @@ def quantize(fmt: int, x: float) -> int:
     return sign | best
 
 
+def quantize_sr(fmt: int, x: float, r16: int) -> int:
+    """Stochastic rounding by table search: the FP8 neighbours lo <= |x| < hi,
+    f = (|x| - lo) / (hi - lo) exactly, up iff floor(f * 2^16) + r16 >= 2^16.
+    Saturation, zeros and exact values as in quantize()."""
+    tab = _TABLES[fmt]
+    a = abs(x)
+    top = max(c for c in range(128) if math.isfinite(tab[c]))
+    if a == 0 or a >= tab[top]:
+        return quantize(fmt, x)
+    sign = 0x80 if _sign(x) < 0 else 0
+    lo_c = max(c for c in range(top + 1) if tab[c] <= a)
+    lo, hi = Fraction(tab[lo_c]), Fraction(tab[lo_c + 1])
+    f = (Fraction(a) - lo) / (hi - lo)
+    d = math.floor(f * 65536)
+    return sign | (lo_c + 1 if d + r16 >= 65536 else lo_c)
+
+
 def dequant(fmt: int, code: int) -> float:
     return _TABLES[fmt][code]
 
@@ -171,11 +188,13 @@ def param_update(p: float, m1: float, v1: float, lr: float, b1: float, b2: float
 def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[float],
          sv: list[float], *, lr: float, b1: float, b2: float, eps: float, wd: float, t: int,
          m_fmt: int = 0, v_fmt: int = 1, block: int = 0, amax_mode: bool = False,
-         master_bf16: bool = False, l2_coupled: bool = False, scale_amax=None, return_amax: bool = False):
+         master_bf16: bool = False, l2_coupled: bool = False, scale_amax=None, return_amax: bool = False,
+         sr_words=None):
     """Returns new (p, cm, cv, sm, sv), plus the per-block (amax m', amax v')
     list with return_amax. All floats are values already exact in their storage
     type (fp32, or bf16 for g and a bf16 master).  scale_amax: (am, av) to
-    choose a per-tensor step's scales from."""
+    choose a per-tensor step's scales from.  sr_words: one random 32-bit word
+    per element for stochastic rounding (m takes the low 16 bits, v the high)."""
     assert scale_amax is None or block == 0
     n = len(p)
     blen = block if block > 0 else max(n, 1)
@@ -205,8 +224,12 @@ def step(p: list[float], g: list[float], cm: list[int], cv: list[int], sm: list[
         nsm, nism = choose(m_fmt, am)
         nsv, nisv = choose(v_fmt, av)
         for j, i in enumerate(range(lo, hi)):
-            cm2[i] = quantize(m_fmt, mul32(m1s[j], nism))
-            cv2[i] = quantize(v_fmt, mul32(v1s[j], nisv))
+            if sr_words is not None:
+                cm2[i] = quantize_sr(m_fmt, mul32(m1s[j], nism), sr_words[i] & 0xFFFF)
+                cv2[i] = quantize_sr(v_fmt, mul32(v1s[j], nisv), sr_words[i] >> 16)
+            else:
+                cm2[i] = quantize(m_fmt, mul32(m1s[j], nism))
+                cv2[i] = quantize(v_fmt, mul32(v1s[j], nisv))
             exact = param_update(p[i], m1s[j], v1s[j], lr, b1, b2, eps, 0.0 if l2_coupled else wd, t)
             p2[i] = round_bf16(exact) if master_bf16 else round_f32(exact)
         sm2[si], sv2[si] = nsm, nsv
