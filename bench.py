@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
     ap.add_argument("--scaling", default="just_in_time", choices=["just_in_time", "delayed"],
                     help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")
+    ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
+                    help="stochastic: moments rounded with a Philox4x32-10 stream (seed 1234)")
     ap.add_argument("--amp", action="store_true",
                     help="loss-scaled gradients (scale 2^16) through the fused unscale / Inf-NaN skip / "
                          "global-norm clip (max_norm 1.0) step")
@@ -153,7 +155,8 @@ def main():
     schedule = args.schedule if (w.granularity == "tensor" and w.decay_mode == "decoupled"
                                  and scaling == "just_in_time") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
-                      schedule=schedule, decay_mode=w.decay_mode, scaling=scaling)
+                      schedule=schedule, decay_mode=w.decay_mode, scaling=scaling, rounding=args.rounding,
+                      seed=1234)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
@@ -258,6 +261,7 @@ def main():
                    "weight_decay": w.weight_decay, "decay_mode": w.decay_mode, "schedule": schedule,
                    "scaling": scaling if scaling == "just_in_time" else "delayed (amax history 16, margin 0)",
                    "loss_scaling": "scale 2^16, Inf/NaN skip, clip to global norm 1.0" if args.amp else None,
+                   "rounding": args.rounding,
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,

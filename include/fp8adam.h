@@ -92,6 +92,16 @@ typedef enum { FP8ADAM_DECAY_DECOUPLED = 0, FP8ADAM_DECAY_L2 = 1 } fp8adam_decay
  *   Steps with t < delayed_from_step are just in time (two passes) and also record their amax,
  *   so the history is seeded.  Needs per-tensor scales and the TWO_PASS schedule value. */
 typedef enum { FP8ADAM_SCALING_JUST_IN_TIME = 0, FP8ADAM_SCALING_DELAYED = 1 } fp8adam_scaling;
+/* How the moments are rounded to FP8.
+ * NEAREST: round to nearest, ties to even (the zyxy.net article's strategies: the standard).
+ * STOCHASTIC: stochastic rounding (same section: against the error that accumulates over many
+ *   updates).  A moment value x with FP8 neighbours lo <= |x| < hi and f = (|x| - lo)/(hi - lo)
+ *   rounds up iff floor(f * 2^16) + r >= 2^16, r = 16 random bits; saturation as for NEAREST.
+ *   The bits come from Philox4x32-10 (Salmon et al., SC 2011) with key = seed and counter
+ *   (i/4 low 32 bits, i/4 high 32 bits, t, tensor index) for element i of a tensor: word i mod 4,
+ *   low 16 bits for m, high 16 bits for v.  Deterministic for a given seed and t; every
+ *   schedule gives the same codes. */
+typedef enum { FP8ADAM_ROUND_NEAREST = 0, FP8ADAM_ROUND_STOCHASTIC = 1 } fp8adam_rounding;
 
 typedef struct {
     int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
@@ -107,6 +117,8 @@ typedef struct {
     int32_t amax_history_len;  /* DELAYED: H in [1, 1024]; <= 0 means 16 */
     int32_t margin;            /* DELAYED: scale chosen for max(history) * 2^margin, margin in [0, 64] */
     int32_t delayed_from_step; /* DELAYED: first t quantized with the delayed scale; <= 0 means 2 */
+    int32_t rounding;          /* fp8adam_rounding */
+    uint64_t seed;             /* STOCHASTIC: the generator's key */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,

@@ -31,6 +31,8 @@ _SCHED = {"two_pass": SCHEDULE_TWO_PASS, "speculative": SCHEDULE_SPECULATIVE}
 DECAY_DECOUPLED, DECAY_L2 = 0, 1
 _DECAY = {"decoupled": DECAY_DECOUPLED, "l2": DECAY_L2}
 SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
+ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
+_ROUNDING = {"nearest": ROUND_NEAREST, "stochastic": ROUND_STOCHASTIC}
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
@@ -63,7 +65,8 @@ class ConfigArg(ctypes.Structure):
                 ("schedule", ctypes.c_int32), ("speculate_from_step", ctypes.c_int32),
                 ("decay_mode", ctypes.c_int32), ("scaling", ctypes.c_int32),
                 ("amax_history_len", ctypes.c_int32), ("margin", ctypes.c_int32),
-                ("delayed_from_step", ctypes.c_int32)]
+                ("delayed_from_step", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -252,7 +255,8 @@ class FP8AdamW:
     ``scaling="delayed"`` quantizes with the scale of the largest amax over the
     last ``amax_history_len`` steps (times 2^margin) in one pass; each tensor
     then carries a float32 history of 2 * amax_history_len entries
-    (``amax_history``; a fifth ``state`` list supplies it).
+    (``amax_history``; a fifth ``state`` list supplies it).  ``rounding="stochastic"``
+    rounds the moments stochastically with a Philox4x32-10 stream keyed by ``seed``.
     Every tensor must be
     contiguous and 16-byte aligned on the same device, and must stay alive with
     the same storage while this object exists.
@@ -261,7 +265,7 @@ class FP8AdamW:
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
                  speculate_from_step=0, decay_mode="decoupled", scaling="just_in_time",
-                 amax_history_len=16, margin=0, delayed_from_step=0):
+                 amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
@@ -302,7 +306,8 @@ class FP8AdamW:
         self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
                              _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode],
-                             _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step))
+                             _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step),
+                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF)
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):

@@ -15,13 +15,18 @@ namespace fp8adam {
 
 // FMAX = 0.875 * 2^kMaxExp for both formats: 448 = 0.875 * 2^9, 57344 = 0.875 * 2^16.
 template <int FMT> struct Format;
+// kMinNormalField: the fp32 exponent field of the smallest normal (2^-6, 2^-14).
 template <> struct Format<0> {  // E4M3
   static constexpr float kMax = 448.0f;
   static constexpr int kMaxExp = 9;
+  static constexpr int kMantBits = 3;
+  static constexpr int kMinNormalField = 127 - 6;
 };
 template <> struct Format<1> {  // E5M2
   static constexpr float kMax = 57344.0f;
   static constexpr int kMaxExp = 16;
+  static constexpr int kMantBits = 2;
+  static constexpr int kMinNormalField = 127 - 14;
 };
 
 // Four codes packed little-endian in a dword -> four floats (exact).
@@ -66,6 +71,63 @@ __device__ __forceinline__ uint32_t encode4(float a, float b, float c, float d) 
 template <int FMT>
 __device__ __forceinline__ uint32_t encode1(float a) {
   return encode4<FMT>(a, 0.0f, 0.0f, 0.0f) & 0xFFu;
+}
+
+// Stochastic rounding (the zyxy.net article's strategies section: stochastic
+// rounding against the error that accumulates over many updates).  q is
+// already clamped to [-FMAX, FMAX].  Its FP8 neighbours are lo and lo + s,
+// s = the FP8 spacing at |q| (fixed below the smallest normal); with
+// f = (|q| - lo) / s, q rounds up iff floor(f * 2^16) + r16 >= 2^16.  Every
+// step is exact in fp32 (scaling by powers of two, truncation, the fraction
+// of a value with at most 24 significant bits), so the result is an FP8 value
+// and the round-to-nearest convert that follows leaves it unchanged.
+template <int FMT>
+__device__ __forceinline__ float sr_round(float q, uint32_t r16) {
+  const float a = fabsf(q);
+  const int ef = (int)(__float_as_uint(a) >> 23);
+  const int ex = ef > Format<FMT>::kMinNormalField ? ef : Format<FMT>::kMinNormalField;
+  const float spacing = __uint_as_float((uint32_t)(ex - Format<FMT>::kMantBits) << 23);
+  const float inv_spacing = __uint_as_float((uint32_t)(254 - (ex - Format<FMT>::kMantBits)) << 23);
+  const float units = a * inv_spacing;
+  const float lo = __builtin_truncf(units);
+  const uint32_t d = (uint32_t)((units - lo) * 65536.0f);
+  const float mag = (d + r16 >= 65536u ? lo + 1.0f : lo) * spacing;
+  return __builtin_copysignf(mag, q);
+}
+
+// Four floats -> four codes with stochastic rounding; r16[j] are 16 random bits each.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4_sr(float a, float b, float c, float d, const uint32_t (&r16)[4]) {
+  constexpr float M = Format<FMT>::kMax;
+  a = sr_round<FMT>(__builtin_amdgcn_fmed3f(a, -M, M), r16[0]);
+  b = sr_round<FMT>(__builtin_amdgcn_fmed3f(b, -M, M), r16[1]);
+  c = sr_round<FMT>(__builtin_amdgcn_fmed3f(c, -M, M), r16[2]);
+  d = sr_round<FMT>(__builtin_amdgcn_fmed3f(d, -M, M), r16[3]);
+  return encode4<FMT>(a, b, c, d);
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32x32->64-bit multiplies; the key
+// is bumped by the two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
 }
 
 // bf16 <-> fp32.  Widening is exact (shift); narrowing rounds to nearest even.
@@ -128,6 +190,8 @@ struct StepConsts {
   float eps;
   float grow_m, grow_v; // speculative schedule: expected amax growth (1-beta^t)/(1-beta^(t-1))
   float gfac;          // factor applied to every bf16 gradient first (1; loss-scale unscaling and clipping)
+  uint32_t seed_lo, seed_hi;  // stochastic rounding: the generator's key
+  uint32_t rng_t;      // stochastic rounding: the step t in the generator's counter
   float margin_scale;  // delayed scaling: 2^margin
   int hist_len;        // delayed scaling: H (0: no history)
   int hist_slot;       // delayed scaling: (t-1) mod H, the slot this step's amax goes to

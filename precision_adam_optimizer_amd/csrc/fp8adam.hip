@@ -128,6 +128,7 @@ struct GradCtl {
   float gfac;
   float step_size, inv_bc2, grow_m, grow_v;
   int32_t hist_slot;  // delayed scaling: (t-1) mod H of the device-side t
+  uint32_t t;         // the device-side t (stochastic rounding's counter)
 };
 
 // With loss scaling, take the step's gradient factor and bias corrections;
@@ -141,7 +142,49 @@ __device__ __forceinline__ bool amp_apply(const GradCtl* gctl, StepConsts& c) {
   c.grow_m = gctl->grow_m;
   c.grow_v = gctl->grow_v;
   c.hist_slot = gctl->hist_slot;
+  c.rng_t = gctl->t;
   return false;
+}
+
+// Random words of the group of 4 elements starting at element i of tensor
+// tid: Philox4x32-10 with counter (i/4, t, tid) and the seed as key.  Word j
+// belongs to element i + j; the first moment uses its low 16 bits, the second
+// its high 16 bits.
+template <bool SR>
+__device__ __forceinline__ void sr_words(const StepConsts& c, int tid, int64_t i, uint32_t (&rw)[4]) {
+  if constexpr (SR) {
+    const uint64_t grp = (uint64_t)i >> 2;
+    philox4x32_10((uint32_t)grp, (uint32_t)(grp >> 32), c.rng_t, (uint32_t)tid, c.seed_lo, c.seed_hi, rw);
+  } else {
+    rw[0] = rw[1] = rw[2] = rw[3] = 0u;
+  }
+}
+
+// Quantize four values: round to nearest even, or stochastically with 16
+// bits of each word (low half for m, high half for v).
+template <int FMT, bool SR, bool HIGH>
+__device__ __forceinline__ uint32_t quant4(const float (&q)[4], const uint32_t (&rw)[4]) {
+  if constexpr (SR) {
+    const uint32_t r[4] = {HIGH ? rw[0] >> 16 : rw[0] & 0xFFFFu, HIGH ? rw[1] >> 16 : rw[1] & 0xFFFFu,
+                           HIGH ? rw[2] >> 16 : rw[2] & 0xFFFFu, HIGH ? rw[3] >> 16 : rw[3] & 0xFFFFu};
+    return encode4_sr<FMT>(q[0], q[1], q[2], q[3], r);
+  } else {
+    return encode4<FMT>(q[0], q[1], q[2], q[3]);
+  }
+}
+
+// One value, element i of tensor tid (the ragged tails).
+template <int FMT, bool SR, bool HIGH>
+__device__ __forceinline__ uint32_t quant1(const StepConsts& c, int tid, int64_t i, float q) {
+  if constexpr (SR) {
+    uint32_t rw[4];
+    sr_words<true>(c, tid, i & ~(int64_t)3, rw);
+    const uint32_t w = rw[i & 3];
+    const uint32_t r[4] = {HIGH ? w >> 16 : w & 0xFFFFu, 0u, 0u, 0u};
+    return encode4_sr<FMT>(q, 0.0f, 0.0f, 0.0f, r) & 0xFFu;
+  } else {
+    return encode1<FMT>(q);
+  }
 }
 
 enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
@@ -492,7 +535,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
 
 // ------------------------------------------------------------------ pass 2
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
 __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
                                                      const TensorDesc* __restrict__ dst_descs,
                                                      const int32_t* __restrict__ chunk_tid,
@@ -576,8 +619,10 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
             av = max(av, abs_bits(v1[j]));
           }
         }
-        const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
-        const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
+        uint32_t rw[4];
+        sr_words<SR>(c, tid, i, rw);
+        const uint32_t wm = quant4<MF, SR, false>(qm, rw);
+        const uint32_t wv = quant4<VF, SR, true>(qv, rw);
         if constexpr (STATS) {
 #pragma unroll
           for (int j = 0; j < 4; j++)
@@ -597,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     const float p = param_update(c, p0, m1, v1);
     const float qm = m1 * ism, qv = v1 * isv;
-    const uint32_t cm = encode1<MF>(qm), cv = encode1<VF>(qv);
+    const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm), cv = quant1<VF, SR, true>(c, tid, i, qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
     if constexpr (PARTS) {
       am = max(am, abs_bits(m1));
@@ -753,8 +798,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
 // the source buffer and requantize them with the true scales into the
 // destination buffer.  p is not touched: its update does not depend on the
 // scales.  Flag bit 0: m, bit 1: v.
-template <int FMT, bool STATS, bool IS_V>
-__device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDesc& d, uint8_t* dst,
+template <int FMT, bool STATS, bool IS_V, bool SR>
+__device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const TensorDesc& d, uint8_t* dst,
                                              int64_t start, int64_t end, float s_old, float inv_new,
                                              uint32_t& under, uint32_t& sat) {
   const uint8_t* src = IS_V ? d.v : d.m;
@@ -785,7 +830,9 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
           x[j] = IS_V ? v1 : m1;
           q[j] = x[j] * inv_new;
         }
-        const uint32_t w = encode4<FMT>(q[0], q[1], q[2], q[3]);
+        uint32_t rw[4];
+        sr_words<SR>(c, tid, i, rw);
+        const uint32_t w = quant4<FMT, SR, IS_V>(q, rw);
         if constexpr (STATS) {
 #pragma unroll
           for (int j = 0; j < 4; j++) {
@@ -805,7 +852,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
     moment_update(c, g, x0, x0, m1, v1);
     const float x = IS_V ? v1 : m1;
     const float q = x * inv_new;
-    const uint32_t code = encode1<FMT>(q);
+    const uint32_t code = quant1<FMT, SR, IS_V>(c, tid, i, q);
     if constexpr (STATS) {
       under += (x != 0.0f && (code & 0x7Fu) == 0u);
       sat += (fabsf(q) > Format<FMT>::kMax);
@@ -814,7 +861,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, const TensorDe
   }
 }
 
-template <int MF, int VF, bool STATS>
+template <int MF, int VF, bool STATS, bool SR>
 __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict__ descs,
                                                     const TensorDesc* __restrict__ dst_descs,
                                                     const int32_t* __restrict__ chunk_tid,
@@ -835,13 +882,13 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
   if (f & 1) {
     float s, inv;
     choose_scale<MF, 0>(amax[2 * tid], s, inv);
-    fixup_moment<MF, STATS, false>(c, d, dst_descs[tid].m, start, end, old_scale[2 * tid], inv, cnt[kUnderM],
+    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[2 * tid], inv, cnt[kUnderM],
                                    cnt[kSatM]);
   }
   if (f & 2) {
     float s, inv;
     choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
-    fixup_moment<VF, STATS, true>(c, d, dst_descs[tid].v, start, end, old_scale[2 * tid + 1], inv, cnt[kUnderV],
+    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[2 * tid + 1], inv, cnt[kUnderV],
                                   cnt[kSatV]);
   }
   flush_counters<STATS>(counters, tid, cnt);
@@ -994,6 +1041,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __rest
   st_global(&ctl->grow_m, bc1p > 0.0 ? (float)(bc1 / bc1p) : 1.0f);
   st_global(&ctl->grow_v, bc2p > 0.0 ? (float)(bc2 / bc2p) : 1.0f);
   st_global(&ctl->hist_slot, hist_len > 0 ? (int32_t)((t - 1) % hist_len) : 0);
+  st_global(&ctl->t, (uint32_t)t);
 }
 
 // Zero the stats counters (and, in block mode, the amax used for stats).
@@ -1023,7 +1071,7 @@ __device__ __forceinline__ uint32_t group32_max(uint32_t x) {
   return x;
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
 __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
                                                       const int32_t* __restrict__ chunk_tid, StepConsts c,
                                                       unsigned long long* __restrict__ counters,
@@ -1111,8 +1159,10 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
         qv[r] = v1[r] * isv;
       }
       if (full[j]) {
-        const uint32_t wm = encode4<MF>(qm[0], qm[1], qm[2], qm[3]);
-        const uint32_t wv = encode4<VF>(qv[0], qv[1], qv[2], qv[3]);
+        uint32_t rw[4];
+        sr_words<SR>(c, tid, i0, rw);
+        const uint32_t wm = quant4<MF, SR, false>(qm, rw);
+        const uint32_t wv = quant4<VF, SR, true>(qv, rw);
         if constexpr (STATS) {
 #pragma unroll
           for (int r = 0; r < 4; r++)
@@ -1126,7 +1176,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
         for (int r = 0; r < 4; r++) {
           const int64_t i = i0 + r;
           if (i < end) {
-            const uint32_t cm = encode1<MF>(qm[r]), cv = encode1<VF>(qv[r]);
+            const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm[r]), cv = quant1<VF, SR, true>(c, tid, i, qv[r]);
             count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], cm, cv);
             store_p1<BF16P>(d, i, p[r]);
             st_global<uint8_t>(d.m + i, (uint8_t)cm);
@@ -1312,9 +1362,9 @@ void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
                      descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts, c->gctl);
 }
@@ -1326,16 +1376,16 @@ void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
                      c->chunk_log2, k, c->gctl);
 }
 
-template <int MF, int VF, bool STATS>
+template <int MF, int VF, bool STATS, bool SR>
 void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_fixup<MF, VF, STATS>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
+  hipLaunchKernelGGL((k_fixup<MF, VF, STATS, SR>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
                      descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
                      c->d_counters, c->chunk_log2, c->nchunks, c->gctl);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
                      descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts, c->gctl);
 }
 
@@ -1355,39 +1405,52 @@ void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
                      dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
 }
 
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
 int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  bool done = false;
   if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
     if (STATS) TIMED(4, launch_reset(c, 4 * (int64_t)c->n, s));
-    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE, L2>(c, k, s)));
-  } else if (!L2 && SMODE == 0 && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
-    // (fp8adam_init refuses the speculative schedule with coupled L2: the fix-up
-    // recomputes moments after p has been overwritten, and g_eff needs the old p)
+    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE, L2, SR>(c, k, s)));
+    done = true;
+  }
+  // (fp8adam_init refuses the speculative schedule with coupled L2 or AMAX scales:
+  // the fix-up recomputes moments after p has been overwritten, and g_eff needs the old p)
+  if constexpr (!L2 && SMODE == 0) {
+    if (!done && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
+      if (STATS) TIMED(4, launch_reset(c, 0, s));
+      if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
+      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
+      if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
+      c->cur = 1 - c->cur;
+      done = true;
+    }
+  }
+  if (!done && c->hist_len > 0 && t >= c->delayed_from) {
     if (STATS) TIMED(4, launch_reset(c, 0, s));
-    if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false>(c, k, s)));
-    TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
-    if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS>(c, k, s)));
-    c->cur = 1 - c->cur;
-  } else if (c->hist_len > 0 && t >= c->delayed_from) {
-    if (STATS) TIMED(4, launch_reset(c, 0, s));
-    if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2>(c, k, s)));
+    if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2, SR>(c, k, s)));
     TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, s)));
-  } else {
+  } else if (!done) {
     if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
     TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, k, s)));
-    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeJit, L2>(c, k, s)));
+    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeJit, L2, SR>(c, k, s)));
   }
   HIP_TRY(hipGetLastError());
   return 0;
+}
+
+template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
+int run_step_r(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
+  return c->cfg.rounding == FP8ADAM_ROUND_STOCHASTIC ? run_step_t<MF, VF, BF16P, STATS, SMODE, L2, true>(c, k, t, s)
+                                                     : run_step_t<MF, VF, BF16P, STATS, SMODE, L2, false>(c, k, t, s);
 }
 
 // Coupled L2 with weight_decay 0 is plain Adam: it runs the kernels without
 // the extra term (which would also turn a -0 gradient into +0).
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
 int run_step_l(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return k.l2 != 0.0f ? run_step_t<MF, VF, BF16P, STATS, SMODE, true>(c, k, t, s)
-                      : run_step_t<MF, VF, BF16P, STATS, SMODE, false>(c, k, t, s);
+  return k.l2 != 0.0f ? run_step_r<MF, VF, BF16P, STATS, SMODE, true>(c, k, t, s)
+                      : run_step_r<MF, VF, BF16P, STATS, SMODE, false>(c, k, t, s);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS>
@@ -1469,6 +1532,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       return fail(FP8ADAM_EINVAL, "bad schedule");
     if (cfg->decay_mode != FP8ADAM_DECAY_DECOUPLED && cfg->decay_mode != FP8ADAM_DECAY_L2)
       return fail(FP8ADAM_EINVAL, "bad decay_mode");
+    if (cfg->rounding != FP8ADAM_ROUND_NEAREST && cfg->rounding != FP8ADAM_ROUND_STOCHASTIC)
+      return fail(FP8ADAM_EINVAL, "bad rounding");
     const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
     if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
       return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
@@ -1615,6 +1680,9 @@ int step_consts(const fp8adam_ctx* ctx, const fp8adam_hparams* hp, StepConsts& k
     k.hist_len = ctx->hist_len;
     k.hist_slot = ctx->hist_len > 0 ? (int)((hp->step - 1) % ctx->hist_len) : 0;
     k.gfac = 1.0f;
+    k.seed_lo = (uint32_t)ctx->cfg.seed;
+    k.seed_hi = (uint32_t)(ctx->cfg.seed >> 32);
+    k.rng_t = (uint32_t)hp->step;
     return 0;
 }
 

@@ -34,7 +34,7 @@ def check_amp_state(name, got: dict, want: oracle.AmpState):
 
 def run_amp(sizes, *, schedule="two_pass", granularity="tensor", scaling="just_in_time", decay_mode="decoupled",
             master="fp32", max_norm=1.0, init_scale=2.0 ** 16, overflow_at=(3,), calls=7, growth_interval=3,
-            seed=0, stats=True, speculate_from_step=2):
+            seed=0, stats=True, speculate_from_step=2, rounding="nearest", rng_seed=0):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -48,7 +48,7 @@ def run_amp(sizes, *, schedule="two_pass", granularity="tensor", scaling="just_i
     H = 4
     opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=stats, state=state, schedule=schedule,
                       speculate_from_step=speculate_from_step, decay_mode=decay_mode, scaling=scaling,
-                      amax_history_len=H)
+                      amax_history_len=H, rounding=rounding, seed=rng_seed)
     delayed = scaling == "delayed"
     host = [OracleState(np_host(params[i]), np_host(state[0][i]), np_host(state[1][i]), np_host(state[2][i]),
                         np_host(state[3][i]), np_host(opt.amax_history[i]) if delayed else None)
@@ -85,10 +85,12 @@ def run_amp(sizes, *, schedule="two_pass", granularity="tensor", scaling="just_i
                 cfg = oracle.make_config(h, 0, 1, block=128 if granularity == "block128" else 0,
                                          master_bf16=(master == "bf16"), l2_coupled=(decay_mode == "l2"),
                                          history_len=H if delayed else 0, delayed_from=2,
-                                         grad_factor=ast.grad_factor, sched_step=t)
+                                         grad_factor=ast.grad_factor, sched_step=t,
+                                         stochastic=(rounding == "stochastic"), seed=rng_seed)
             for i, n in enumerate(sizes):
                 name = f"tensor {i} (numel {n}) call {t}"
                 if not ast.found_inf:
+                    cfg.tensor_index = i
                     host[i].step(cfg, gh[i])
                     if stats and granularity == "tensor":
                         _compare_stats(name, gstats[i], host[i].stats, granularity)

@@ -30,7 +30,7 @@ def compare_history(name, st: OracleState, hist_gpu: np.ndarray):
 
 def run_delayed(sizes, *, H=16, margin=0, delayed_from=2, scale_mode="pow2", master="fp32", stats=True,
                 decay_mode="decoupled", fmts=("e4m3", "e5m2"), seed=0, factors=FACTORS, lr=3e-4,
-                preset_history=False):
+                preset_history=False, rounding="nearest", rng_seed=0):
     m_fmt, v_fmt = fmts
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
@@ -46,7 +46,7 @@ def run_delayed(sizes, *, H=16, margin=0, delayed_from=2, scale_mode="pow2", mas
         state.append(hist)
     opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, scale_mode=scale_mode, collect_stats=stats,
                       state=state, decay_mode=decay_mode, scaling="delayed", amax_history_len=H, margin=margin,
-                      delayed_from_step=delayed_from)
+                      delayed_from_step=delayed_from, rounding=rounding, seed=rng_seed)
     host = [OracleState(np_host(params[i]), np_host(state[0][i]), np_host(state[1][i]), np_host(state[2][i]),
                         np_host(state[3][i]), np_host(opt.amax_history[i])) for i in range(len(sizes))]
     saturated = 0
@@ -60,8 +60,10 @@ def run_delayed(sizes, *, H=16, margin=0, delayed_from=2, scale_mode="pow2", mas
             h = oracle.Hyper(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
             cfg = oracle_config(h, m_fmt, v_fmt, "tensor", scale_mode, master, decay_mode, history_len=H,
                                 margin=margin, delayed_from=delayed_from)
+            cfg.stochastic, cfg.seed = int(rounding == "stochastic"), rng_seed
             gstats = opt.stats() if stats else None
             for i, n in enumerate(sizes):
+                cfg.tensor_index = i
                 host[i].step(cfg, np_host(grads[i]))
                 name = f"tensor {i} (numel {n}) step {t}"
                 compare_tensor(name, host[i], np_host(params[i]), np_host(opt.m[i]), np_host(opt.v[i]),

@@ -43,7 +43,8 @@ def _compare_stats(name, got: dict, want: dict, granularity: str):
 
 
 def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init, sizes=SIZES, steps=3,
-              lr=3e-4, seed=0, schedule="two_pass", speculate_from_step=0, decay_mode="decoupled", wd=0.1):
+              lr=3e-4, seed=0, schedule="two_pass", speculate_from_step=0, decay_mode="decoupled", wd=0.1,
+              rounding="nearest", rng_seed=0):
     m_fmt, v_fmt = fmts
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
@@ -68,7 +69,8 @@ def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init,
                         np_host(state[3][i])) for i in range(len(sizes))]
     opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, granularity=granularity,
                       scale_mode=scale_mode, collect_stats=collect_stats, state=state, schedule=schedule,
-                      speculate_from_step=speculate_from_step, decay_mode=decay_mode)
+                      speculate_from_step=speculate_from_step, decay_mode=decay_mode, rounding=rounding,
+                      seed=rng_seed)
     requantized = 0
     try:
         for t in range(1, steps + 1):
@@ -78,8 +80,10 @@ def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init,
             torch.cuda.synchronize()
             h = oracle.Hyper(lr=lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=wd, step=t)
             cfg = oracle_config(h, m_fmt, v_fmt, granularity, scale_mode, master, decay_mode)
+            cfg.stochastic, cfg.seed = int(rounding == "stochastic"), rng_seed
             gstats = opt.stats() if collect_stats else None
             for i, n in enumerate(sizes):
+                cfg.tensor_index = i
                 host[i].step(cfg, np_host(grads[i]))
                 name = f"tensor {i} (numel {n}) step {t}"
                 compare_tensor(name, host[i], np_host(params[i]), np_host(opt.m[i]), np_host(opt.v[i]),
@@ -159,7 +163,7 @@ def _top_code(fmt: str) -> int:
 
 
 def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0, collect_stats: bool = False,
-             schedule: str = "two_pass", speculate_from_step: int = 0):
+             schedule: str = "two_pass", speculate_from_step: int = 0, rounding: str = "nearest", rng_seed: int = 0):
     dev = torch.device("cuda")
     shapes = w.shapes
     params = [workloads.make_param(w, i, s, dev, base_seed) for i, (_, s) in enumerate(shapes)]
@@ -172,7 +176,7 @@ def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0
                               np.ones(nb, np.float32), np.ones(nb, np.float32))
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
                       collect_stats=collect_stats, schedule=schedule, speculate_from_step=speculate_from_step,
-                      decay_mode=w.decay_mode)
+                      decay_mode=w.decay_mode, rounding=rounding, seed=rng_seed)
     top_m, top_v = _top_code(w.m_fmt), _top_code(w.v_fmt)
     all_stats = []
     try:
@@ -186,7 +190,9 @@ def run_full(w: workloads.Workload, steps: int, sample: list, base_seed: int = 0
 
             def check(i):
                 st = host[i]
-                st.step(cfg, np_host(grads[i]))
+                cfg_i = oracle.Config.from_buffer_copy(cfg)
+                cfg_i.stochastic, cfg_i.seed, cfg_i.tensor_index = int(rounding == "stochastic"), rng_seed, i
+                st.step(cfg_i, np_host(grads[i]))
                 compare_tensor(f"{shapes[i][0]} step {t}", st, np_host(params[i]), np_host(opt.m[i]),
                                np_host(opt.v[i]), np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), w.master)
                 upload_params(params[i], st)
