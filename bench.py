@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0
 #   block-128 pass, fp32 master: 14 + 2 scales * (read 4 + write 4) / 128      = 14.125
 BYTES_PER_PARAM = {("tensor", "fp32"): 14.0, ("tensor", "bf16"): 10.0,
                    ("block128", "fp32"): 14.125, ("block128", "bf16"): 10.125}
-KERNEL_SOURCES = ["precision_adam_optimizer_amd/csrc/fp8adam.hip", "precision_adam_optimizer_amd/csrc/fp8_codec.h"]
+KERNEL_SOURCES = ["precision_adam_optimizer_amd/csrc/fp8adam.hip", "precision_adam_optimizer_amd/csrc/fp8adam_engine.h",
+                  "precision_adam_optimizer_amd/csrc/fp8_codec.h"]
 
 
 def log(*a):
@@ -164,7 +165,7 @@ def main():
     amp = pk.amp_state(loss_scale, dev) if args.amp else None
 
     def load_grads(t):
-        if args.same_grad and t > 1:
+        if args.same_grad and (t > 1 or not args.amp):  # (--amp: step 1 draws the scaled gradient)
             return
         for i, (_, shp) in enumerate(shapes):
             g = workloads.make_grad(w, i, shp, t, dev)

@@ -1,40 +1,9 @@
-// fp8adam.hip -- FP8-moment Adam/AdamW step for AMD MI355X (gfx950): kernels
-// and the C ABI declared in include/fp8adam.h.
-//
-// Method: Adam whose first moment is stored in FP8 E4M3 and second moment in
-// FP8 E5M2, each with a scale (daoxuan.cc explainer of arXiv 2409.12517,
-// section on why Adam keeps m in E4M3 and v in E5M2; shd-paper.top summary of
-// arXiv 2409.12517v2, method details: both Adam moments quantized to FP8).
-//
-// Device work per step:
-//   per-tensor scales (two streaming passes over a chunked multi-tensor list)
-//     k_amax    : dequantize, update m and v in registers, max|m'| / max v'
-//                 per chunk (wave DPP/shuffle max, then LDS) -> one partial
-//                 per chunk, no atomics
-//     k_reduce  : one work-group per tensor: max over the tensor's partials,
-//                 stage the old scales, write the new scales into the
-//                 caller's slots (and clear the tensor's stats counters)
-//     k_update  : recompute m', v' with the staged old scales; update p;
-//                 requantize m', v' with the new scales and saturation
-//   per-tensor scales, speculative schedule (opt-in; bit-identical results)
-//     k_update<SPEC> : one streaming pass that quantizes with the scale the
-//                 tensor had before the step (the prediction), writes the
-//                 codes into the other code buffer (ping-pong), updates p
-//                 and records per-part amax partials
-//     k_spec_reduce : per tensor, the true scale from the partials; where it
-//                 differs from the prediction the tensor is flagged
-//     k_fixup   : flagged tensors only: recompute m', v' from the old codes
-//                 (still intact in the source buffer) and requantize
-//   per-128-element scales (one streaming pass)
-//     k_block   : 32 lanes own one 128-element block; the block amax is a
-//                 5-step DPP/swizzle max, then update and requantize as above
-// The chunk table (built once at init) cuts every tensor into chunks of
-// 2^chunk_log2 elements (4096..32768, chosen per context so that even small
-// lists give a few thousand work-groups); an amax-pass work-group owns one
-// chunk, an update- or block-pass work-group owns one kPart-element part.  Loads and stores are dword-granular per lane
-// and contiguous across the wave (fp32 master: 16 B per lane).
-#include <hip/hip_runtime.h>
+// fp8adam.hip -- FP8-moment Adam/AdamW step for AMD MI355X (gfx950): the C
+// ABI declared in include/fp8adam.h, the loss-scaling kernels (gradient norm
+// and the scaler's decision) and the codec probes.  The step kernels and their
+// dispatch are in fp8adam_engine.h, instantiated in fp8adam_step_*.hip.
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -47,852 +16,27 @@
 
 #include "../../include/fp8adam.h"
 #include "fp8_codec.h"
+#include "fp8adam_engine.h"
 
 using namespace fp8adam;
+using namespace fp8adam_engine;
+
+namespace fp8adam_engine {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FP8ADAM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace fp8adam_engine
 
 namespace {
-
-// Launch-shape tunables (compile-time; the defaults are the measured best on MI355X).
-#ifndef FP8ADAM_MAX_CHUNK_LOG2
-#define FP8ADAM_MAX_CHUNK_LOG2 15  // largest chunk = amax-pass work-group (32768 elements)
-#endif
-#ifndef FP8ADAM_PART_LOG2
-#define FP8ADAM_PART_LOG2 12       // update / block work-group (4096 elements)
-#endif
-#ifndef FP8ADAM_AMAX_UNROLL
-#define FP8ADAM_AMAX_UNROLL 8
-#endif
-#ifndef FP8ADAM_UPDATE_UNROLL
-#define FP8ADAM_UPDATE_UNROLL 4
-#endif
-// 1: non-temporal loads / stores (each byte is touched once per pass)
-#ifndef FP8ADAM_NT_AMAX
-#define FP8ADAM_NT_AMAX 1
-#endif
-#ifndef FP8ADAM_NT_UPDATE_LD
-#define FP8ADAM_NT_UPDATE_LD 1
-#endif
-#ifndef FP8ADAM_NT_UPDATE_ST
-#define FP8ADAM_NT_UPDATE_ST 1
-#endif
-#ifndef FP8ADAM_NT_BLOCK_LD
-#define FP8ADAM_NT_BLOCK_LD 1
-#endif
-#ifndef FP8ADAM_XCD_ORDER
-#define FP8ADAM_XCD_ORDER 1  // update / block passes: each XCD walks its own contiguous eighth
-#endif
-#ifndef FP8ADAM_NT_BLOCK_ST
-#define FP8ADAM_NT_BLOCK_ST 1
-#endif
-
-constexpr int kThreads = 256;                     // 4 waves of 64
-constexpr int kGroup = 4;                         // consecutive elements per lane per access
-constexpr int kSubTile = kThreads * kGroup;       // 1024 elements per work-group access
-constexpr int kAmaxUnroll = FP8ADAM_AMAX_UNROLL;  // accesses in flight per lane, amax pass
-constexpr int kUpdUnroll = FP8ADAM_UPDATE_UNROLL; // accesses in flight per lane, update pass
-constexpr int kPartLog2 = FP8ADAM_PART_LOG2;
-constexpr int64_t kPart = (int64_t)1 << kPartLog2;  // elements per update / block work-group
-constexpr int kMaxChunkLog2 = FP8ADAM_MAX_CHUNK_LOG2;
-constexpr int kMinAmaxGroups = 2048;                // 8 work-groups per CU
-constexpr int kBlock = 128;                       // block-scale granularity
-constexpr int kReduceThreads = 1024;              // one work-group per tensor in k_reduce
-constexpr int kStatsPerTensor = 5;
-
-static_assert(kMaxChunkLog2 >= kPartLog2, "a chunk holds whole parts");
-static_assert(kPart % (kSubTile * kUpdUnroll) == 0, "part must hold whole unrolled update tiles");
-static_assert(kPart % (kBlock * 32) == 0, "part must hold whole block tiles");
-
-struct TensorDesc {
-  void* p;
-  const uint16_t* g;
-  uint8_t* m;
-  uint8_t* v;
-  float* sm;
-  float* sv;
-  int64_t numel;
-  int64_t chunk0;  // index of the tensor's first chunk
-  float* hist;     // delayed scaling: [2][H] amax history of m, v
-};
-
-// Update-pass variants: just-in-time scales known before the pass (two-pass
-// schedule), a predicted scale with codes to the other buffer (speculative),
-// or the delayed scale from the amax history.
-enum UpdateMode { kModeJit = 0, kModeSpec = 1, kModeDelayed = 2 };
-
-// Loss-scaling control of the step in flight, written on the device by
-// k_gradctl (library-owned): whether the step is skipped (a non-finite
-// gradient), the gradient factor clip_coef / S, and the bias-correction
-// constants of the device-side step count.
-struct GradCtl {
-  int32_t skip;
-  float gfac;
-  float step_size, inv_bc2, grow_m, grow_v;
-  int32_t hist_slot;  // delayed scaling: (t-1) mod H of the device-side t
-  uint32_t t;         // the device-side t (stochastic rounding's counter)
-};
-
-// With loss scaling, take the step's gradient factor and bias corrections;
-// true if the step is skipped (the kernel then changes nothing).
-__device__ __forceinline__ bool amp_apply(const GradCtl* gctl, StepConsts& c) {
-  if (gctl == nullptr) return false;
-  if (gctl->skip) return true;
-  c.gfac = gctl->gfac;
-  c.step_size = gctl->step_size;
-  c.inv_bc2 = gctl->inv_bc2;
-  c.grow_m = gctl->grow_m;
-  c.grow_v = gctl->grow_v;
-  c.hist_slot = gctl->hist_slot;
-  c.rng_t = gctl->t;
-  return false;
-}
-
-// Random words of the group of 4 elements starting at element i of tensor
-// tid: Philox4x32-10 with counter (i/4, t, tid) and the seed as key.  Word j
-// belongs to element i + j; the first moment uses its low 16 bits, the second
-// its high 16 bits.
-template <bool SR>
-__device__ __forceinline__ void sr_words(const StepConsts& c, int tid, int64_t i, uint32_t (&rw)[4]) {
-  if constexpr (SR) {
-    const uint64_t grp = (uint64_t)i >> 2;
-    philox4x32_10((uint32_t)grp, (uint32_t)(grp >> 32), c.rng_t, (uint32_t)tid, c.seed_lo, c.seed_hi, rw);
-  } else {
-    rw[0] = rw[1] = rw[2] = rw[3] = 0u;
-  }
-}
-
-// Quantize four values: round to nearest even, or stochastically with 16
-// bits of each word (low half for m, high half for v).
-template <int FMT, bool SR, bool HIGH>
-__device__ __forceinline__ uint32_t quant4(const float (&q)[4], const uint32_t (&rw)[4]) {
-  if constexpr (SR) {
-    const uint32_t r[4] = {HIGH ? rw[0] >> 16 : rw[0] & 0xFFFFu, HIGH ? rw[1] >> 16 : rw[1] & 0xFFFFu,
-                           HIGH ? rw[2] >> 16 : rw[2] & 0xFFFFu, HIGH ? rw[3] >> 16 : rw[3] & 0xFFFFu};
-    return encode4_sr<FMT>(q[0], q[1], q[2], q[3], r);
-  } else {
-    return encode4<FMT>(q[0], q[1], q[2], q[3]);
-  }
-}
-
-// One value, element i of tensor tid (the ragged tails).
-template <int FMT, bool SR, bool HIGH>
-__device__ __forceinline__ uint32_t quant1(const StepConsts& c, int tid, int64_t i, float q) {
-  if constexpr (SR) {
-    uint32_t rw[4];
-    sr_words<true>(c, tid, i & ~(int64_t)3, rw);
-    const uint32_t w = rw[i & 3];
-    const uint32_t r[4] = {HIGH ? w >> 16 : w & 0xFFFFu, 0u, 0u, 0u};
-    return encode4_sr<FMT>(q, 0.0f, 0.0f, 0.0f, r) & 0xFFu;
-  } else {
-    return encode1<FMT>(q);
-  }
-}
-
-enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
-  return x;
-}
-
-// Logical work item (chunk or part) of this work-group.  Work-groups are
-// dispatched round-robin over the 8 XCDs (work-group b runs on XCD b % 8).
-// In XCD order, work-group b takes item (b % 8) * ceil(n/8) + b / 8, so each
-// XCD streams through its own contiguous eighth of the list (measured: update
-// pass -3%, block pass -5%); the grid is then 8 * ceil(n/8) and a surplus
-// work-group gets -1 (returns at once).  The amax pass and the fix-up keep
-// the linear order (XCD order measured +4% there, and it would put a flagged
-// tensor's chunks on few XCDs).
-template <bool XCD>
-__device__ __forceinline__ int64_t work_index(int64_t n) {
-  if constexpr (XCD) {
-    const int64_t per = (n + 7) >> 3;
-    const int64_t w = (int64_t)(blockIdx.x & 7u) * per + (int64_t)(blockIdx.x >> 3);
-    return w < n ? w : -1;
-  } else {
-    (void)n;
-    return (int64_t)blockIdx.x;
-  }
-}
-
-template <bool XCD>
-inline unsigned grid_for(int64_t n) {
-  return XCD ? (unsigned)(((n + 7) >> 3) << 3) : (unsigned)n;
-}
-
-constexpr bool kXcdStreams = FP8ADAM_XCD_ORDER != 0;  // update and block passes
-
-// Work-group max of two values; result valid in thread 0.
-__device__ __forceinline__ void block_max2(uint32_t& a, uint32_t& b) {
-  __shared__ uint32_t red[2][kThreads / 64];
-  a = wave_max(a);
-  b = wave_max(b);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[0][wave] = a;
-    red[1][wave] = b;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; w++) {
-      a = max(a, red[0][w]);
-      b = max(b, red[1][w]);
-    }
-  }
-}
-
-template <bool STATS>
-__device__ __forceinline__ void flush_counters(unsigned long long* counters, int tid,
-                                               const uint32_t (&cnt)[kStatsPerTensor]) {
-  if constexpr (STATS) {
-#pragma unroll
-    for (int k = 0; k < kStatsPerTensor; k++) {
-      const uint32_t s = wave_sum(cnt[k]);
-      if ((threadIdx.x & 63) == 0 && s != 0)
-        atomicAdd(&counters[(int64_t)tid * kStatsPerTensor + k], (unsigned long long)s);
-    }
-  }
-}
-
-template <int MF, int VF, bool STATS>
-__device__ __forceinline__ void count_element(uint32_t (&cnt)[kStatsPerTensor], float m1, float v1,
-                                              float qm, float qv, uint32_t cm, uint32_t cv) {
-  if constexpr (STATS) {
-    cnt[kUnderM] += (m1 != 0.0f && (cm & 0x7Fu) == 0u);
-    cnt[kUnderV] += (v1 != 0.0f && (cv & 0x7Fu) == 0u);
-    cnt[kSatM] += (fabsf(qm) > Format<MF>::kMax);
-    cnt[kSatV] += (fabsf(qv) > Format<VF>::kMax);
-    cnt[kNonFinite] += (!isfinite(m1) || !isfinite(v1));
-  }
-}
-
-typedef float vf4 __attribute__((ext_vector_type(4)));
-typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
-typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
-
-// Streamed loads and stores (optionally non-temporal: the data is touched once per pass).
-// The tensor pointers come from a descriptor in memory, so the compiler cannot
-// prove they are global and would emit flat instructions; these helpers cast
-// them into the global address space (global_load / global_store).
-#define FP8ADAM_GLOBAL __attribute__((address_space(1)))
-
-template <typename T, bool NT>
-__device__ __forceinline__ T ld_stream(const void* p) {
-  const FP8ADAM_GLOBAL T* g = (const FP8ADAM_GLOBAL T*)(p);
-  if constexpr (NT) return __builtin_nontemporal_load(g);
-  else return *g;
-}
-
-template <typename T, bool NT>
-__device__ __forceinline__ void st_stream(void* p, T x) {
-  FP8ADAM_GLOBAL T* g = (FP8ADAM_GLOBAL T*)(p);
-  if constexpr (NT) __builtin_nontemporal_store(x, g);
-  else *g = x;
-}
-
-template <typename T>
-__device__ __forceinline__ T ld_global(const void* p) {
-  return *(const FP8ADAM_GLOBAL T*)(p);
-}
-
-template <typename T>
-__device__ __forceinline__ void st_global(void* p, T x) {
-  *(FP8ADAM_GLOBAL T*)(p) = x;
-}
-
-// Loads of one group of four consecutive elements.
-struct Group {
-  vu2 g;         // 4 bf16
-  uint32_t cm;   // 4 codes
-  uint32_t cv;   // 4 codes
-  vf4 p;         // fp32 master (or 4 bf16 in .x/.y)
-};
-
-template <bool BF16P, bool NT>
-__device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group& G, bool with_p) {
-  G.g = ld_stream<vu2, NT>(d.g + i);
-  G.cm = ld_stream<uint32_t, NT>(d.m + i);
-  G.cv = ld_stream<uint32_t, NT>(d.v + i);
-  if (with_p) {
-    if constexpr (BF16P) {
-      const vu2 pb = ld_stream<vu2, NT>(static_cast<const uint16_t*>(d.p) + i);
-      G.p = vf4{__uint_as_float(pb.x), __uint_as_float(pb.y), 0.0f, 0.0f};
-    } else {
-      G.p = ld_stream<vf4, NT>(static_cast<const float*>(d.p) + i);
-    }
-  }
-}
-
-// Unpack 4 grads, 4 dequantized moments, and the fresh moments.  p (the
-// parameters before the step) is read only with coupled L2.
-template <int MF, int VF, bool L2>
-__device__ __forceinline__ void fresh_moments(const StepConsts& c, const Group& G, const float (&p)[4], float sm,
-                                              float sv, float (&m1)[4], float (&v1)[4]) {
-  const float g[4] = {bf16_lo(G.g.x), bf16_hi(G.g.x), bf16_lo(G.g.y), bf16_hi(G.g.y)};
-  float m[4], v[4];
-  decode4<MF>(G.cm, m);
-  decode4<VF>(G.cv, v);
-#pragma unroll
-  for (int j = 0; j < 4; j++) moment_update(c, grad_in<L2>(c, g[j], p[j]), m[j] * sm, v[j] * sv, m1[j], v1[j]);
-}
-
-template <bool BF16P>
-__device__ __forceinline__ void unpack_p(const Group& G, float (&p)[4]) {
-  if constexpr (BF16P) {
-    const uint32_t a = __float_as_uint(G.p.x), b = __float_as_uint(G.p.y);
-    p[0] = bf16_lo(a); p[1] = bf16_hi(a); p[2] = bf16_lo(b); p[3] = bf16_hi(b);
-  } else {
-    p[0] = G.p.x; p[1] = G.p.y; p[2] = G.p.z; p[3] = G.p.w;
-  }
-}
-
-template <bool BF16P, bool NT>
-__device__ __forceinline__ void store_p4(const TensorDesc& d, int64_t i, const float (&p)[4]) {
-  if constexpr (BF16P) {
-    st_stream<vu2, NT>(static_cast<uint16_t*>(d.p) + i, vu2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-  } else {
-    st_stream<vf4, NT>(static_cast<float*>(d.p) + i, vf4{p[0], p[1], p[2], p[3]});
-  }
-}
-
-template <bool BF16P>
-__device__ __forceinline__ float load_p1(const TensorDesc& d, int64_t i) {
-  if constexpr (BF16P) return __uint_as_float((uint32_t)ld_global<uint16_t>(static_cast<const uint16_t*>(d.p) + i) << 16);
-  else return ld_global<float>(static_cast<const float*>(d.p) + i);
-}
-
-__device__ __forceinline__ float load_g1(const TensorDesc& d, int64_t i) {
-  return __uint_as_float((uint32_t)ld_global<uint16_t>(d.g + i) << 16);
-}
-
-template <bool BF16P>
-__device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x) {
-  if constexpr (BF16P) st_global<uint16_t>(static_cast<uint16_t*>(d.p) + i, (uint16_t)f32_to_bf16_rne(x));
-  else st_global<float>(static_cast<float*>(d.p) + i, x);
-}
-
-// Speculative schedule: the predicted scale is the POW2 scale of the previous
-// step's amax times the growth a stationary gradient would give the moving
-// average, (1-beta^t)/(1-beta^(t-1)).  Without a usable previous amax (zero or
-// non-finite) it is the power of two with the exponent of the tensor's current
-// scale (1 if that is zero, subnormal, Inf or NaN).  The update pass and the
-// check evaluate exactly the same expression, so they agree on the prediction.
-__device__ __forceinline__ uint32_t exponent_scale_bits(float s_old) {
-  const uint32_t e = (__float_as_uint(s_old) >> 23) & 0xFFu;
-  if (e == 0u || e == 255u) return 0x3F800000u;
-  return e << 23;
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t predicted_scale_bits(uint32_t amax_prev, float s_old, float growth) {
-  if (amax_prev == 0u || (amax_prev >> 23) >= 255u) return exponent_scale_bits(s_old);
-  float s, inv;
-  choose_scale<FMT, 0>(__float_as_uint(__uint_as_float(amax_prev) * growth) & 0x7FFFFFFFu, s, inv);
-  return __float_as_uint(s);
-}
-
-__device__ __forceinline__ float inverse_pow2(uint32_t pow2_bits) {
-  return __uint_as_float((254u - (pow2_bits >> 23)) << 23);
-}
-
-// Delayed scaling: the scale of the largest entry of a tensor's amax history
-// (H entries, sign bits ignored; a non-finite entry gives scale 1) times
-// 2^margin.  Called by whole waves; every lane gets the same s and inv.
-template <int FMT, int SMODE>
-__device__ __forceinline__ void delayed_scale(const float* h, const StepConsts& c, float& s, float& inv) {
-  uint32_t r = 0;
-  for (int j = threadIdx.x & 63; j < c.hist_len; j += 64) r = max(r, abs_bits(ld_global<float>(h + j)));
-  r = wave_max(r);
-  choose_scale<FMT, SMODE>(abs_bits(__uint_as_float(r) * c.margin_scale), s, inv);
-}
-
-// ------------------------------------------------------------------ pass 1
-
-template <int MF, int VF, bool BF16P, bool L2>
-__global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
-                                                   const int32_t* __restrict__ chunk_tid,
-                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2,
-                                                   int64_t nwork, const GradCtl* __restrict__ gctl) {
-  const int64_t w = work_index<false>(nwork);
-  if (w < 0 || amp_apply(gctl, c)) return;
-  const int tid = chunk_tid[w];
-  const TensorDesc d = descs[tid];
-  const int64_t start = (w - d.chunk0) << chunk_log2;
-  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
-  const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
-  const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
-  uint32_t am = 0, av = 0;
-
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
-    Group G[kAmaxUnroll];
-#pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_AMAX != 0>(d, i, G[u], L2);
-    }
-#pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        float m1[4], v1[4], p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if constexpr (L2) unpack_p<BF16P>(G[u], p);
-        fresh_moments<MF, VF, L2>(c, G[u], p, sm, sv, m1, v1);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          am = max(am, abs_bits(m1[j]));
-          av = max(av, abs_bits(v1[j]));
-        }
-      }
-    }
-  }
-  // ragged tail (< 4 elements at the end of a tensor)
-  if (gend + threadIdx.x < end) {
-    const int64_t i = gend + threadIdx.x;
-    const float g = grad_in<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
-    float m1, v1;
-    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
-    am = max(am, abs_bits(m1));
-    av = max(av, abs_bits(v1));
-  }
-  block_max2(am, av);
-  if (threadIdx.x == 0) partial[w] = make_uint2(am, av);
-}
-
-// ------------------------------------------------------------------ reduce
-//
-// One work-group per tensor: amax over the tensor's chunk partials (unsigned
-// max of fp32 bit patterns of non-negative values: exact and order-free),
-// then the old scales are staged for the update pass and the new scales are
-// written into the caller's slots.  Non-finite amax (NaN/Inf bit patterns
-// are the largest) gives scale 1.
-
-template <int MF, int VF, int SMODE, bool STATS>
-__global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __restrict__ descs,
-                                                           const uint2* __restrict__ partial,
-                                                           uint32_t* __restrict__ amax,
-                                                           float* __restrict__ old_scale,
-                                                           unsigned long long* __restrict__ counters,
-                                                           int chunk_log2, int32_t* __restrict__ flags,
-                                                           int hist_len, int hist_slot,
-                                                           const GradCtl* __restrict__ gctl) {
-  const int t = blockIdx.x;
-  if (gctl != nullptr && gctl->skip) {  // skipped step: scales, amax and history stay
-    if (threadIdx.x == 0) flags[t] = 0;
-    if (STATS && threadIdx.x < kStatsPerTensor) counters[(int64_t)t * kStatsPerTensor + threadIdx.x] = 0ull;
-    return;
-  }
-  if (gctl != nullptr) hist_slot = gctl->hist_slot;
-  const TensorDesc d = descs[t];
-  const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
-  uint32_t am = 0, av = 0;
-  for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) {
-    const uint2 pv = partial[d.chunk0 + k];
-    am = max(am, pv.x);
-    av = max(av, pv.y);
-  }
-  __shared__ uint32_t red[2][kReduceThreads / 64];
-  am = wave_max(am);
-  av = wave_max(av);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[0][wave] = am;
-    red[1][wave] = av;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kReduceThreads / 64; w++) {
-      am = max(am, red[0][w]);
-      av = max(av, red[1][w]);
-    }
-    amax[2 * t] = am;
-    amax[2 * t + 1] = av;
-    flags[t] = 0;
-    if (d.numel > 0) {
-      old_scale[2 * t] = ld_global<float>(d.sm);
-      old_scale[2 * t + 1] = ld_global<float>(d.sv);
-      float s, inv;
-      choose_scale<MF, SMODE>(am, s, inv);
-      st_global<float>(d.sm, s);
-      choose_scale<VF, SMODE>(av, s, inv);
-      st_global<float>(d.sv, s);
-      if (hist_len > 0) {  // just-in-time step of delayed scaling: seed the history
-        st_global<float>(d.hist + hist_slot, __uint_as_float(am));
-        st_global<float>(d.hist + hist_len + hist_slot, __uint_as_float(av));
-      }
-    }
-  }
-  if constexpr (STATS) {
-    if (threadIdx.x < kStatsPerTensor) counters[(int64_t)t * kStatsPerTensor + threadIdx.x] = 0ull;
-  }
-}
-
-// ------------------------------------------------------------------ pass 2
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
-__global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
-                                                     const TensorDesc* __restrict__ dst_descs,
-                                                     const int32_t* __restrict__ chunk_tid,
-                                                     const uint32_t* __restrict__ amax,
-                                                     const float* __restrict__ old_scale, StepConsts c,
-                                                     unsigned long long* __restrict__ counters, int chunk_log2,
-                                                     uint2* __restrict__ part_amax, int64_t nwork,
-                                                     const GradCtl* __restrict__ gctl) {
-  constexpr bool SPEC = MODE == kModeSpec;
-  constexpr bool PARTS = MODE != kModeJit;  // per-part amax partials for the commit kernel
-  const int64_t w = work_index<kXcdStreams>(nwork);
-  if (w < 0) return;
-  const int split_log2 = chunk_log2 - kPartLog2;
-  const int64_t chunk = w >> split_log2;
-  const int tid = chunk_tid[chunk];
-  const TensorDesc d = descs[tid];
-  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << kPartLog2);
-  const int64_t end = min(start + kPart, d.numel);
-  if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
-  const int64_t gend = start + ((end - start) & ~(int64_t)3);
-  // codes go back in place (two-pass) or into the other buffer (speculative)
-  uint8_t* const dm = SPEC ? dst_descs[tid].m : d.m;
-  uint8_t* const dv = SPEC ? dst_descs[tid].v : d.v;
-  if (amp_apply(gctl, c)) {  // skipped step
-    // the speculative schedule switches buffers regardless: carry the codes over
-    if constexpr (SPEC) {
-      for (int64_t i = start + kGroup * threadIdx.x; i < gend; i += kSubTile) {
-        st_global<uint32_t>(dm + i, ld_global<uint32_t>(d.m + i));
-        st_global<uint32_t>(dv + i, ld_global<uint32_t>(d.v + i));
-      }
-      if (gend + threadIdx.x < end) {
-        st_global<uint8_t>(dm + gend + threadIdx.x, ld_global<uint8_t>(d.m + gend + threadIdx.x));
-        st_global<uint8_t>(dv + gend + threadIdx.x, ld_global<uint8_t>(d.v + gend + threadIdx.x));
-      }
-    }
-    return;
-  }
-  float sm, sv, ism, isv;
-  if constexpr (SPEC) {
-    sm = ld_global<float>(d.sm);
-    sv = ld_global<float>(d.sv);
-    ism = inverse_pow2(predicted_scale_bits<MF>(amax[2 * tid], sm, c.grow_m));
-    isv = inverse_pow2(predicted_scale_bits<VF>(amax[2 * tid + 1], sv, c.grow_v));
-  } else if constexpr (MODE == kModeDelayed) {
-    float unused;
-    sm = ld_global<float>(d.sm);
-    sv = ld_global<float>(d.sv);
-    delayed_scale<MF, SMODE>(d.hist, c, unused, ism);
-    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, unused, isv);
-  } else {
-    float nsm, nsv;
-    sm = old_scale[2 * tid];
-    sv = old_scale[2 * tid + 1];
-    choose_scale<MF, SMODE>(amax[2 * tid], nsm, ism);
-    choose_scale<VF, SMODE>(amax[2 * tid + 1], nsv, isv);
-  }
-  uint32_t am = 0, av = 0;  // speculative / delayed: this part's amax
-  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
-
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUpdUnroll) {
-    Group G[kUpdUnroll];
-#pragma unroll
-    for (int u = 0; u < kUpdUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_UPDATE_LD != 0>(d, i, G[u], true);
-    }
-#pragma unroll
-    for (int u = 0; u < kUpdUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        float m1[4], v1[4], p[4], qm[4], qv[4];
-        unpack_p<BF16P>(G[u], p);
-        fresh_moments<MF, VF, L2>(c, G[u], p, sm, sv, m1, v1);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          p[j] = param_update(c, p[j], m1[j], v1[j]);
-          qm[j] = m1[j] * ism;
-          qv[j] = v1[j] * isv;
-          if constexpr (PARTS) {
-            am = max(am, abs_bits(m1[j]));
-            av = max(av, abs_bits(v1[j]));
-          }
-        }
-        uint32_t rw[4];
-        sr_words<SR>(c, tid, i, rw);
-        const uint32_t wm = quant4<MF, SR, false>(qm, rw);
-        const uint32_t wv = quant4<VF, SR, true>(qv, rw);
-        if constexpr (STATS) {
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-            count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
-        }
-        store_p4<BF16P, FP8ADAM_NT_UPDATE_ST != 0>(d, i, p);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dm + i, wm);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dv + i, wv);
-      }
-    }
-  }
-  if (gend + threadIdx.x < end) {
-    const int64_t i = gend + threadIdx.x;
-    const float p0 = load_p1<BF16P>(d, i);
-    const float g = grad_in<L2>(c, load_g1(d, i), p0);
-    float m1, v1;
-    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
-    const float p = param_update(c, p0, m1, v1);
-    const float qm = m1 * ism, qv = v1 * isv;
-    const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm), cv = quant1<VF, SR, true>(c, tid, i, qv);
-    count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
-    if constexpr (PARTS) {
-      am = max(am, abs_bits(m1));
-      av = max(av, abs_bits(v1));
-    }
-    store_p1<BF16P>(d, i, p);
-    st_global<uint8_t>(dm + i, (uint8_t)cm);
-    st_global<uint8_t>(dv + i, (uint8_t)cv);
-  }
-  flush_counters<STATS>(counters, tid, cnt);
-  if constexpr (PARTS) {
-    block_max2(am, av);
-    if (threadIdx.x == 0) part_amax[w] = make_uint2(am, av);
-  }
-}
-
-// ------------------------------------------------------- delayed: commit
-//
-// One work-group per tensor, after the delayed pass: the tensor's amax from the
-// per-part partials; wave 0 recomputes the delayed scales exactly as the pass
-// did (before the history changes), thread 0 commits them and records this
-// step's amax in the history slot.
-
-template <int MF, int VF, int SMODE>
-__global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorDesc* __restrict__ descs,
-                                                                   const uint2* __restrict__ part_amax,
-                                                                   uint32_t* __restrict__ amax, StepConsts c,
-                                                                   int chunk_log2, const GradCtl* __restrict__ gctl) {
-  if (amp_apply(gctl, c)) return;  // skipped step: scales, amax and history stay
-  const int t = blockIdx.x;
-  const TensorDesc d = descs[t];
-  const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
-  const int64_t part0 = d.chunk0 << (chunk_log2 - kPartLog2);
-  uint32_t am = 0, av = 0;
-  for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
-    const uint2 pv = part_amax[part0 + k];
-    am = max(am, pv.x);
-    av = max(av, pv.y);
-  }
-  __shared__ uint32_t red[2][kReduceThreads / 64];
-  am = wave_max(am);
-  av = wave_max(av);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[0][wave] = am;
-    red[1][wave] = av;
-  }
-  __syncthreads();
-  if (wave == 0 && d.numel > 0) {  // uniform: all of wave 0, or none
-    float s_m, s_v, inv;
-    delayed_scale<MF, SMODE>(d.hist, c, s_m, inv);
-    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, s_v, inv);
-    if (lane == 0) {
-      for (int w = 1; w < kReduceThreads / 64; w++) {
-        am = max(am, red[0][w]);
-        av = max(av, red[1][w]);
-      }
-      st_global<float>(d.sm, s_m);
-      st_global<float>(d.sv, s_v);
-      st_global<float>(d.hist + c.hist_slot, __uint_as_float(am));
-      st_global<float>(d.hist + c.hist_len + c.hist_slot, __uint_as_float(av));
-      amax[2 * t] = am;
-      amax[2 * t + 1] = av;
-    }
-  } else if (threadIdx.x == 0) {
-    amax[2 * t] = 0u;
-    amax[2 * t + 1] = 0u;
-  }
-}
-
-// ------------------------------------------------- speculative: verify, fix up
-//
-// One work-group per tensor: the true amax from the per-part partials, the
-// true POW2 scales, and a comparison with the predicted ones.  The old scales
-// are staged for the fix-up, the true scales committed; a flagged tensor's
-// stats counters are cleared (the fix-up recounts them).
-
-template <int MF, int VF, bool STATS>
-__global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc* __restrict__ descs,
-                                                                const uint2* __restrict__ part_amax,
-                                                                uint32_t* __restrict__ amax,
-                                                                float* __restrict__ old_scale,
-                                                                int32_t* __restrict__ flags,
-                                                                unsigned long long* __restrict__ counters,
-                                                                int chunk_log2, StepConsts c,
-                                                                const GradCtl* __restrict__ gctl) {
-  const int t = blockIdx.x;
-  if (amp_apply(gctl, c)) {  // skipped step: scales and amax stay, nothing to fix up
-    if (threadIdx.x == 0) flags[t] = 0;
-    return;
-  }
-  const float grow_m = c.grow_m, grow_v = c.grow_v;
-  const TensorDesc d = descs[t];
-  const int64_t nparts = (d.numel + kPart - 1) >> kPartLog2;
-  const int64_t part0 = d.chunk0 << (chunk_log2 - kPartLog2);
-  uint32_t am = 0, av = 0;
-  for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
-    const uint2 pv = part_amax[part0 + k];
-    am = max(am, pv.x);
-    av = max(av, pv.y);
-  }
-  __shared__ uint32_t red[2][kReduceThreads / 64];
-  __shared__ int32_t flag;
-  am = wave_max(am);
-  av = wave_max(av);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    red[0][wave] = am;
-    red[1][wave] = av;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kReduceThreads / 64; w++) {
-      am = max(am, red[0][w]);
-      av = max(av, red[1][w]);
-    }
-    int32_t f = 0;
-    if (d.numel > 0) {
-      const float so_m = ld_global<float>(d.sm), so_v = ld_global<float>(d.sv);
-      // the prediction the update pass used: from the previous amax, read before it is replaced
-      const uint32_t pm = predicted_scale_bits<MF>(amax[2 * t], so_m, grow_m);
-      const uint32_t pv = predicted_scale_bits<VF>(amax[2 * t + 1], so_v, grow_v);
-      float s_m, s_v, inv;
-      choose_scale<MF, 0>(am, s_m, inv);
-      choose_scale<VF, 0>(av, s_v, inv);
-      f = (__float_as_uint(s_m) != pm ? 1 : 0) | (__float_as_uint(s_v) != pv ? 2 : 0);
-      old_scale[2 * t] = so_m;
-      old_scale[2 * t + 1] = so_v;
-      st_global<float>(d.sm, s_m);
-      st_global<float>(d.sv, s_v);
-    }
-    amax[2 * t] = am;
-    amax[2 * t + 1] = av;
-    flags[t] = f;
-    flag = f;
-  }
-  __syncthreads();
-  if constexpr (STATS) {
-    // the fix-up recounts the underflow / saturation counts of a re-quantized moment
-    if (threadIdx.x == 0 && (flag & 1)) {
-      counters[(int64_t)t * kStatsPerTensor + kUnderM] = 0ull;
-      counters[(int64_t)t * kStatsPerTensor + kSatM] = 0ull;
-    }
-    if (threadIdx.x == 0 && (flag & 2)) {
-      counters[(int64_t)t * kStatsPerTensor + kUnderV] = 0ull;
-      counters[(int64_t)t * kStatsPerTensor + kSatV] = 0ull;
-    }
-  }
-}
-
-// One work-group per chunk of a flagged tensor (the others return at once):
-// recompute the mispredicted moment(s) from the gradient and the old codes in
-// the source buffer and requantize them with the true scales into the
-// destination buffer.  p is not touched: its update does not depend on the
-// scales.  Flag bit 0: m, bit 1: v.
-template <int FMT, bool STATS, bool IS_V, bool SR>
-__device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const TensorDesc& d, uint8_t* dst,
-                                             int64_t start, int64_t end, float s_old, float inv_new,
-                                             uint32_t& under, uint32_t& sat) {
-  const uint8_t* src = IS_V ? d.v : d.m;
-  const int64_t gend = start + ((end - start) & ~(int64_t)3);
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
-    vu2 gg[kAmaxUnroll];
-    uint32_t cc[kAmaxUnroll];
-#pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        gg[u] = ld_stream<vu2, FP8ADAM_NT_AMAX != 0>(d.g + i);
-        cc[u] = ld_stream<uint32_t, FP8ADAM_NT_AMAX != 0>(src + i);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        const float g[4] = {bf16_lo(gg[u].x), bf16_hi(gg[u].x), bf16_lo(gg[u].y), bf16_hi(gg[u].y)};
-        float x[4], q[4];
-        decode4<FMT>(cc[u], x);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          float m1, v1;
-          // moment_update computes both moments; only the one being fixed is used
-          moment_update(c, g[j] * c.gfac, x[j] * s_old, x[j] * s_old, m1, v1);
-          x[j] = IS_V ? v1 : m1;
-          q[j] = x[j] * inv_new;
-        }
-        uint32_t rw[4];
-        sr_words<SR>(c, tid, i, rw);
-        const uint32_t w = quant4<FMT, SR, IS_V>(q, rw);
-        if constexpr (STATS) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            under += (x[j] != 0.0f && ((w >> (8 * j)) & 0x7Fu) == 0u);
-            sat += (fabsf(q[j]) > Format<FMT>::kMax);
-          }
-        }
-        st_global<uint32_t>(dst + i, w);
-      }
-    }
-  }
-  if (gend + threadIdx.x < end) {
-    const int64_t i = gend + threadIdx.x;
-    const float g = load_g1(d, i) * c.gfac;
-    const float x0 = decode1<FMT>(ld_global<uint8_t>(src + i)) * s_old;
-    float m1, v1;
-    moment_update(c, g, x0, x0, m1, v1);
-    const float x = IS_V ? v1 : m1;
-    const float q = x * inv_new;
-    const uint32_t code = quant1<FMT, SR, IS_V>(c, tid, i, q);
-    if constexpr (STATS) {
-      under += (x != 0.0f && (code & 0x7Fu) == 0u);
-      sat += (fabsf(q) > Format<FMT>::kMax);
-    }
-    st_global<uint8_t>(dst + i, (uint8_t)code);
-  }
-}
-
-template <int MF, int VF, bool STATS, bool SR>
-__global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict__ descs,
-                                                    const TensorDesc* __restrict__ dst_descs,
-                                                    const int32_t* __restrict__ chunk_tid,
-                                                    const uint32_t* __restrict__ amax,
-                                                    const float* __restrict__ old_scale,
-                                                    const int32_t* __restrict__ flags, StepConsts c,
-                                                    unsigned long long* __restrict__ counters, int chunk_log2,
-                                                    int64_t nwork, const GradCtl* __restrict__ gctl) {
-  const int64_t w = work_index<false>(nwork);
-  if (w < 0 || amp_apply(gctl, c)) return;
-  const int tid = chunk_tid[w];
-  const int32_t f = flags[tid];
-  if (!f) return;  // uniform for the work-group
-  const TensorDesc d = descs[tid];
-  const int64_t start = (w - d.chunk0) << chunk_log2;
-  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
-  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
-  if (f & 1) {
-    float s, inv;
-    choose_scale<MF, 0>(amax[2 * tid], s, inv);
-    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[2 * tid], inv, cnt[kUnderM],
-                                   cnt[kSatM]);
-  }
-  if (f & 2) {
-    float s, inv;
-    choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
-    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[2 * tid + 1], inv, cnt[kUnderV],
-                                  cnt[kSatV]);
-  }
-  flush_counters<STATS>(counters, tid, cnt);
-}
 
 // ------------------------------------------- loss scaling and clipping
 //
@@ -1044,167 +188,6 @@ __global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __rest
   st_global(&ctl->t, (uint32_t)t);
 }
 
-// Zero the stats counters (and, in block mode, the amax used for stats).
-__global__ __launch_bounds__(kThreads) void k_reset(unsigned long long* __restrict__ counters, int64_t ncnt,
-                                                    uint32_t* __restrict__ amax, int64_t namax) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ncnt; i += (int64_t)gridDim.x * blockDim.x)
-    counters[i] = 0ull;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < namax; i += (int64_t)gridDim.x * blockDim.x)
-    amax[i] = 0u;
-}
-
-// ------------------------------------------------------------ block-128 mode
-//
-// 32 lanes own one 128-element block, each lane 4
-// consecutive elements per access, so every access of the wave covers two
-// whole blocks (a full 128-byte line of codes per block and moment; a layout
-// with 8 lanes x 16 elements per block wrote 32-byte pieces of each line and
-// ran ~4% slower).  The block amax is a 5-step max over the 32 lanes (DPP
-// within 16 lanes, then a swizzle across the two 16-lane rows).
-
-__device__ __forceinline__ uint32_t group32_max(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
-  x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F));                          // lane ^ 16
-  return x;
-}
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
-__global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict__ descs,
-                                                      const int32_t* __restrict__ chunk_tid, StepConsts c,
-                                                      unsigned long long* __restrict__ counters,
-                                                      uint32_t* __restrict__ amax, int chunk_log2, int64_t nwork,
-                                                      const GradCtl* __restrict__ gctl) {
-  const int64_t w = work_index<kXcdStreams>(nwork);
-  if (w < 0 || amp_apply(gctl, c)) return;
-  const int split_log2 = chunk_log2 - kPartLog2;
-  const int64_t chunk = w >> split_log2;
-  const int tid = chunk_tid[chunk];
-  const TensorDesc d = descs[tid];
-  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << kPartLog2);
-  const int64_t end = min(start + kPart, d.numel);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, hl = lane & 31;
-  uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
-  uint32_t tam = 0, tav = 0;
-  float tsm = 0.0f, tsv = 0.0f;
-
-  for (int64_t tile = start; tile < end; tile += (int64_t)kBlock * 32) {
-    int64_t b0[4];
-    bool ex[4], full[4];
-    float sm[4], sv[4];
-    Group G[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      b0[j] = tile + (int64_t)(wave * 8 + 2 * j + half) * kBlock;
-      ex[j] = b0[j] < end;
-      full[j] = b0[j] + kBlock <= end;
-      sm[j] = 1.0f;
-      sv[j] = 1.0f;
-      if (ex[j]) {
-        sm[j] = ld_global<float>(d.sm + b0[j] / kBlock);
-        sv[j] = ld_global<float>(d.sv + b0[j] / kBlock);
-      }
-      if (full[j]) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0[j] + 4 * hl, G[j], true);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      float m1[4], v1[4], p[4];
-      const int64_t i0 = b0[j] + 4 * hl;
-      if (full[j]) {
-        unpack_p<BF16P>(G[j], p);
-        fresh_moments<MF, VF, L2>(c, G[j], p, sm[j], sv[j], m1, v1);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int64_t i = i0 + r;
-          float a = 0.0f, b = 0.0f, q = 0.0f;
-          if (ex[j] && i < end) {
-            q = load_p1<BF16P>(d, i);
-            const float g = grad_in<L2>(c, load_g1(d, i), q);
-            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm[j],
-                          decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv[j], a, b);
-          }
-          m1[r] = a;
-          v1[r] = b;
-          p[r] = q;
-        }
-      }
-      uint32_t am = 0, av = 0;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        am = max(am, abs_bits(m1[r]));
-        av = max(av, abs_bits(v1[r]));
-      }
-      am = group32_max(am);
-      av = group32_max(av);
-      float nsm, ism, nsv, isv;
-      choose_scale<MF, SMODE>(am, nsm, ism);
-      choose_scale<VF, SMODE>(av, nsv, isv);
-      if constexpr (STATS) {
-        if (ex[j]) {
-          tam = max(tam, am);
-          tav = max(tav, av);
-          tsm = fmaxf(tsm, nsm);
-          tsv = fmaxf(tsv, nsv);
-        }
-      }
-      float qm[4], qv[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = param_update(c, p[r], m1[r], v1[r]);
-        qm[r] = m1[r] * ism;
-        qv[r] = v1[r] * isv;
-      }
-      if (full[j]) {
-        uint32_t rw[4];
-        sr_words<SR>(c, tid, i0, rw);
-        const uint32_t wm = quant4<MF, SR, false>(qm, rw);
-        const uint32_t wv = quant4<VF, SR, true>(qv, rw);
-        if constexpr (STATS) {
-#pragma unroll
-          for (int r = 0; r < 4; r++)
-            count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], wm >> (8 * r), wv >> (8 * r));
-        }
-        store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i0, p);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i0, wm);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i0, wv);
-      } else if (ex[j]) {
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int64_t i = i0 + r;
-          if (i < end) {
-            const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm[r]), cv = quant1<VF, SR, true>(c, tid, i, qv[r]);
-            count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], cm, cv);
-            store_p1<BF16P>(d, i, p[r]);
-            st_global<uint8_t>(d.m + i, (uint8_t)cm);
-            st_global<uint8_t>(d.v + i, (uint8_t)cv);
-          }
-        }
-      }
-      if (ex[j] && hl == 0) {
-        st_global<float>(d.sm + b0[j] / kBlock, nsm);
-        st_global<float>(d.sv + b0[j] / kBlock, nsv);
-      }
-    }
-  }
-  if constexpr (STATS) {
-    flush_counters<STATS>(counters, tid, cnt);
-    uint32_t sa = __float_as_uint(tsm), sb = __float_as_uint(tsv);
-    uint32_t a = wave_max(tam), b = wave_max(tav);
-    sa = wave_max(sa);
-    sb = wave_max(sb);
-    if (lane == 0) {
-      if (a) atomicMax(&amax[4 * tid], a);
-      if (b) atomicMax(&amax[4 * tid + 1], b);
-      if (sa) atomicMax(&amax[4 * tid + 2], sa);
-      if (sb) atomicMax(&amax[4 * tid + 3], sb);
-    }
-  }
-}
-
 // ------------------------------------------------------------- codec probes
 
 template <int FMT>
@@ -1246,60 +229,6 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
     out[i] = decode1<FMT>(codes[i]);
 }
 
-// ================================================================== host side
-
-thread_local std::string g_last_error;
-
-int fail(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(FP8ADAM_EHIP, std::string(what) + ": " + hipGetErrorString(e));
-}
-
-#define HIP_TRY(expr)                                    \
-  do {                                                   \
-    hipError_t e_ = (expr);                              \
-    if (e_ != hipSuccess) return hip_fail(e_, #expr);    \
-  } while (0)
-
-constexpr int kMaxTimed = 4096;
-
-}  // namespace
-
-struct fp8adam_ctx {
-  int device = 0;
-  fp8adam_config cfg{};
-  int32_t n = 0;
-  int64_t nchunks = 0;
-  int chunk_log2 = kMaxChunkLog2;  // elements per chunk = 2^chunk_log2
-  int speculate_from = 4;          // first step t that runs the speculative schedule
-  int hist_len = 0;                // delayed scaling: amax history length H (0: just in time)
-  int delayed_from = 2;            // delayed scaling: first step t quantized with the delayed scale
-  float margin_scale = 1.0f;       // delayed scaling: 2^margin
-  int cur = 0;                     // code buffer holding the moments: 0 = m/v, 1 = m_alt/v_alt
-  int64_t nparts = 0;              // update / block work-groups
-  TensorDesc* d_desc = nullptr;    // [2][n]: descriptors with m/v, then with m_alt/v_alt
-  int32_t* d_chunk_tid = nullptr;
-  uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
-  uint2* d_partial = nullptr;       // tensor mode: [nchunks] per-chunk amax of m', v'
-  uint2* d_part_amax = nullptr;     // speculative: [nparts] per-part amax of m', v'
-  float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
-  int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
-  unsigned long long* d_counters = nullptr;  // [n][5]
-  double* d_gpart = nullptr;        // loss scaling: [norm groups][2] sum of squares and Inf/NaN count of g
-  GradCtl* d_gctl = nullptr;        // loss scaling: the decision of the step in flight
-  const GradCtl* gctl = nullptr;    // d_gctl during fp8adam_step_amp, else null
-  bool timing = false;
-  std::vector<hipEvent_t> ev;  // pairs
-  std::vector<int> ev_kind;
-  int ev_used = 0;
-};
-
-namespace {
-
 bool valid_fmt(int32_t f) { return f == FP8ADAM_E4M3 || f == FP8ADAM_E5M2; }
 
 int check_aligned(const void* p, const char* what, int32_t t) {
@@ -1322,153 +251,6 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_gctl) (void)hipFree(c->d_gctl);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
   delete c;
-}
-
-int timed_begin(fp8adam_ctx* c, int kind, hipStream_t s, int* slot) {
-  *slot = -1;
-  if (!c->timing || c->ev_used >= kMaxTimed) return 0;
-  *slot = c->ev_used++;
-  c->ev_kind[*slot] = kind;
-  HIP_TRY(hipEventRecord(c->ev[2 * *slot], s));
-  return 0;
-}
-
-int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
-  if (slot < 0) return 0;
-  HIP_TRY(hipEventRecord(c->ev[2 * slot + 1], s));
-  return 0;
-}
-
-// ---- kernel dispatch over the template parameters ----
-
-const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d_desc + (size_t)which * c->n; }
-
-template <int MF, int VF, bool BF16P, bool L2>
-void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_amax<MF, VF, BF16P && L2, L2>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks, c->gctl);
-}
-
-template <int MF, int VF, int SMODE, bool STATS>
-void launch_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
-                     c->d_flags, k.hist_len, k.hist_slot, c->gctl);
-}
-
-template <int MF, int VF, int SMODE>
-void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl);
-}
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
-void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
-                     descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nparts, c->gctl);
-}
-
-template <int MF, int VF, bool STATS>
-void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, k, c->gctl);
-}
-
-template <int MF, int VF, bool STATS, bool SR>
-void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_fixup<MF, VF, STATS, SR>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
-                     c->d_counters, c->chunk_log2, c->nchunks, c->gctl);
-}
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
-void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
-                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts, c->gctl);
-}
-
-// Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
-// 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up,
-// 8 delayed pass, 9 delayed commit, 10 gradient-norm pass, 11 loss-scale decision.
-#define TIMED(kind, call)                              \
-  do {                                                 \
-    int slot_;                                         \
-    if (int r_ = timed_begin(c, (kind), s, &slot_)) return r_; \
-    call;                                              \
-    if (int r_ = timed_end(c, slot_, s)) return r_;    \
-  } while (0)
-
-void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
-  hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
-                     dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
-}
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
-int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  bool done = false;
-  if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
-    if (STATS) TIMED(4, launch_reset(c, 4 * (int64_t)c->n, s));
-    if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE, L2, SR>(c, k, s)));
-    done = true;
-  }
-  // (fp8adam_init refuses the speculative schedule with coupled L2 or AMAX scales:
-  // the fix-up recomputes moments after p has been overwritten, and g_eff needs the old p)
-  if constexpr (!L2 && SMODE == 0) {
-    if (!done && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
-      if (STATS) TIMED(4, launch_reset(c, 0, s));
-      if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
-      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
-      if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
-      c->cur = 1 - c->cur;
-      done = true;
-    }
-  }
-  if (!done && c->hist_len > 0 && t >= c->delayed_from) {
-    if (STATS) TIMED(4, launch_reset(c, 0, s));
-    if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2, SR>(c, k, s)));
-    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, s)));
-  } else if (!done) {
-    if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
-    // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
-    TIMED(2, (launch_reduce<MF, VF, SMODE, STATS>(c, k, s)));
-    if (c->nchunks > 0) TIMED(1, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeJit, L2, SR>(c, k, s)));
-  }
-  HIP_TRY(hipGetLastError());
-  return 0;
-}
-
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2>
-int run_step_r(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return c->cfg.rounding == FP8ADAM_ROUND_STOCHASTIC ? run_step_t<MF, VF, BF16P, STATS, SMODE, L2, true>(c, k, t, s)
-                                                     : run_step_t<MF, VF, BF16P, STATS, SMODE, L2, false>(c, k, t, s);
-}
-
-// Coupled L2 with weight_decay 0 is plain Adam: it runs the kernels without
-// the extra term (which would also turn a -0 gradient into +0).
-template <int MF, int VF, bool BF16P, bool STATS, int SMODE>
-int run_step_l(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return k.l2 != 0.0f ? run_step_r<MF, VF, BF16P, STATS, SMODE, true>(c, k, t, s)
-                      : run_step_r<MF, VF, BF16P, STATS, SMODE, false>(c, k, t, s);
-}
-
-template <int MF, int VF, bool BF16P, bool STATS>
-int run_step_s(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return c->cfg.scale_mode == FP8ADAM_SCALE_POW2 ? run_step_l<MF, VF, BF16P, STATS, 0>(c, k, t, s)
-                                                 : run_step_l<MF, VF, BF16P, STATS, 1>(c, k, t, s);
-}
-
-template <int MF, int VF, bool BF16P>
-int run_step_b(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return c->cfg.collect_stats ? run_step_s<MF, VF, BF16P, true>(c, k, t, s)
-                              : run_step_s<MF, VF, BF16P, false>(c, k, t, s);
-}
-
-template <int MF, int VF>
-int run_step_f(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
-  return c->cfg.master == FP8ADAM_MASTER_BF16 ? run_step_b<MF, VF, true>(c, k, t, s)
-                                              : run_step_b<MF, VF, false>(c, k, t, s);
 }
 
 int64_t norm_groups(const fp8adam_ctx* c) { return std::min<int64_t>(c->nchunks, kNormGroups); }
