@@ -1,0 +1,138 @@
+"""Invariants of the options (delayed scaling, loss scaling, stochastic
+rounding) that need no oracle: resuming from a checkpoint of the whole
+optimizer state is bit-exact, and a loss-scaled step with scale 1 and no
+clipping is the plain step, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_adam_optimizer_amd as pk
+from tests.gpu_util import np_host, random_grad
+
+pytestmark = pytest.mark.gpu
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+SIZES = [50_001, 4096, 777]
+
+
+def _params(seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return [torch.randn(n, generator=g, device="cuda") * 0.02 for n in SIZES]
+
+
+def _load(grads, t, scale=1.0, inf_at=None):
+    for i, n in enumerate(SIZES):
+        x = random_grad(n, 100 * t + i, "cuda", lo=-6.0, hi=-1.0).float() * scale
+        if inf_at == t and i == 1:
+            x[3] = float("inf")
+        grads[i].copy_(x.to(torch.bfloat16))
+
+
+def _snapshot(params, opt, amp):
+    out = [np_host(x) for x in params + opt.m + opt.v + opt.m_scale + opt.v_scale]
+    if opt.amax_history[0] is not None:
+        out += [np_host(h) for h in opt.amax_history]
+    if amp is not None:
+        out.append(np_host(amp))
+    return out
+
+
+def _same(a, b):
+    assert len(a) == len(b)
+    for k, (x, y) in enumerate(zip(a, b)):
+        assert x.tobytes() == y.tobytes(), f"array {k} differs"
+
+
+CASES = [
+    dict(schedule="speculative", rounding="stochastic", amp=True),
+    dict(scaling="delayed", rounding="stochastic", amp=True),
+    dict(scaling="delayed", amp=False),
+    dict(schedule="two_pass", rounding="stochastic", amp=False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["spec_sr_amp", "delayed_sr_amp", "delayed", "twopass_sr"])
+def test_resume_with_options_is_bit_exact(case):
+    """Six calls in one context against three, a checkpoint of every piece of
+    state (weights, codes, scales, amax history, loss-scaler state), a new
+    context built from it, and three more calls; an overflow at call 2."""
+    amp_on = case.get("amp", False)
+    kw = dict(schedule=case.get("schedule", "two_pass"), scaling=case.get("scaling", "just_in_time"),
+              rounding=case.get("rounding", "nearest"), seed=77, amax_history_len=4, speculate_from_step=2)
+
+    def call(opt, amp, t, grads):
+        if amp_on:
+            opt.step_amp(amp, step=t, max_norm=0.5, growth_interval=2, **HP)
+        else:
+            opt.step(step=t, **HP)
+
+    def scale_of(amp):
+        return pk.read_amp_state(amp)["scale"] if amp is not None else 1.0
+
+    params = _params(1)
+    grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in SIZES]
+    opt = pk.FP8AdamW(params, grads, **kw)
+    amp = pk.amp_state(2.0 ** 10) if amp_on else None
+    for t in range(1, 7):
+        _load(grads, t, scale_of(amp), inf_at=2 if amp_on else None)
+        call(opt, amp, t, grads)
+    torch.cuda.synchronize()
+    ref = _snapshot(params, opt, amp)
+    opt.close()
+
+    params = _params(1)
+    opt = pk.FP8AdamW(params, grads, **kw)
+    amp = pk.amp_state(2.0 ** 10) if amp_on else None
+    for t in range(1, 4):
+        _load(grads, t, scale_of(amp), inf_at=2 if amp_on else None)
+        call(opt, amp, t, grads)
+    torch.cuda.synchronize()
+    state = [[x.clone() for x in opt.m], [x.clone() for x in opt.v], [x.clone() for x in opt.m_scale],
+             [x.clone() for x in opt.v_scale]]
+    if kw["scaling"] == "delayed":
+        state.append([x.clone() for x in opt.amax_history])
+    p2 = [p.clone() for p in params]
+    amp2 = amp.clone() if amp_on else None
+    opt.close()
+    opt2 = pk.FP8AdamW(p2, grads, state=state, **kw)
+    for t in range(4, 7):
+        _load(grads, t, scale_of(amp2), inf_at=None)
+        call(opt2, amp2, t, grads)
+    torch.cuda.synchronize()
+    out = _snapshot(p2, opt2, amp2)
+    opt2.close()
+    _same(ref, out)
+
+
+def test_amp_with_unit_scale_and_no_clipping_is_the_plain_step():
+    """Scale 1, no clipping, no overflow: the gradient factor is exactly 1 and
+    the device-side step count equals the caller's t, so the codes and scales
+    match the plain step bit for bit.  The weights may differ by one fp32 ulp:
+    with loss scaling the bias corrections are computed on the device (its
+    double-precision pow, not the host's)."""
+    for kw in (dict(schedule="speculative", speculate_from_step=2), dict(rounding="stochastic", seed=5)):
+        outs = []
+        for amp_on in (False, True):
+            params = _params(2)
+            grads = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in SIZES]
+            opt = pk.FP8AdamW(params, grads, **kw)
+            amp = pk.amp_state(1.0) if amp_on else None
+            for t in range(1, 6):
+                _load(grads, t)
+                if amp_on:
+                    opt.step_amp(amp, step=t, max_norm=0.0, **HP)
+                else:
+                    opt.step(step=t, **HP)
+            torch.cuda.synchronize()
+            outs.append([np_host(x) for x in params + opt.m + opt.v + opt.m_scale + opt.v_scale])
+            if amp_on:
+                st = pk.read_amp_state(amp)
+                assert st["step"] == 5 and st["grad_factor"] == 1.0 and st["clip_coef"] == 1.0
+            opt.close()
+        k = len(SIZES)
+        _same(outs[0][k:], outs[1][k:])
+        for a, b in zip(outs[0][:k], outs[1][:k]):
+            ia, ib = a.view(np.int32).astype(np.int64), b.view(np.int32).astype(np.int64)
+            assert np.abs(ia - ib).max() <= 1
