@@ -282,6 +282,7 @@ class FP8AdamW:
             state = (m, v, ms, vs)
         m, v, self.m_scale, self.v_scale = [list(x) for x in state[:4]]
         delayed = _SCALING[scaling] == SCALING_DELAYED
+        amax_history_len = int(amax_history_len) if int(amax_history_len) > 0 else 16  # the library's default
         if delayed and len(state) > 4:
             self.amax_history = list(state[4])
         elif delayed:
@@ -300,6 +301,16 @@ class FP8AdamW:
             for t in (p, g, m[i], v[i], self.m_scale[i], self.v_scale[i]):
                 if not t.is_contiguous() or t.device != p.device:
                     raise ValueError(f"tensor {i}: every buffer must be contiguous on one device")
+            # the kernels read and write these sizes through plain pointers: check them here
+            n, ns = p.numel(), self.num_scales(p.numel())
+            if any(x.dtype != torch.uint8 or x.numel() != n for x in (m[i], v[i])):
+                raise ValueError(f"tensor {i}: moment codes must be uint8 with one byte per element")
+            if any(x.dtype != torch.float32 or x.numel() < ns for x in (self.m_scale[i], self.v_scale[i])):
+                raise ValueError(f"tensor {i}: scales must be float32, at least {ns} of them")
+            h = self.amax_history[i]
+            if delayed and (h.dtype != torch.float32 or h.numel() != 2 * amax_history_len
+                            or not h.is_contiguous() or h.device != p.device):
+                raise ValueError(f"tensor {i}: amax_history must be {2 * amax_history_len} contiguous float32")
             args.append(TensorArg(p.data_ptr(), g.data_ptr(), m[i].data_ptr(), v[i].data_ptr(),
                                   self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel(),
                                   _ptr(m_alt[i]), _ptr(v_alt[i]), _ptr(self.amax_history[i])))

@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import precision_adam_optimizer_amd as pk
 
@@ -118,3 +119,22 @@ def test_speculative_schedule_argument_errors():
     misaligned = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10, 113, 128))
     assert L.fp8adam_init(ctypes.byref(h), misaligned, 1, ctypes.byref(cfg), None) == -2
     assert L.fp8adam_current_buffer(None) == -1
+
+
+def test_binding_checks_state_sizes_before_the_library():
+    """The kernels read and write the moment codes, scales and amax history
+    through plain pointers, so the binding refuses buffers of the wrong size
+    or dtype (these checks run before any device work)."""
+    p, g = [torch.zeros(10)], [torch.zeros(10, dtype=torch.bfloat16)]
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    cases = [
+        ((u8(9), u8(10), torch.ones(1), torch.ones(1)), {}, "codes"),
+        ((u8(10), u8(10), torch.ones(1, dtype=torch.float64), torch.ones(1)), {}, "scales"),
+        ((u8(10), u8(10), torch.ones(1), torch.ones(1), torch.zeros(7)),
+         dict(scaling="delayed", amax_history_len=4), "amax_history"),
+        ((u8(10), u8(10), torch.ones(1), torch.ones(1), torch.zeros(8)),
+         dict(scaling="delayed", amax_history_len=0), "amax_history"),  # 0 means 16: 32 floats
+    ]
+    for st, kw, what in cases:
+        with pytest.raises(ValueError, match=what):
+            pk.FP8AdamW(p, g, state=tuple([x] for x in st), **kw)
