@@ -247,6 +247,12 @@ int fp8adam_decode(int32_t fmt, const uint8_t *codes, float *out, int64_t n, hip
 int fp8adam_encode_bits_range(int32_t fmt, uint32_t start, int64_t count, uint8_t *out,
                               hipStream_t stream);
 
+/* out[i] = stochastic-rounding encode of the fp32 with bit pattern start + i, with the 16
+ * random bits r16 (< 2^16) for every value: the rounding FP8ADAM_ROUND_STOCHASTIC applies to
+ * each moment value.  count <= 2^32 - start; out: device, count bytes. */
+int fp8adam_encode_sr_bits_range(int32_t fmt, uint32_t start, int64_t count, uint32_t r16, uint8_t *out,
+                                 hipStream_t stream);
+
 /* ---- measurement ---- */
 
 /* Enable (1) or disable (0) per-kernel timing with HIP events around every

@@ -119,6 +119,7 @@ def lib() -> ctypes.CDLL:
         L.ref_encode_sr.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_uint32]
         L.ref_encode_sr.restype = ctypes.c_uint8
         L.ref_philox4x32_10.argtypes = [P, P, P]
+        L.ref_encode_sr_bits_range.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_int64, ctypes.c_uint32, u8p]
         L.ref_sr_word.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64]
         L.ref_sr_word.restype = ctypes.c_uint32
         L.ref_grad_sumsq.argtypes = [u16p, ctypes.c_int64, P, ctypes.POINTER(ctypes.c_int64)]
@@ -273,6 +274,14 @@ def amp_control(sums: GradSums, cfg: AmpConfig, state: AmpState) -> AmpState:
 def encode_sr(fmt, x: float, r16: int) -> int:
     """Stochastic rounding of one value with 16 random bits."""
     return lib().ref_encode_sr(fmt_id(fmt), x, r16)
+
+
+def encode_sr_bits_range(fmt, start: int, count: int, r16: int, out: np.ndarray | None = None) -> np.ndarray:
+    """Stochastic-rounding encode of the fp32 patterns start .. start+count-1 with one r16."""
+    out = np.empty(count, dtype=np.uint8) if out is None else out
+    assert out.dtype == np.uint8 and out.size >= count and out.flags["C_CONTIGUOUS"]
+    lib().ref_encode_sr_bits_range(fmt_id(fmt), start, count, r16, _ptr(out))
+    return out
 
 
 def philox4x32_10(ctr, key) -> list:

@@ -206,6 +206,13 @@ uint8_t ref_encode_sr(int fmt, float x, uint32_t r16)
     return ref_encode(fmt, (float)copysign(mag, (double)x)); /* an FP8 value: exact */
 }
 
+/* Stochastic-rounding encode of every fp32 bit pattern in [start, start+count) with one
+ * fixed r16; used to compare against a device sweep. */
+void ref_encode_sr_bits_range(int fmt, uint32_t start, int64_t count, uint32_t r16, uint8_t *out)
+{
+    for (int64_t i = 0; i < count; i++) out[i] = ref_encode_sr(fmt, u2f(start + (uint32_t)i), r16);
+}
+
 /* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
  * as 1, 2, 3", SC 2011): ten rounds of two 32x32->64 multiplies with the
  * round constants below, the key bumped by the Weyl constants between rounds. */

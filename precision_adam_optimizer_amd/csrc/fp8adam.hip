@@ -222,6 +222,23 @@ __global__ __launch_bounds__(kThreads) void k_encode_bits(uint32_t start, int64_
 }
 
 template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_encode_sr_bits(uint32_t start, int64_t count, uint32_t r16,
+                                                             uint8_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  const uint32_t r[4] = {r16, r16, r16, r16};
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < count; i += stride) {
+    const uint32_t b = start + (uint32_t)i;
+    if (i + 4 <= count && (((uintptr_t)(out + i)) & 3) == 0) {
+      *reinterpret_cast<uint32_t*>(out + i) = encode4_sr<FMT>(__uint_as_float(b), __uint_as_float(b + 1u),
+                                                              __uint_as_float(b + 2u), __uint_as_float(b + 3u), r);
+    } else {
+      for (int64_t k = i; k < count && k < i + 4; k++)
+        out[k] = (uint8_t)(encode4_sr<FMT>(__uint_as_float(start + (uint32_t)k), 0.0f, 0.0f, 0.0f, r) & 0xFFu);
+    }
+  }
+}
+
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__ codes, float* __restrict__ out,
                                                      int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -621,6 +638,22 @@ int fp8adam_decode(int32_t fmt, const uint8_t* codes, float* out, int64_t n, hip
     hipLaunchKernelGGL(k_decode<0>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, codes, out, n);
   else
     hipLaunchKernelGGL(k_decode<1>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, codes, out, n);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_encode_sr_bits_range(int32_t fmt, uint32_t start, int64_t count, uint32_t r16, uint8_t* out,
+                                 hipStream_t stream) {
+  if (!valid_fmt(fmt) || count < 0 || count > ((int64_t)1 << 32) - (int64_t)start || r16 > 0xFFFFu ||
+      (count > 0 && !out))
+    return fail(FP8ADAM_EINVAL, "bad argument");
+  if (count == 0) return 0;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_encode_sr_bits<0>, dim3(probe_grid(count, 4)), dim3(kThreads), 0, stream, start, count, r16,
+                       out);
+  else
+    hipLaunchKernelGGL(k_encode_sr_bits<1>, dim3(probe_grid(count, 4)), dim3(kThreads), 0, stream, start, count, r16,
+                       out);
   HIP_TRY(hipGetLastError());
   return 0;
 }

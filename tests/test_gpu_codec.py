@@ -2,6 +2,7 @@
 used by the step kernels) against the oracle codec: all 256 codes decoded,
 all 2^32 fp32 bit patterns encoded, through the C ABI."""
 import concurrent.futures as cf
+import os
 
 import numpy as np
 import pytest
@@ -76,3 +77,36 @@ def test_encode_all_fp32_bit_patterns(fmt):
                 i = int(np.nonzero(diff)[0][0])
                 first = (s + i, int(got[i]), int(want[i]))
     assert mismatches == 0, f"{mismatches} mismatches; first bits {first[0]:#010x}: gpu {first[1]:#04x} oracle {first[2]:#04x}"
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_encode_sr_matches_oracle_over_the_fp8_range(fmt):
+    """The device's stochastic-rounding encode (the one the step kernels use)
+    equals the oracle's for every fp32 pattern from 2^-24 to just past FMAX,
+    both signs, for five values of the 16 random bits; and for the smallest
+    patterns (fp32 subnormals) with all random bits set."""
+    lo = 0x33800000                                   # 2^-24
+    hi = {0: 0x43E40000, 1: 0x47680000}[fmt]          # a little above 448 / 57344
+    threads = max(1, min(16, os.cpu_count() or 1))
+    ranges = [(s | lo, hi - lo, r) for s in (0, 0x80000000) for r in (0, 0x3A5C, 0x7FFF, 0x8000, 0xFFFF)]
+    ranges += [(0, 1 << 20, 0xFFFF), (0x80000000, 1 << 20, 0xFFFF)]
+    out = torch.empty(max(c for _, c, _ in ranges), dtype=torch.uint8, device="cuda")
+    for start, count, r16 in ranges:
+        pk.fp8adam_encode_sr_bits_range(fmt, start, count, r16, out)
+        got = out[:count].cpu().numpy()
+        want = np.empty(count, np.uint8)
+        step = -(-count // threads)
+
+        def work(k):
+            a = k * step
+            b = min(count, a + step)
+            if a < b:
+                oracle.encode_sr_bits_range(fmt, start + a, b - a, r16, want[a:b])
+
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(threads)))
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (f"fmt {fmt} r16 {r16:#06x}: {bad.size} codes differ, first at pattern "
+                               f"{start + int(bad[0]):#010x}: gpu {got[bad[0]]:#04x} oracle {want[bad[0]]:#04x}")
+        print(f"sr sweep fmt {fmt} start {start:#010x} count {count} r16 {r16:#06x}: equal", flush=True)
