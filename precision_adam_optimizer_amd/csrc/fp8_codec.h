@@ -77,33 +77,38 @@ __device__ __forceinline__ uint32_t encode1(float a) {
 // rounding against the error that accumulates over many updates).  q is
 // already clamped to [-FMAX, FMAX].  Its FP8 neighbours are lo and lo + s,
 // s = the FP8 spacing at |q| (fixed below the smallest normal); with
-// f = (|q| - lo) / s, q rounds up iff floor(f * 2^16) + r16 >= 2^16.  Every
-// step is exact in fp32 (scaling by powers of two, truncation, the fraction
-// of a value with at most 24 significant bits), so the result is an FP8 value
-// and the round-to-nearest convert that follows leaves it unchanged.
+// f = (|q| - lo) / s, q rounds up iff floor(f * 2^16) + r16 >= 2^16.
+// Integer form, straight to the code: the significand (implicit bit set) is
+// shifted so that the FP8 spacing sits at bit 16, i.e. to |q| / s in fixed
+// point with 16 fraction bits (the shift is 7 - MB in the normal range and
+// larger below it; fp32 subnormals shift out entirely); adding r16 carries
+// into bit 16 exactly when the rounding goes up, so the top bits are the
+// chosen neighbour in units of s, and the code is that count plus the
+// exponent offset of the binade (a carry past the binade's last code lands
+// on the next binade's first, as the code layout requires).
 template <int FMT>
-__device__ __forceinline__ float sr_round(float q, uint32_t r16) {
-  const float a = fabsf(q);
-  const int ef = (int)(__float_as_uint(a) >> 23);
-  const int ex = ef > Format<FMT>::kMinNormalField ? ef : Format<FMT>::kMinNormalField;
-  const float spacing = __uint_as_float((uint32_t)(ex - Format<FMT>::kMantBits) << 23);
-  const float inv_spacing = __uint_as_float((uint32_t)(254 - (ex - Format<FMT>::kMantBits)) << 23);
-  const float units = a * inv_spacing;
-  const float lo = __builtin_truncf(units);
-  const uint32_t d = (uint32_t)((units - lo) * 65536.0f);
-  const float mag = (d + r16 >= 65536u ? lo + 1.0f : lo) * spacing;
-  return __builtin_copysignf(mag, q);
+__device__ __forceinline__ uint32_t sr_code(float q, uint32_t r16) {
+  constexpr int MB = Format<FMT>::kMantBits;
+  constexpr int MINF = Format<FMT>::kMinNormalField;
+  const uint32_t u = __float_as_uint(q);
+  const int e = (int)((u >> 23) & 0xFFu);
+  const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
+  const int sh = min(max(MINF + 7 - MB - e, 7 - MB), 31);
+  const uint32_t units = ((sig >> sh) + r16) >> 16;
+  const uint32_t mag = ((uint32_t)max(e - MINF, 0) << MB) + units;
+  const uint32_t sign = (u >> 24) & 0x80u;
+  return sign | (e == 0xFF ? 0x7Fu : mag);  // a NaN keeps the NaN code
 }
 
 // Four floats -> four codes with stochastic rounding; r16[j] are 16 random bits each.
 template <int FMT>
 __device__ __forceinline__ uint32_t encode4_sr(float a, float b, float c, float d, const uint32_t (&r16)[4]) {
   constexpr float M = Format<FMT>::kMax;
-  a = sr_round<FMT>(__builtin_amdgcn_fmed3f(a, -M, M), r16[0]);
-  b = sr_round<FMT>(__builtin_amdgcn_fmed3f(b, -M, M), r16[1]);
-  c = sr_round<FMT>(__builtin_amdgcn_fmed3f(c, -M, M), r16[2]);
-  d = sr_round<FMT>(__builtin_amdgcn_fmed3f(d, -M, M), r16[3]);
-  return encode4<FMT>(a, b, c, d);
+  const uint32_t c0 = sr_code<FMT>(__builtin_amdgcn_fmed3f(a, -M, M), r16[0]);
+  const uint32_t c1 = sr_code<FMT>(__builtin_amdgcn_fmed3f(b, -M, M), r16[1]);
+  const uint32_t c2 = sr_code<FMT>(__builtin_amdgcn_fmed3f(c, -M, M), r16[2]);
+  const uint32_t c3 = sr_code<FMT>(__builtin_amdgcn_fmed3f(d, -M, M), r16[3]);
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
