@@ -349,12 +349,12 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       if (cfg->margin < 0 || cfg->margin > 64) return fail(FP8ADAM_EINVAL, "margin must lie in [0, 64]");
     }
 
-    // Chunk size: the largest power of two in [kPart, 2^kMaxChunkLog2] that still
+    // Chunk size: the largest power of two in [2^kMinChunkLog2, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
     int64_t total = 0;
     for (int32_t t = 0; t < n; t++) total += tensors[t].numel > 0 ? tensors[t].numel : 0;
     int chunk_log2 = kMaxChunkLog2;
-    while (chunk_log2 > kPartLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
+    while (chunk_log2 > kMinChunkLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
     const int64_t chunk = (int64_t)1 << chunk_log2;
 
     std::vector<TensorDesc> desc(2 * (size_t)n);  // [m/v set][m_alt/v_alt set]
@@ -393,7 +393,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         desc[(size_t)n + t].m = T.m_alt;
         desc[(size_t)n + t].v = T.v_alt;
       }
-      if (((nchunks + nc) << (chunk_log2 - kPartLog2)) > (int64_t)INT32_MAX)
+      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2))) > (int64_t)INT32_MAX)
         return fail(FP8ADAM_EINVAL, "too many elements for one context");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
       nchunks += nc;
@@ -406,6 +406,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->nchunks = nchunks;
     c->chunk_log2 = chunk_log2;
     c->nparts = nchunks << (chunk_log2 - kPartLog2);
+    c->nuparts = nchunks << (chunk_log2 - kUPartLog2);
     c->speculate_from = cfg->speculate_from_step > 0 ? cfg->speculate_from_step : 4;
     c->hist_len = delayed ? hist_len : 0;
     c->delayed_from = cfg->delayed_from_step > 0 ? cfg->delayed_from_step : 2;
@@ -413,7 +414,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     hipError_t e = hipGetDevice(&c->device);
     const size_t namax = (size_t)n * 4;
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * 2 * (size_t)n);
-    if (e == hipSuccess && (spec || delayed)) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nparts));
+    if (e == hipSuccess && (spec || delayed)) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nuparts));
     if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
