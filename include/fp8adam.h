@@ -264,7 +264,8 @@ int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
  * 6 = speculative scale check, 7 = re-quantization fix-up, 8 = delayed-scaling pass,
- * 9 = delayed-scaling commit, 10 = gradient-norm pass, 11 = loss-scale decision),
+ * 9 = delayed-scaling commit, 10 = gradient-norm pass, 11 = loss-scale decision,
+ * 12 = scale preparation of the speculative and delayed passes),
  * total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);

@@ -36,7 +36,8 @@ _ROUNDING = {"nearest": ROUND_NEAREST, "stochastic": ROUND_STOCHASTIC}
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
-                "spec_check", "fixup", "delayed_pass", "delayed_commit", "gradnorm_pass", "amp_decision")
+                "spec_check", "fixup", "delayed_pass", "delayed_commit", "gradnorm_pass", "amp_decision",
+                "scale_prepare")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",

@@ -419,7 +419,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
-    if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 2 * (size_t)n);
+    if (e == hipSuccess) e = hipMalloc(&c->d_old_scale, sizeof(float) * 4 * (size_t)n);
     if (e == hipSuccess) e = hipMalloc(&c->d_counters, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor);
     if (e == hipSuccess)
       e = hipMalloc(&c->d_gpart, 2 * sizeof(double) * (size_t)std::max<int64_t>(1, std::min<int64_t>(nchunks, kNormGroups)));

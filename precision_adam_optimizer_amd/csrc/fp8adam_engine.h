@@ -603,16 +603,17 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   }
   float sm, sv, ism, isv;
   if constexpr (SPEC) {
-    sm = ld_global<float>(d.sm);
-    sv = ld_global<float>(d.sv);
-    ism = inverse_pow2(predicted_scale_bits<MF>(amax[2 * tid], sm, c.grow_m));
-    isv = inverse_pow2(predicted_scale_bits<VF>(amax[2 * tid + 1], sv, c.grow_v));
+    // prepared per tensor by k_spec_prepare: [old s_m, old s_v, predicted s_m, predicted s_v]
+    sm = old_scale[4 * tid];
+    sv = old_scale[4 * tid + 1];
+    ism = inverse_pow2(__float_as_uint(old_scale[4 * tid + 2]));
+    isv = inverse_pow2(__float_as_uint(old_scale[4 * tid + 3]));
   } else if constexpr (MODE == kModeDelayed) {
-    float unused;
+    // the delayed scales, prepared per tensor by k_delayed_prepare: [s_m, s_v, inv_m, inv_v]
     sm = ld_global<float>(d.sm);
     sv = ld_global<float>(d.sv);
-    delayed_scale<MF, SMODE>(d.hist, c, unused, ism);
-    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, unused, isv);
+    ism = old_scale[4 * tid + 2];
+    isv = old_scale[4 * tid + 3];
   } else {
     float nsm, nsv;
     sm = old_scale[2 * tid];
@@ -694,11 +695,33 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
 // did (before the history changes), thread 0 commits them and records this
 // step's amax in the history slot.
 
+// One wave per tensor, before the delayed pass: the tensor's delayed scales
+// from its amax history, into prep[4t..4t+3] = [s_m, s_v, inv_m, inv_v], so
+// the pass and the commit read them instead of reducing the history in every
+// work-group.
+template <int MF, int VF, int SMODE>
+__global__ __launch_bounds__(64) void k_delayed_prepare(const TensorDesc* __restrict__ descs, StepConsts c,
+                                                        float* __restrict__ prep) {
+  const int t = blockIdx.x;
+  const TensorDesc d = descs[t];
+  if (d.numel == 0) return;  // uniform: the whole wave
+  float s_m, s_v, i_m, i_v;
+  delayed_scale<MF, SMODE>(d.hist, c, s_m, i_m);
+  delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, s_v, i_v);
+  if (threadIdx.x == 0) {
+    st_global<float>(prep + 4 * t, s_m);
+    st_global<float>(prep + 4 * t + 1, s_v);
+    st_global<float>(prep + 4 * t + 2, i_m);
+    st_global<float>(prep + 4 * t + 3, i_v);
+  }
+}
+
 template <int MF, int VF, int SMODE>
 __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorDesc* __restrict__ descs,
                                                                    const uint2* __restrict__ part_amax,
                                                                    uint32_t* __restrict__ amax, StepConsts c,
-                                                                   int chunk_log2, const GradCtl* __restrict__ gctl) {
+                                                                   int chunk_log2, const GradCtl* __restrict__ gctl,
+                                                                   const float* __restrict__ prep) {
   if (amp_apply(gctl, c)) return;  // skipped step: scales, amax and history stay
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
@@ -720,9 +743,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorD
   }
   __syncthreads();
   if (wave == 0 && d.numel > 0) {  // uniform: all of wave 0, or none
-    float s_m, s_v, inv;
-    delayed_scale<MF, SMODE>(d.hist, c, s_m, inv);
-    delayed_scale<VF, SMODE>(d.hist + c.hist_len, c, s_v, inv);
+    const float s_m = prep[4 * t], s_v = prep[4 * t + 1];  // the scales the pass quantized with
     if (lane == 0) {
       for (int w = 1; w < kReduceThreads / 64; w++) {
         am = max(am, red[0][w]);
@@ -748,6 +769,25 @@ __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorD
 // are staged for the fix-up, the true scales committed; a flagged tensor's
 // stats counters are cleared (the fix-up recounts them).
 
+// One thread per tensor, before the speculative pass: stage the old scales
+// and the predicted ones in prep[4t..4t+3] = [s_m, s_v, pred s_m, pred s_v]
+// (the pass, the check and the fix-up all read them from there).
+template <int MF, int VF>
+__global__ __launch_bounds__(64) void k_spec_prepare(const TensorDesc* __restrict__ descs,
+                                                     const uint32_t* __restrict__ amax, StepConsts c,
+                                                     const GradCtl* __restrict__ gctl, float* __restrict__ prep,
+                                                     int32_t n) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= n || amp_apply(gctl, c)) return;
+  const TensorDesc d = descs[t];
+  if (d.numel == 0) return;
+  const float so_m = ld_global<float>(d.sm), so_v = ld_global<float>(d.sv);
+  st_global<float>(prep + 4 * t, so_m);
+  st_global<float>(prep + 4 * t + 1, so_v);
+  st_global<uint32_t>(prep + 4 * t + 2, predicted_scale_bits<MF>(amax[2 * t], so_m, c.grow_m));
+  st_global<uint32_t>(prep + 4 * t + 3, predicted_scale_bits<VF>(amax[2 * t + 1], so_v, c.grow_v));
+}
+
 template <int MF, int VF, bool STATS>
 __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc* __restrict__ descs,
                                                                 const uint2* __restrict__ part_amax,
@@ -762,7 +802,6 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     if (threadIdx.x == 0) flags[t] = 0;
     return;
   }
-  const float grow_m = c.grow_m, grow_v = c.grow_v;
   const TensorDesc d = descs[t];
   const int64_t nparts = (d.numel + kUPart - 1) >> kUPartLog2;
   const int64_t part0 = d.chunk0 << (chunk_log2 - kUPartLog2);
@@ -789,16 +828,13 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     }
     int32_t f = 0;
     if (d.numel > 0) {
-      const float so_m = ld_global<float>(d.sm), so_v = ld_global<float>(d.sv);
-      // the prediction the update pass used: from the previous amax, read before it is replaced
-      const uint32_t pm = predicted_scale_bits<MF>(amax[2 * t], so_m, grow_m);
-      const uint32_t pv = predicted_scale_bits<VF>(amax[2 * t + 1], so_v, grow_v);
+      // the prediction the update pass used, as k_spec_prepare left it (old scales stay staged there)
+      const uint32_t pm = __float_as_uint(old_scale[4 * t + 2]);
+      const uint32_t pv = __float_as_uint(old_scale[4 * t + 3]);
       float s_m, s_v, inv;
       choose_scale<MF, 0>(am, s_m, inv);
       choose_scale<VF, 0>(av, s_v, inv);
       f = (__float_as_uint(s_m) != pm ? 1 : 0) | (__float_as_uint(s_v) != pv ? 2 : 0);
-      old_scale[2 * t] = so_m;
-      old_scale[2 * t + 1] = so_v;
       st_global<float>(d.sm, s_m);
       st_global<float>(d.sv, s_v);
     }
@@ -910,13 +946,13 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
   if (f & 1) {
     float s, inv;
     choose_scale<MF, 0>(amax[2 * tid], s, inv);
-    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[2 * tid], inv, cnt[kUnderM],
+    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[4 * tid], inv, cnt[kUnderM],
                                    cnt[kSatM]);
   }
   if (f & 2) {
     float s, inv;
     choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
-    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[2 * tid + 1], inv, cnt[kUnderV],
+    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[4 * tid + 1], inv, cnt[kUnderV],
                                   cnt[kSatV]);
   }
   flush_counters<STATS>(counters, tid, cnt);
@@ -1122,7 +1158,7 @@ struct fp8adam_ctx {
   uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
   uint2* d_partial = nullptr;       // tensor mode: [nchunks] per-chunk amax of m', v'
   uint2* d_part_amax = nullptr;     // speculative / delayed: [nuparts] per-part amax of m', v'
-  float* d_old_scale = nullptr;     // tensor mode: [n][2] scales before the current step
+  float* d_old_scale = nullptr;     // tensor mode: [n][4]: scales before the step (+ prepared ones)
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   unsigned long long* d_counters = nullptr;  // [n][5]
   double* d_gpart = nullptr;        // loss scaling: [norm groups][2] sum of squares and Inf/NaN count of g
@@ -1169,9 +1205,15 @@ void launch_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 }
 
 template <int MF, int VF, int SMODE>
+void launch_delayed_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_delayed_prepare<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(64), 0, s, descs_of(c, 0), k,
+                     c->d_old_scale);
+}
+
+template <int MF, int VF, int SMODE>
 void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl);
+                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl, c->d_old_scale);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
@@ -1179,6 +1221,12 @@ void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nuparts)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nuparts, c->gctl);
+}
+
+template <int MF, int VF>
+void launch_spec_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_spec_prepare<MF, VF>), dim3((unsigned)((c->n + 63) / 64)), dim3(64), 0, s, descs_of(c, c->cur),
+                     c->d_amax, k, c->gctl, c->d_old_scale, c->n);
 }
 
 template <int MF, int VF, bool STATS>
@@ -1203,7 +1251,8 @@ void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
 // 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up,
-// 8 delayed pass, 9 delayed commit, 10 gradient-norm pass, 11 loss-scale decision.
+// 8 delayed pass, 9 delayed commit, 10 gradient-norm pass, 11 loss-scale decision,
+// 12 scale preparation (speculative / delayed).
 #define TIMED(kind, call)                              \
   do {                                                 \
     int slot_;                                         \
@@ -1230,6 +1279,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   if constexpr (!L2 && SMODE == 0) {
     if (!done && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
       if (STATS) TIMED(4, launch_reset(c, 0, s));
+      TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
       if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
       TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
       if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
@@ -1239,6 +1289,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   }
   if (!done && c->hist_len > 0 && t >= c->delayed_from) {
     if (STATS) TIMED(4, launch_reset(c, 0, s));
+    TIMED(12, (launch_delayed_prepare<MF, VF, SMODE>(c, k, s)));
     if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2, SR>(c, k, s)));
     TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, s)));
   } else if (!done) {
