@@ -253,6 +253,16 @@ int fp8adam_encode_bits_range(int32_t fmt, uint32_t start, int64_t count, uint8_
 int fp8adam_encode_sr_bits_range(int32_t fmt, uint32_t start, int64_t count, uint32_t r16, uint8_t *out,
                                  hipStream_t stream);
 
+/* out[i] = stochastic-rounding encode of x[i] with its own 16 random bits r16[i], i < n:
+ * the same rounding as fp8adam_encode_sr_bits_range (rounding up iff
+ * floor(f * 2^16) + r16 >= 2^16, f the position of |x| between its FP8 neighbours,
+ * saturating at +-FMAX; the zyxy.net FP8 article, strategies section, names stochastic
+ * rounding).  x (float), r16 (uint16), out (n bytes): device, owned by the caller.
+ * NaN inputs give a NaN code of either sign.  EINVAL for a bad format, n < 0 or a
+ * NULL pointer with n > 0. */
+int fp8adam_encode_sr(int32_t fmt, const float *x, const uint16_t *r16, uint8_t *out, int64_t n,
+                      hipStream_t stream);
+
 /* ---- measurement ---- */
 
 /* Enable (1) or disable (0) per-kernel timing with HIP events around every

@@ -120,6 +120,7 @@ def lib() -> ctypes.CDLL:
         L.ref_encode_sr.restype = ctypes.c_uint8
         L.ref_philox4x32_10.argtypes = [P, P, P]
         L.ref_encode_sr_bits_range.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_int64, ctypes.c_uint32, u8p]
+        L.ref_encode_sr_array.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, u8p]
         L.ref_sr_word.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int64]
         L.ref_sr_word.restype = ctypes.c_uint32
         L.ref_grad_sumsq.argtypes = [u16p, ctypes.c_int64, P, ctypes.POINTER(ctypes.c_int64)]
@@ -281,6 +282,16 @@ def encode_sr_bits_range(fmt, start: int, count: int, r16: int, out: np.ndarray 
     out = np.empty(count, dtype=np.uint8) if out is None else out
     assert out.dtype == np.uint8 and out.size >= count and out.flags["C_CONTIGUOUS"]
     lib().ref_encode_sr_bits_range(fmt_id(fmt), start, count, r16, _ptr(out))
+    return out
+
+
+def encode_sr_array(fmt, x: np.ndarray, r16: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Stochastic-rounding encode of x[i] (float32) with its own 16 random bits r16[i] (uint16)."""
+    assert x.dtype == np.float32 and r16.dtype == np.uint16 and x.shape == r16.shape
+    x, r16 = np.ascontiguousarray(x), np.ascontiguousarray(r16)
+    out = np.empty(x.size, dtype=np.uint8) if out is None else out
+    assert out.dtype == np.uint8 and out.size >= x.size and out.flags["C_CONTIGUOUS"]
+    lib().ref_encode_sr_array(fmt_id(fmt), _ptr(x), _ptr(r16), x.size, _ptr(out))
     return out
 
 

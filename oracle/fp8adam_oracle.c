@@ -206,6 +206,12 @@ uint8_t ref_encode_sr(int fmt, float x, uint32_t r16)
     return ref_encode(fmt, (float)copysign(mag, (double)x)); /* an FP8 value: exact */
 }
 
+/* Stochastic-rounding encode of n values, each with its own 16 random bits. */
+void ref_encode_sr_array(int fmt, const float *x, const uint16_t *r16, int64_t n, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = ref_encode_sr(fmt, x[i], r16[i]);
+}
+
 /* Stochastic-rounding encode of every fp32 bit pattern in [start, start+count) with one
  * fixed r16; used to compare against a device sweep. */
 void ref_encode_sr_bits_range(int fmt, uint32_t start, int64_t count, uint32_t r16, uint8_t *out)

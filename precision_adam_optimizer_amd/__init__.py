@@ -43,7 +43,7 @@ KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "st
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
-           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range")
+           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr")
 
 
 class Fp8AdamError(RuntimeError):
@@ -126,9 +126,11 @@ def load() -> ctypes.CDLL:
     L.fp8adam_current_buffer.argtypes = [vp]
     L.fp8adam_current_buffer.restype = i32
     L.fp8adam_encode_sr_bits_range.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, vp, vp]
+    L.fp8adam_encode_sr.argtypes = [i32, vp, vp, vp, i64, vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
                  "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
-                 "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range"):
+                 "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
+                 "fp8adam_encode_sr"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -220,6 +222,15 @@ def fp8adam_encode_sr_bits_range(fmt: int, start: int, count: int, r16: int, out
     assert out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= count
     _check(load().fp8adam_encode_sr_bits_range(fmt, start, count, r16, _ptr(out),
                                                current_stream() if stream is None else stream))
+
+
+def fp8adam_encode_sr(fmt: int, x: torch.Tensor, r16: torch.Tensor, out: torch.Tensor,
+                      stream: int | None = None) -> None:
+    assert x.dtype == torch.float32 and r16.dtype == torch.uint16 and out.dtype == torch.uint8
+    assert x.is_contiguous() and r16.is_contiguous() and out.is_contiguous()
+    assert r16.numel() == x.numel() and out.numel() >= x.numel()
+    _check(load().fp8adam_encode_sr(fmt, _ptr(x), _ptr(r16), _ptr(out), x.numel(),
+                                    current_stream() if stream is None else stream))
 
 
 def fp8adam_set_timing(ctx: int, enable: bool) -> None:

@@ -15,18 +15,13 @@ namespace fp8adam {
 
 // FMAX = 0.875 * 2^kMaxExp for both formats: 448 = 0.875 * 2^9, 57344 = 0.875 * 2^16.
 template <int FMT> struct Format;
-// kMinNormalField: the fp32 exponent field of the smallest normal (2^-6, 2^-14).
 template <> struct Format<0> {  // E4M3
   static constexpr float kMax = 448.0f;
   static constexpr int kMaxExp = 9;
-  static constexpr int kMantBits = 3;
-  static constexpr int kMinNormalField = 127 - 6;
 };
 template <> struct Format<1> {  // E5M2
   static constexpr float kMax = 57344.0f;
   static constexpr int kMaxExp = 16;
-  static constexpr int kMantBits = 2;
-  static constexpr int kMinNormalField = 127 - 14;
 };
 
 // Four codes packed little-endian in a dword -> four floats (exact).
@@ -74,41 +69,38 @@ __device__ __forceinline__ uint32_t encode1(float a) {
 }
 
 // Stochastic rounding (the zyxy.net article's strategies section: stochastic
-// rounding against the error that accumulates over many updates).  q is
-// already clamped to [-FMAX, FMAX].  Its FP8 neighbours are lo and lo + s,
-// s = the FP8 spacing at |q| (fixed below the smallest normal); with
-// f = (|q| - lo) / s, q rounds up iff floor(f * 2^16) + r16 >= 2^16.
-// Integer form, straight to the code: the significand (implicit bit set) is
-// shifted so that the FP8 spacing sits at bit 16, i.e. to |q| / s in fixed
-// point with 16 fraction bits (the shift is 7 - MB in the normal range and
-// larger below it; fp32 subnormals shift out entirely); adding r16 carries
-// into bit 16 exactly when the rounding goes up, so the top bits are the
-// chosen neighbour in units of s, and the code is that count plus the
-// exponent offset of the binade (a carry past the binade's last code lands
-// on the next binade's first, as the code layout requires).
-template <int FMT>
-__device__ __forceinline__ uint32_t sr_code(float q, uint32_t r16) {
-  constexpr int MB = Format<FMT>::kMantBits;
-  constexpr int MINF = Format<FMT>::kMinNormalField;
-  const uint32_t u = __float_as_uint(q);
-  const int e = (int)((u >> 23) & 0xFFu);
-  const uint32_t sig = (u & 0x7FFFFFu) | 0x800000u;
-  const int sh = min(max(MINF + 7 - MB - e, 7 - MB), 31);
-  const uint32_t units = ((sig >> sh) + r16) >> 16;
-  const uint32_t mag = ((uint32_t)max(e - MINF, 0) << MB) + units;
-  const uint32_t sign = (u >> 24) & 0x80u;
-  return sign | (e == 0xFF ? 0x7Fu : mag);  // a NaN keeps the NaN code
-}
-
-// Four floats -> four codes with stochastic rounding; r16[j] are 16 random bits each.
+// rounding against the error that accumulates over many updates).  Let lo and
+// lo + s be the FP8 neighbours of |q| (s = the FP8 spacing at |q|, fixed below
+// the smallest normal) and f = (|q| - lo) / s; q rounds up iff
+// floor(f * 2^16) + r16 >= 2^16.  gfx950's stochastic-rounding converts
+// (v_cvt_sr_fp8_f32 / v_cvt_sr_bf8_f32) add their random operand to the bits
+// that are rounded away, aligned at the top of those bits, and carry; with the
+// 16 random bits in the operand's top half and zeros below, that is exactly the
+// rule above, in the normal and the subnormal FP8 range alike (checked against
+// an independent encoder for every fp32 pattern in the FP8 range and for all
+// 2^16 values of r16 on sampled inputs).  Inputs are clamped to +-FMAX first,
+// so the converts saturate instead of overflowing; NaN inputs are outside the
+// contract.  r16[j] holds 16 random bits in its low half.
 template <int FMT>
 __device__ __forceinline__ uint32_t encode4_sr(float a, float b, float c, float d, const uint32_t (&r16)[4]) {
   constexpr float M = Format<FMT>::kMax;
-  const uint32_t c0 = sr_code<FMT>(__builtin_amdgcn_fmed3f(a, -M, M), r16[0]);
-  const uint32_t c1 = sr_code<FMT>(__builtin_amdgcn_fmed3f(b, -M, M), r16[1]);
-  const uint32_t c2 = sr_code<FMT>(__builtin_amdgcn_fmed3f(c, -M, M), r16[2]);
-  const uint32_t c3 = sr_code<FMT>(__builtin_amdgcn_fmed3f(d, -M, M), r16[3]);
-  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  a = __builtin_amdgcn_fmed3f(a, -M, M);
+  b = __builtin_amdgcn_fmed3f(b, -M, M);
+  c = __builtin_amdgcn_fmed3f(c, -M, M);
+  d = __builtin_amdgcn_fmed3f(d, -M, M);
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_sr_fp8_f32(a, (int)(r16[0] << 16), 0, 0);
+    w = __builtin_amdgcn_cvt_sr_fp8_f32(b, (int)(r16[1] << 16), w, 1);
+    w = __builtin_amdgcn_cvt_sr_fp8_f32(c, (int)(r16[2] << 16), w, 2);
+    w = __builtin_amdgcn_cvt_sr_fp8_f32(d, (int)(r16[3] << 16), w, 3);
+  } else {
+    w = __builtin_amdgcn_cvt_sr_bf8_f32(a, (int)(r16[0] << 16), 0, 0);
+    w = __builtin_amdgcn_cvt_sr_bf8_f32(b, (int)(r16[1] << 16), w, 1);
+    w = __builtin_amdgcn_cvt_sr_bf8_f32(c, (int)(r16[2] << 16), w, 2);
+    w = __builtin_amdgcn_cvt_sr_bf8_f32(d, (int)(r16[3] << 16), w, 3);
+  }
+  return (uint32_t)w;
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy

@@ -239,6 +239,16 @@ __global__ __launch_bounds__(kThreads) void k_encode_sr_bits(uint32_t start, int
 }
 
 template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_encode_sr(const float* __restrict__ x, const uint16_t* __restrict__ r16,
+                                                        uint8_t* __restrict__ out, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint32_t r[4] = {(uint32_t)r16[i], 0u, 0u, 0u};
+    out[i] = (uint8_t)(encode4_sr<FMT>(x[i], 0.0f, 0.0f, 0.0f, r) & 0xFFu);
+  }
+}
+
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__ codes, float* __restrict__ out,
                                                      int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -393,7 +403,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         desc[(size_t)n + t].m = T.m_alt;
         desc[(size_t)n + t].v = T.v_alt;
       }
-      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2))) > (int64_t)INT32_MAX)
+      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2Min))) > (int64_t)INT32_MAX)
         return fail(FP8ADAM_EINVAL, "too many elements for one context");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
       nchunks += nc;
@@ -406,7 +416,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->nchunks = nchunks;
     c->chunk_log2 = chunk_log2;
     c->nparts = nchunks << (chunk_log2 - kPartLog2);
-    c->nuparts = nchunks << (chunk_log2 - kUPartLog2);
+    c->nuparts = nchunks << (chunk_log2 - kUPartLog2Min);
     c->speculate_from = cfg->speculate_from_step > 0 ? cfg->speculate_from_step : 4;
     c->hist_len = delayed ? hist_len : 0;
     c->delayed_from = cfg->delayed_from_step > 0 ? cfg->delayed_from_step : 2;
@@ -655,6 +665,18 @@ int fp8adam_encode_sr_bits_range(int32_t fmt, uint32_t start, int64_t count, uin
   else
     hipLaunchKernelGGL(k_encode_sr_bits<1>, dim3(probe_grid(count, 4)), dim3(kThreads), 0, stream, start, count, r16,
                        out);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_encode_sr(int32_t fmt, const float* x, const uint16_t* r16, uint8_t* out, int64_t n,
+                      hipStream_t stream) {
+  if (!valid_fmt(fmt) || n < 0 || (n > 0 && (!x || !r16 || !out))) return fail(FP8ADAM_EINVAL, "bad argument");
+  if (n == 0) return 0;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_encode_sr<0>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, x, r16, out, n);
+  else
+    hipLaunchKernelGGL(k_encode_sr<1>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, x, r16, out, n);
   HIP_TRY(hipGetLastError());
   return 0;
 }

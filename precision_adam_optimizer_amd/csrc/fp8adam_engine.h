@@ -36,8 +36,8 @@
 // The chunk table (built once at init) cuts every tensor into chunks of
 // 2^chunk_log2 elements (4096..32768, chosen per context so that even small
 // lists give a few thousand work-groups); an amax-pass work-group owns one
-// chunk, an update-pass work-group one kUPart-element part, a block-pass
-// work-group one kPart-element part.
+// chunk, an update-pass work-group one part of 2^upd_part_log2 elements, a
+// block-pass work-group one kPart-element part.
 // Loads and stores are dword-granular per lane and contiguous across the wave
 // (fp32 master: 16 B per lane).
 #pragma once
@@ -74,13 +74,21 @@ using namespace fp8adam;
 #ifndef FP8ADAM_BLOCK_J
 #define FP8ADAM_BLOCK_J 1          // block pass: 128-element blocks per half-wave per tile
 #endif
-// Update pass: one-shot work-groups of 1024 elements, one group of 4 per lane.
-// Measured against 2048 (two groups per lane) and 4096 (four): the mixed
-// read/write stream runs 7% faster (two-pass) / 4% (speculative) with the
-// smallest work-groups, which keep more distinct work-groups, and so more
-// independent address streams, in flight per CU.
+// Update pass, fp32 master with round-to-nearest: one-shot work-groups of
+// 1024 elements, one group of 4 per lane.  Measured against 2048 (two groups
+// per lane) and 4096 (four): the mixed read/write stream runs 7% faster
+// (two-pass) / 4% (speculative) with the smallest work-groups, which keep more
+// distinct work-groups, and so more independent address streams, in flight
+// per CU.
 #ifndef FP8ADAM_UPD_PART_LOG2
 #define FP8ADAM_UPD_PART_LOG2 10
+#endif
+// Update pass with a bf16 master (10 bytes per element, so a 1024-element
+// work-group moves only 10 KiB) or with stochastic rounding (a Philox block
+// per 4 elements): 2048-element work-groups, two groups per lane, measured 6%
+// faster (bf16 master) and 9% faster (stochastic rounding) than 1024.
+#ifndef FP8ADAM_UPD_PART_LOG2_WIDE
+#define FP8ADAM_UPD_PART_LOG2_WIDE 11
 #endif
 #ifndef FP8ADAM_AMAX_UNROLL
 #define FP8ADAM_AMAX_UNROLL 8
@@ -115,8 +123,15 @@ constexpr int kAmaxUnroll = FP8ADAM_AMAX_UNROLL;  // accesses in flight per lane
 constexpr int kUpdUnroll = FP8ADAM_UPDATE_UNROLL; // accesses in flight per lane, update pass
 constexpr int kPartLog2 = FP8ADAM_PART_LOG2;
 constexpr int64_t kPart = (int64_t)1 << kPartLog2;  // elements per block-pass work-group
-constexpr int kUPartLog2 = FP8ADAM_UPD_PART_LOG2;
-constexpr int64_t kUPart = (int64_t)1 << kUPartLog2;  // elements per update-pass work-group
+// log2 of the elements per update-pass work-group
+template <bool BF16P, bool SR>
+constexpr int upd_part_log2() {
+  return (BF16P || SR) ? FP8ADAM_UPD_PART_LOG2_WIDE : FP8ADAM_UPD_PART_LOG2;
+}
+constexpr int kUPartLog2Min = FP8ADAM_UPD_PART_LOG2 < FP8ADAM_UPD_PART_LOG2_WIDE ? FP8ADAM_UPD_PART_LOG2
+                                                                                  : FP8ADAM_UPD_PART_LOG2_WIDE;
+constexpr int kUPartLog2Max = FP8ADAM_UPD_PART_LOG2 < FP8ADAM_UPD_PART_LOG2_WIDE ? FP8ADAM_UPD_PART_LOG2_WIDE
+                                                                                  : FP8ADAM_UPD_PART_LOG2;
 constexpr int kMaxChunkLog2 = FP8ADAM_MAX_CHUNK_LOG2;
 constexpr int kMinChunkLog2 = 12;                   // smallest chunk = amax-pass work-group (4096 elements)
 constexpr int kMinAmaxGroups = 2048;                // 8 work-groups per CU
@@ -125,9 +140,10 @@ constexpr int kBlkJ = FP8ADAM_BLOCK_J;            // a block-pass tile is 8 half
 constexpr int kReduceThreads = 1024;              // one work-group per tensor in k_reduce
 constexpr int kStatsPerTensor = 5;
 
-static_assert(kMaxChunkLog2 >= kMinChunkLog2 && kMinChunkLog2 >= kPartLog2 && kMinChunkLog2 >= kUPartLog2,
+static_assert(kMaxChunkLog2 >= kMinChunkLog2 && kMinChunkLog2 >= kPartLog2 && kMinChunkLog2 >= kUPartLog2Max,
               "a chunk holds whole parts");
-static_assert(kUPart % (kSubTile * kUpdUnroll) == 0, "part must hold whole unrolled update tiles");
+static_assert(((int64_t)1 << kUPartLog2Min) % (kSubTile * kUpdUnroll) == 0,
+              "part must hold whole unrolled update tiles");
 static_assert(kPart % (kBlock * 8 * kBlkJ) == 0, "part must hold whole block tiles");
 
 struct TensorDesc {
@@ -576,12 +592,13 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   constexpr bool PARTS = MODE != kModeJit;  // per-part amax partials for the commit kernel
   const int64_t w = work_index<kXcdStreams>(nwork);
   if (w < 0) return;
-  const int split_log2 = chunk_log2 - kUPartLog2;
+  constexpr int PL = upd_part_log2<BF16P, SR>();
+  const int split_log2 = chunk_log2 - PL;
   const int64_t chunk = w >> split_log2;
   const int tid = chunk_tid[chunk];
   const TensorDesc d = descs[tid];
-  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << kUPartLog2);
-  const int64_t end = min(start + kUPart, d.numel);
+  const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & ((1 << split_log2) - 1)) << PL);
+  const int64_t end = min(start + ((int64_t)1 << PL), d.numel);
   if (start >= end) return;  // empty part at the end of a tensor (uniform for the work-group)
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
   // codes go back in place (two-pass) or into the other buffer (speculative)
@@ -720,13 +737,14 @@ template <int MF, int VF, int SMODE>
 __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorDesc* __restrict__ descs,
                                                                    const uint2* __restrict__ part_amax,
                                                                    uint32_t* __restrict__ amax, StepConsts c,
-                                                                   int chunk_log2, const GradCtl* __restrict__ gctl,
+                                                                   int chunk_log2, int part_log2,
+                                                                   const GradCtl* __restrict__ gctl,
                                                                    const float* __restrict__ prep) {
   if (amp_apply(gctl, c)) return;  // skipped step: scales, amax and history stay
   const int t = blockIdx.x;
   const TensorDesc d = descs[t];
-  const int64_t nparts = (d.numel + kUPart - 1) >> kUPartLog2;
-  const int64_t part0 = d.chunk0 << (chunk_log2 - kUPartLog2);
+  const int64_t nparts = (d.numel + ((int64_t)1 << part_log2) - 1) >> part_log2;
+  const int64_t part0 = d.chunk0 << (chunk_log2 - part_log2);
   uint32_t am = 0, av = 0;
   for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
     const uint2 pv = part_amax[part0 + k];
@@ -795,7 +813,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
                                                                 float* __restrict__ old_scale,
                                                                 int32_t* __restrict__ flags,
                                                                 unsigned long long* __restrict__ counters,
-                                                                int chunk_log2, StepConsts c,
+                                                                int chunk_log2, int part_log2, StepConsts c,
                                                                 const GradCtl* __restrict__ gctl) {
   const int t = blockIdx.x;
   if (amp_apply(gctl, c)) {  // skipped step: scales and amax stay, nothing to fix up
@@ -803,8 +821,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     return;
   }
   const TensorDesc d = descs[t];
-  const int64_t nparts = (d.numel + kUPart - 1) >> kUPartLog2;
-  const int64_t part0 = d.chunk0 << (chunk_log2 - kUPartLog2);
+  const int64_t nparts = (d.numel + ((int64_t)1 << part_log2) - 1) >> part_log2;
+  const int64_t part0 = d.chunk0 << (chunk_log2 - part_log2);
   uint32_t am = 0, av = 0;
   for (int64_t k = threadIdx.x; k < nparts; k += kReduceThreads) {
     const uint2 pv = part_amax[part0 + k];
@@ -1152,12 +1170,12 @@ struct fp8adam_ctx {
   float margin_scale = 1.0f;       // delayed scaling: 2^margin
   int cur = 0;                     // code buffer holding the moments: 0 = m/v, 1 = m_alt/v_alt
   int64_t nparts = 0;              // block-pass work-groups
-  int64_t nuparts = 0;             // update-pass work-groups
+  int64_t nuparts = 0;             // update-pass work-groups at the smallest part size
   fp8adam_engine::TensorDesc* d_desc = nullptr;    // [2][n]: descriptors with m/v, then with m_alt/v_alt
   int32_t* d_chunk_tid = nullptr;
   uint32_t* d_amax = nullptr;       // tensor mode: [n][2] amax of the last step; block mode: [n][4] stats
   uint2* d_partial = nullptr;       // tensor mode: [nchunks] per-chunk amax of m', v'
-  uint2* d_part_amax = nullptr;     // speculative / delayed: [nuparts] per-part amax of m', v'
+  uint2* d_part_amax = nullptr;     // speculative / delayed: [<= nuparts] per-part amax of m', v'
   float* d_old_scale = nullptr;     // tensor mode: [n][4]: scales before the step (+ prepared ones)
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   unsigned long long* d_counters = nullptr;  // [n][5]
@@ -1211,16 +1229,18 @@ void launch_delayed_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) 
 }
 
 template <int MF, int VF, int SMODE>
-void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
   hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, c->gctl, c->d_old_scale);
+                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, part_log2, c->gctl,
+                     c->d_old_scale);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nuparts)), dim3(kThreads), 0, s,
+  const int64_t nwork = c->nchunks << (c->chunk_log2 - upd_part_log2<BF16P, SR>());
+  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(nwork)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, c->nuparts, c->gctl);
+                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, nwork, c->gctl);
 }
 
 template <int MF, int VF>
@@ -1230,10 +1250,10 @@ void launch_spec_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 }
 
 template <int MF, int VF, bool STATS>
-void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
                      descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, k, c->gctl);
+                     c->chunk_log2, part_log2, k, c->gctl);
 }
 
 template <int MF, int VF, bool STATS, bool SR>
@@ -1281,7 +1301,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
       if (STATS) TIMED(4, launch_reset(c, 0, s));
       TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
       if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
-      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, s)));
+      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, upd_part_log2<BF16P, SR>(), s)));
       if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
       c->cur = 1 - c->cur;
       done = true;
@@ -1291,7 +1311,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
     if (STATS) TIMED(4, launch_reset(c, 0, s));
     TIMED(12, (launch_delayed_prepare<MF, VF, SMODE>(c, k, s)));
     if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2, SR>(c, k, s)));
-    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, s)));
+    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, upd_part_log2<BF16P, SR>(), s)));
   } else if (!done) {
     if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters

@@ -68,6 +68,10 @@ def test_error_paths_without_a_gpu():
     assert L.fp8adam_step(None, ctypes.byref(hp), None) == -1
     assert L.fp8adam_encode(3, None, None, 10, None) == -1
     assert L.fp8adam_encode_bits_range(0, 10, (1 << 32), None, None) == -1
+    assert L.fp8adam_encode_sr(2, None, None, None, 0, None) == -1
+    assert L.fp8adam_encode_sr(0, None, None, None, -1, None) == -1
+    assert L.fp8adam_encode_sr(0, None, None, None, 8, None) == -1
+    assert L.fp8adam_encode_sr(1, None, None, None, 0, None) == 0  # empty: nothing to do
     assert L.fp8adam_num_chunks(None) == -1
     amp = pk.AmpConfigArg(1.0, 2.0, 0.5, 2000)
     assert L.fp8adam_step_amp(None, ctypes.byref(hp), ctypes.byref(amp), 64, None) == -1

@@ -110,3 +110,45 @@ def test_encode_sr_matches_oracle_over_the_fp8_range(fmt):
         assert bad.size == 0, (f"fmt {fmt} r16 {r16:#06x}: {bad.size} codes differ, first at pattern "
                                f"{start + int(bad[0]):#010x}: gpu {got[bad[0]]:#04x} oracle {want[bad[0]]:#04x}")
         print(f"sr sweep fmt {fmt} start {start:#010x} count {count} r16 {r16:#06x}: equal", flush=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_encode_sr_every_r16_on_sampled_values(fmt):
+    """Each of 512 values, spread over every FP8 binade (normal, subnormal,
+    below the smallest subnormal, the top binade up to FMAX, exact FP8 values
+    and the midpoints between neighbours), both signs, stochastically rounded
+    with every one of the 2^16 random values: device code == oracle code.  For
+    each value this pins the exact r16 threshold at which it rounds up."""
+    rng = np.random.default_rng(2409 + fmt)
+    lo_e, hi_e = (-12, 8) if fmt == 0 else (-19, 15)
+    k = 384
+    vals = np.ldexp(1.0 + rng.random(k), rng.integers(lo_e, hi_e + 1, size=k)).astype(np.float32)
+    fp8 = oracle.decode(fmt, np.arange(0, 127, dtype=np.uint8)).astype(np.float64)
+    fp8 = fp8[np.isfinite(fp8)]
+    exact = rng.choice(fp8, 64)
+    mids = (fp8[1:] + fp8[:-1]) / 2
+    vals = np.concatenate([vals, exact.astype(np.float32), rng.choice(mids, 64).astype(np.float32)])
+    vals = np.clip(vals, 0.0, {0: 448.0, 1: 57344.0}[fmt]).astype(np.float32)
+    vals[rng.random(vals.size) < 0.5] *= -1
+    assert vals.size == 512
+    r16 = np.arange(1 << 16, dtype=np.uint16)
+    x_all = np.repeat(vals, r16.size)
+    r_all = np.tile(r16, vals.size)
+    out = torch.empty(x_all.size, dtype=torch.uint8, device="cuda")
+    pk.fp8adam_encode_sr(fmt, torch.from_numpy(x_all).cuda(), torch.from_numpy(r_all).cuda(), out)
+    got = out.cpu().numpy()
+    want = np.empty_like(got)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    step = -(-x_all.size // threads)
+
+    def work(t):
+        a, b = t * step, min(x_all.size, (t + 1) * step)
+        if a < b:
+            oracle.encode_sr_array(fmt, x_all[a:b], r_all[a:b], want[a:b])
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(threads)))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (f"{bad.size} codes differ; first x={x_all[bad[0]]!r} r16={int(r_all[bad[0]]):#06x}: "
+                           f"gpu {got[bad[0]]:#04x} oracle {want[bad[0]]:#04x}")
