@@ -219,7 +219,8 @@ def main():
     bpp = BYTES_PER_PARAM[(w.granularity, w.master)]
     alg_bytes = bpp * total
     achieved = alg_bytes / kavg_s / 1e9
-    traffic = load_traffic(w.name, kernel)
+    # the counters are per kernel instantiation: stochastic rounding has its own
+    traffic = load_traffic(w.name, kernel + ("_sr" if args.rounding == "stochastic" else ""))
     # bytes the whole step moved: + the amax pass (g, m, v; and p with coupled L2) in the
     # two-pass schedule, + the fix-up (g, m, v read, m, v written) of re-quantized tensors
     # in the speculative one

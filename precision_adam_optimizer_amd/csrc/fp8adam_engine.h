@@ -74,8 +74,8 @@ using namespace fp8adam;
 #ifndef FP8ADAM_BLOCK_J
 #define FP8ADAM_BLOCK_J 1          // block pass: 128-element blocks per half-wave per tile
 #endif
-// Update pass, fp32 master with round-to-nearest: one-shot work-groups of
-// 1024 elements, one group of 4 per lane.  Measured against 2048 (two groups
+// Update pass, fp32 master: one-shot work-groups of 1024 elements, one group
+// of 4 per lane.  Measured against 2048 (two groups
 // per lane) and 4096 (four): the mixed read/write stream runs 7% faster
 // (two-pass) / 4% (speculative) with the smallest work-groups, which keep more
 // distinct work-groups, and so more independent address streams, in flight
@@ -84,9 +84,8 @@ using namespace fp8adam;
 #define FP8ADAM_UPD_PART_LOG2 10
 #endif
 // Update pass with a bf16 master (10 bytes per element, so a 1024-element
-// work-group moves only 10 KiB) or with stochastic rounding (a Philox block
-// per 4 elements): 2048-element work-groups, two groups per lane, measured 6%
-// faster (bf16 master) and 9% faster (stochastic rounding) than 1024.
+// work-group moves only 10 KiB): 2048-element work-groups, two groups per
+// lane, measured 5-6% faster than 1024 and 3% faster than 4096.
 #ifndef FP8ADAM_UPD_PART_LOG2_WIDE
 #define FP8ADAM_UPD_PART_LOG2_WIDE 11
 #endif
@@ -124,9 +123,9 @@ constexpr int kUpdUnroll = FP8ADAM_UPDATE_UNROLL; // accesses in flight per lane
 constexpr int kPartLog2 = FP8ADAM_PART_LOG2;
 constexpr int64_t kPart = (int64_t)1 << kPartLog2;  // elements per block-pass work-group
 // log2 of the elements per update-pass work-group
-template <bool BF16P, bool SR>
+template <bool BF16P>
 constexpr int upd_part_log2() {
-  return (BF16P || SR) ? FP8ADAM_UPD_PART_LOG2_WIDE : FP8ADAM_UPD_PART_LOG2;
+  return BF16P ? FP8ADAM_UPD_PART_LOG2_WIDE : FP8ADAM_UPD_PART_LOG2;
 }
 constexpr int kUPartLog2Min = FP8ADAM_UPD_PART_LOG2 < FP8ADAM_UPD_PART_LOG2_WIDE ? FP8ADAM_UPD_PART_LOG2
                                                                                   : FP8ADAM_UPD_PART_LOG2_WIDE;
@@ -592,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   constexpr bool PARTS = MODE != kModeJit;  // per-part amax partials for the commit kernel
   const int64_t w = work_index<kXcdStreams>(nwork);
   if (w < 0) return;
-  constexpr int PL = upd_part_log2<BF16P, SR>();
+  constexpr int PL = upd_part_log2<BF16P>();
   const int split_log2 = chunk_log2 - PL;
   const int64_t chunk = w >> split_log2;
   const int tid = chunk_tid[chunk];
@@ -1237,7 +1236,7 @@ void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, h
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  const int64_t nwork = c->nchunks << (c->chunk_log2 - upd_part_log2<BF16P, SR>());
+  const int64_t nwork = c->nchunks << (c->chunk_log2 - upd_part_log2<BF16P>());
   hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(nwork)), dim3(kThreads), 0, s,
                      descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, nwork, c->gctl);
@@ -1301,7 +1300,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
       if (STATS) TIMED(4, launch_reset(c, 0, s));
       TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
       if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
-      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, upd_part_log2<BF16P, SR>(), s)));
+      TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, upd_part_log2<BF16P>(), s)));
       if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
       c->cur = 1 - c->cur;
       done = true;
@@ -1311,7 +1310,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
     if (STATS) TIMED(4, launch_reset(c, 0, s));
     TIMED(12, (launch_delayed_prepare<MF, VF, SMODE>(c, k, s)));
     if (c->nchunks > 0) TIMED(8, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeDelayed, L2, SR>(c, k, s)));
-    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, upd_part_log2<BF16P, SR>(), s)));
+    TIMED(9, (launch_delayed_reduce<MF, VF, SMODE>(c, k, upd_part_log2<BF16P>(), s)));
   } else if (!done) {
     if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, L2>(c, k, s)));
     // the reduce also runs for an all-empty list: it sets amax 0 and clears the counters
