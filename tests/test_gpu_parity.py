@@ -26,8 +26,8 @@ from tests.gpu_util import (OracleState, compare_tensor, np_host, oracle_config,
 
 pytestmark = pytest.mark.gpu
 
-SIZES = [1, 2, 3, 4, 5, 7, 127, 128, 129, 255, 1000, 1023, 1024, 1025, 4095, 4096, 4097, 16383, 16384,
-         16385, 16387, 40000, 65539]
+SIZES = [1, 2, 3, 4, 5, 7, 127, 128, 129, 255, 1000, 1023, 1024, 1025, 2047, 2049, 4095, 4096, 4097, 16383,
+         16384, 16385, 16387, 40000, 65539]
 FORMATS = [("e4m3", "e5m2"), ("e5m2", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e4m3")]
 COMBOS = list(itertools.product(FORMATS, ["tensor", "block128"], ["pow2", "amax"], ["fp32", "bf16"]))
 
