@@ -119,6 +119,10 @@ typedef struct {
     int32_t delayed_from_step; /* DELAYED: first t quantized with the delayed scale; <= 0 means 2 */
     int32_t rounding;          /* fp8adam_rounding */
     uint64_t seed;             /* STOCHASTIC: the generator's key */
+    int32_t zero_state;        /* nonzero: fp8adam_init writes a fresh optimizer state into the
+                                  caller's buffers (m, v codes 0; every scale 1.0; the amax
+                                  history 0), so they may start with any content; 0: the caller
+                                  provides the state (fresh, or restored from a checkpoint) */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,
@@ -134,7 +138,10 @@ typedef struct {
  *   amax_history : DELAYED scaling only (else ignored, may be NULL): 2*H floats, 4-byte
  *             aligned, the amax history of m (first H) then of v; read and updated by
  *             every step.  Part of the optimizer state (checkpoint it with the codes).
- * The state before the first step is all-zero codes with scales 1.0 (and a zero history). */
+ * The state before the first step is all-zero codes with scales 1.0 (and a zero history);
+ * fp8adam_config.zero_state asks fp8adam_init to write it.  An empty tensor (numel 0) needs
+ * no pointers; with zero_state and tensor granularity its m_scale / v_scale, if not NULL,
+ * still receive 1.0. */
 typedef struct {
     void *param;
     const void *grad;

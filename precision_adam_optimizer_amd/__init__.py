@@ -67,7 +67,7 @@ class ConfigArg(ctypes.Structure):
                 ("decay_mode", ctypes.c_int32), ("scaling", ctypes.c_int32),
                 ("amax_history_len", ctypes.c_int32), ("margin", ctypes.c_int32),
                 ("delayed_from_step", ctypes.c_int32), ("rounding", ctypes.c_int32),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("zero_state", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -266,8 +266,9 @@ class FP8AdamW:
 
     params: fp32 or bf16 master weights (all the same dtype); grads: bf16, same
     numel as their parameter.  The moment codes (uint8) and scales (fp32) are
-    allocated here, zero codes with unit scales, unless ``state`` supplies
-    (m, v, m_scale, v_scale) lists.  With ``schedule="speculative"`` a second
+    allocated here and the library writes the fresh state into them (zero codes,
+    unit scales, a zero amax history: the config's zero_state), unless ``state``
+    supplies (m, v, m_scale, v_scale) lists.  With ``schedule="speculative"`` a second
     pair of code buffers is allocated and the moments alternate between the two;
     ``m`` and ``v`` always return the pair that holds them.  ``decay_mode="l2"``
     adds weight_decay * p to the gradient instead of decaying p (Adam on an
@@ -294,9 +295,11 @@ class FP8AdamW:
             raise ValueError("master weights must be float32 or bfloat16")
         self.granularity = _GRAN[granularity]
         self.params, self.grads = params, grads
-        if state is None:
-            m = [torch.zeros(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
-            v = [torch.zeros(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
+        fresh = state is None  # the library writes the fresh state (zero_state) into these buffers
+        if fresh:
+            m = [torch.empty(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
+            v = [torch.empty(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
+            # (the scales are written too; ones keep an empty tensor's unused slot defined)
             ms = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             vs = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
             state = (m, v, ms, vs)
@@ -306,8 +309,8 @@ class FP8AdamW:
         if delayed and len(state) > 4:
             self.amax_history = list(state[4])
         elif delayed:
-            self.amax_history = [torch.zeros(2 * amax_history_len, dtype=torch.float32, device=p.device)
-                                 for p in params]
+            self.amax_history = [(torch.empty if fresh else torch.zeros)(2 * amax_history_len, dtype=torch.float32,
+                                                                         device=p.device) for p in params]
         else:
             self.amax_history = [None] * len(params)
         spec = _SCHED[schedule] == SCHEDULE_SPECULATIVE
@@ -338,7 +341,7 @@ class FP8AdamW:
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
                              _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode],
                              _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step),
-                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF)
+                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, int(fresh))
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):

@@ -238,6 +238,20 @@ __global__ __launch_bounds__(kThreads) void k_encode_sr_bits(uint32_t start, int
   }
 }
 
+// A fresh optimizer state's scales and history (fp8adam_config.zero_state): one
+// work-group per tensor writes 1.0 into every scale slot of m and v and zeroes
+// the 2H-entry amax history; the codes are cleared with a memset.
+__global__ __launch_bounds__(kThreads) void k_fresh_state(const TensorDesc* __restrict__ descs, int block, int hist2) {
+  const TensorDesc d = descs[blockIdx.x];
+  const int64_t ns = block ? (d.numel + kBlock - 1) / kBlock : 1;
+  for (int64_t i = threadIdx.x; i < ns; i += kThreads) {
+    if (d.sm) st_global<float>(d.sm + i, 1.0f);
+    if (d.sv) st_global<float>(d.sv + i, 1.0f);
+  }
+  if (d.hist)
+    for (int j = threadIdx.x; j < hist2; j += kThreads) st_global<float>(d.hist + j, 0.0f);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_encode_sr(const float* __restrict__ x, const uint16_t* __restrict__ r16,
                                                         uint8_t* __restrict__ out, int64_t n) {
@@ -441,6 +455,18 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       e = hipMemcpyAsync(c->d_chunk_tid, chunk_tid.data(), sizeof(int32_t) * (size_t)nchunks, hipMemcpyHostToDevice,
                          stream);
     if (e == hipSuccess) e = hipMemsetAsync(c->d_amax, 0, sizeof(uint32_t) * namax, stream);
+    if (cfg->zero_state) {
+      for (int32_t t = 0; e == hipSuccess && t < n; t++) {
+        if (tensors[t].numel <= 0) continue;
+        e = hipMemsetAsync(tensors[t].m, 0, (size_t)tensors[t].numel, stream);
+        if (e == hipSuccess) e = hipMemsetAsync(tensors[t].v, 0, (size_t)tensors[t].numel, stream);
+      }
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(k_fresh_state, dim3((unsigned)n), dim3(kThreads), 0, stream, c->d_desc,
+                           cfg->granularity == FP8ADAM_SCALE_BLOCK128 ? 1 : 0, 2 * c->hist_len);
+        e = hipGetLastError();
+      }
+    }
     if (e == hipSuccess)
       e = hipMemsetAsync(c->d_counters, 0, sizeof(unsigned long long) * (size_t)n * kStatsPerTensor, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);

@@ -142,3 +142,35 @@ def test_binding_checks_state_sizes_before_the_library():
     for st, kw, what in cases:
         with pytest.raises(ValueError, match=what):
             pk.FP8AdamW(p, g, state=tuple([x] for x in st), **kw)
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """Every struct the binding marshals has the header's size and field
+    offsets (a C program built against include/fp8adam.h prints them)."""
+    structs = {"fp8adam_tensor": pk.TensorArg, "fp8adam_config": pk.ConfigArg, "fp8adam_hparams": pk.HParamsArg,
+               "fp8adam_amp_config": pk.AmpConfigArg, "fp8adam_stats_t": pk.StatsArg}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "fp8adam.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append('  printf("fp8adam_amp_state size %zu\\n", sizeof(fp8adam_amp_state));')
+    for f in pk.AMP_STATE_DTYPE.names:
+        lines.append(f'  printf("fp8adam_amp_state {f} %zu\\n", offsetof(fp8adam_amp_state, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", f"-I{os.path.join(ROOT, 'include')}",
+                    "-I/opt/rocm/include", "-o", str(exe), str(src)], check=True, capture_output=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, f"{cname}.{f}"
+    assert got[("fp8adam_amp_state", "size")] == pk.AMP_STATE_DTYPE.itemsize
+    for f in pk.AMP_STATE_DTYPE.names:
+        assert got[("fp8adam_amp_state", f)] == pk.AMP_STATE_DTYPE.fields[f][1], f"fp8adam_amp_state.{f}"
