@@ -187,7 +187,9 @@ int fp8adam_init(fp8adam_ctx **out, const fp8adam_tensor *tensors, int32_t n,
 /* One optimizer step over every tensor of the context, enqueued on `stream`
  * and returning at once.  Validates hp (EINVAL).  Allocates nothing.  After the
  * stream reaches the end of the step each tensor's (codes, scale) pair is
- * consistent.  Steps of one context must not overlap. */
+ * consistent.  Steps of one context must not overlap.  `stream` must belong to the
+ * context's device (EINVAL otherwise; the same holds for fp8adam_step_amp and
+ * fp8adam_stats). */
 int fp8adam_step(fp8adam_ctx *ctx, const fp8adam_hparams *hp, hipStream_t stream);
 
 /* ---- loss scaling, non-finite skip and global-norm clipping, fused ----

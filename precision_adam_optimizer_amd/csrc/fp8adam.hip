@@ -486,6 +486,18 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
 
 namespace {
 
+// The context's buffers live on the device it was built on: a stream of
+// another device would run the kernels there, against this device's memory.
+int check_device(const fp8adam_ctx* ctx, hipStream_t stream) {
+  hipDevice_t dev = -1;
+  const hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  if (dev != ctx->device)
+    return fail(FP8ADAM_EINVAL, "the stream belongs to device " + std::to_string(dev) + ", the context to device " +
+                                    std::to_string(ctx->device));
+  return 0;
+}
+
 // Validate the hyperparameters and fill the per-step constants of step hp->step.
 int step_consts(const fp8adam_ctx* ctx, const fp8adam_hparams* hp, StepConsts& k) {
     if (!ctx || !hp) return fail(FP8ADAM_EINVAL, "ctx or hp is null");
@@ -528,6 +540,7 @@ int fp8adam_step(fp8adam_ctx* ctx, const fp8adam_hparams* hp, hipStream_t stream
   try {
     StepConsts k;
     if (int r = step_consts(ctx, hp, k)) return r;
+    if (int r = check_device(ctx, stream)) return r;
     return run_step(ctx, k, hp->step, stream);
   } catch (...) {
     return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step");
@@ -540,6 +553,7 @@ int fp8adam_step_amp(fp8adam_ctx* ctx, const fp8adam_hparams* hp, const fp8adam_
     StepConsts k;
     if (int r = step_consts(ctx, hp, k)) return r;
     if (!amp || !state) return fail(FP8ADAM_EINVAL, "amp or state is null");
+    if (int r = check_device(ctx, stream)) return r;
     if ((uintptr_t)state & 7u) return fail(FP8ADAM_EINVAL, "state must be 8-byte aligned");
     if (!(amp->growth_factor > 1.0f) || !isfinite(amp->growth_factor) || !(amp->backoff_factor > 0.0f) ||
         !(amp->backoff_factor < 1.0f) || amp->growth_interval < 1 || !isfinite(amp->max_norm))
@@ -564,6 +578,7 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
   try {
     if (!ctx || !out_host) return fail(FP8ADAM_EINVAL, "ctx or out is null");
     if (n != ctx->n) return fail(FP8ADAM_EINVAL, "n must equal the context's tensor count");
+    if (int r = check_device(ctx, stream)) return r;
     std::vector<uint32_t> amax((size_t)n * 4, 0u);
     std::vector<unsigned long long> cnt((size_t)n * kStatsPerTensor, 0ull);
     std::vector<TensorDesc> desc((size_t)n);
