@@ -274,6 +274,13 @@ int fp8adam_encode_sr(int32_t fmt, const float *x, const uint16_t *r16, uint8_t 
 
 /* ---- measurement ---- */
 
+/* dst[0..bytes) = src[0..bytes) on `stream` with the step kernels' access pattern (16-byte
+ * non-temporal loads and stores, four in flight per lane, 16 KiB per work-group): a plain
+ * streaming copy whose rate is the practical read + write ceiling the step's kernels are
+ * compared with.  src, dst: device, 16-byte aligned, not overlapping; bytes a multiple of
+ * 16 (EINVAL otherwise, EALIGN for misaligned pointers). */
+int fp8adam_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
 /* Enable (1) or disable (0) per-kernel timing with HIP events around every
  * launch of later steps (creates the events; may allocate).  Timing records
  * at most 4096 launches between two fp8adam_kernel_times calls. */

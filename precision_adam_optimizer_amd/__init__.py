@@ -43,7 +43,7 @@ KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "st
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
-           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr")
+           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy")
 
 
 class Fp8AdamError(RuntimeError):
@@ -127,10 +127,11 @@ def load() -> ctypes.CDLL:
     L.fp8adam_current_buffer.restype = i32
     L.fp8adam_encode_sr_bits_range.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, vp, vp]
     L.fp8adam_encode_sr.argtypes = [i32, vp, vp, vp, i64, vp]
+    L.fp8adam_stream_copy.argtypes = [vp, vp, i64, vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
                  "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
                  "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
-                 "fp8adam_encode_sr"):
+                 "fp8adam_encode_sr", "fp8adam_stream_copy"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -231,6 +232,13 @@ def fp8adam_encode_sr(fmt: int, x: torch.Tensor, r16: torch.Tensor, out: torch.T
     assert r16.numel() == x.numel() and out.numel() >= x.numel()
     _check(load().fp8adam_encode_sr(fmt, _ptr(x), _ptr(r16), _ptr(out), x.numel(),
                                     current_stream() if stream is None else stream))
+
+
+def fp8adam_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream: int | None = None) -> None:
+    assert src.is_contiguous() and dst.is_contiguous()
+    nbytes = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nbytes
+    _check(load().fp8adam_stream_copy(_ptr(src), _ptr(dst), nbytes, current_stream() if stream is None else stream))
 
 
 def fp8adam_set_timing(ctx: int, enable: bool) -> None:

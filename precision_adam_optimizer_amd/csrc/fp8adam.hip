@@ -238,6 +238,25 @@ __global__ __launch_bounds__(kThreads) void k_encode_sr_bits(uint32_t start, int
   }
 }
 
+// Streaming copy with the step kernels' access pattern (16-byte non-temporal
+// loads and stores, four per lane in flight, 16 KiB per one-shot work-group):
+// the box's practical ceiling for a read + write stream, measured beside the step.
+__global__ __launch_bounds__(kThreads) void k_stream_copy(const vu4* __restrict__ src, vu4* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * (4 * kThreads) + threadIdx.x;
+  vu4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n16) x[u] = ld_stream<vu4, true>(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int64_t i = base + (int64_t)u * kThreads;
+    if (i < n16) st_stream<vu4, true>(dst + i, x[u]);
+  }
+}
+
 // A fresh optimizer state's scales and history (fp8adam_config.zero_state): one
 // work-group per tensor writes 1.0 into every scale slot of m and v and zeroes
 // the 2H-entry amax history; the codes are cleared with a memset.
@@ -718,6 +737,20 @@ int fp8adam_encode_sr(int32_t fmt, const float* x, const uint16_t* r16, uint8_t*
     hipLaunchKernelGGL(k_encode_sr<0>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, x, r16, out, n);
   else
     hipLaunchKernelGGL(k_encode_sr<1>, dim3(probe_grid(n, 1)), dim3(kThreads), 0, stream, x, r16, out, n);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (bytes < 0 || (bytes & 15) || (bytes > 0 && (!src || !dst)))
+    return fail(FP8ADAM_EINVAL, "bytes must be a non-negative multiple of 16 with non-null pointers");
+  if (((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return fail(FP8ADAM_EALIGN, "src and dst must be 16-byte aligned");
+  if (bytes == 0) return 0;
+  const int64_t n16 = bytes / 16;
+  const int64_t groups = (n16 + 4 * kThreads - 1) / (4 * kThreads);
+  if (groups > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "copy too large");
+  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)groups), dim3(kThreads), 0, stream, static_cast<const vu4*>(src),
+                     static_cast<vu4*>(dst), n16);
   HIP_TRY(hipGetLastError());
   return 0;
 }

@@ -72,6 +72,10 @@ def test_error_paths_without_a_gpu():
     assert L.fp8adam_encode_sr(0, None, None, None, -1, None) == -1
     assert L.fp8adam_encode_sr(0, None, None, None, 8, None) == -1
     assert L.fp8adam_encode_sr(1, None, None, None, 0, None) == 0  # empty: nothing to do
+    assert L.fp8adam_stream_copy(None, None, 24, None) == -1        # not a multiple of 16
+    assert L.fp8adam_stream_copy(None, None, 32, None) == -1        # null pointers
+    assert L.fp8adam_stream_copy(8, 16, 32, None) == -2             # misaligned
+    assert L.fp8adam_stream_copy(None, None, 0, None) == 0
     assert L.fp8adam_num_chunks(None) == -1
     amp = pk.AmpConfigArg(1.0, 2.0, 0.5, 2000)
     assert L.fp8adam_step_amp(None, ctypes.byref(hp), ctypes.byref(amp), 64, None) == -1

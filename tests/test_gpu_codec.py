@@ -152,3 +152,16 @@ def test_encode_sr_every_r16_on_sampled_values(fmt):
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, (f"{bad.size} codes differ; first x={x_all[bad[0]]!r} r16={int(r_all[bad[0]]):#06x}: "
                            f"gpu {got[bad[0]]:#04x} oracle {want[bad[0]]:#04x}")
+
+
+def test_stream_copy_copies_every_byte():
+    """The bandwidth probe the benchmark compares the step with is a real copy:
+    sizes around its 16 KiB work-group tile, and the destination's bytes past
+    the copied range stay untouched."""
+    for nbytes in (16, 4096, 16384 - 16, 16384, 16384 + 16, 3 * 16384 + 4096 + 48, 1 << 22):
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+        dst = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+        pk.fp8adam_stream_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes], src), nbytes
+        assert bool((dst[nbytes:] == 0xA5).all()), nbytes
