@@ -1,7 +1,8 @@
 // fp8adam.hip -- FP8-moment Adam/AdamW step for AMD MI355X (gfx950): the C
 // ABI declared in include/fp8adam.h, the loss-scaling kernels (gradient norm
-// and the scaler's decision) and the codec probes.  The step kernels and their
-// dispatch are in fp8adam_engine.h, instantiated in fp8adam_step_*.hip.
+// and the scaler's decision), the fresh-state kernel of zero_state, the codec
+// probes and the streaming-copy probe.  The step kernels and their dispatch
+// are in fp8adam_engine.h, instantiated in fp8adam_step_*.hip.
 
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -19,6 +19,7 @@
 //     k_update  : recompute m', v' with the staged old scales; update p;
 //                 requantize m', v' with the new scales and saturation
 //   per-tensor scales, speculative schedule (bit-identical results)
+//     k_spec_prepare : per tensor, stage the old scales and the predicted ones
 //     k_update<kModeSpec> : one pass that quantizes with a predicted scale,
 //                 writes the codes into the other code buffer (ping-pong),
 //                 updates p and records per-part amax partials
@@ -27,7 +28,8 @@
 //     k_fixup   : flagged tensors only: recompute the moment from the old
 //                 codes (still intact in the source buffer) and requantize
 //   per-tensor delayed scaling (scale from an amax history)
-//     k_update<kModeDelayed>, k_delayed_reduce
+//     k_delayed_prepare (scales from the history), k_update<kModeDelayed>,
+//     k_delayed_reduce (commit the scales, record this step's amax)
 //   per-128-element scales (one pass)
 //     k_block   : 32 lanes own one 128-element block; the block amax is a
 //                 5-step DPP/swizzle max, then update and requantize as above
