@@ -276,10 +276,12 @@ def test_llama2_7b_block128_full_size():
 
 @pytest.mark.timeout(1200)
 def test_llama2_13b_bf16_master_full_size():
+    """The 13B list as benchmarked: bf16 master, speculative schedule (step 1
+    two-pass, steps 2-5 speculative, with the bf16 master's 2048-element parts)."""
     w = workloads.llama2_13b_bf16()
     n = len(w.shapes)
     sample = _layer_indices(40, [0]) + [n - 2, n - 1]
-    run_full(w, steps=5, sample=sample)
+    run_full(w, steps=5, sample=sample, schedule="speculative", speculate_from_step=2)
 
 
 @pytest.mark.timeout(300)
