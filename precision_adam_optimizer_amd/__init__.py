@@ -372,6 +372,19 @@ class FP8AdamW:
     def v(self) -> list:
         return self._v[self.current_buffer]
 
+    def checkpoint(self) -> list:
+        """Copies of the whole optimizer state in the form ``state=`` takes:
+        [m, v, m_scale, v_scale] (m and v from the pair that holds the moments),
+        plus the amax histories with delayed scaling.  Together with the master
+        weights (and, for step_amp, the loss-scaler state) it resumes bit for bit."""
+        with torch.cuda.device(self.device):
+            torch.cuda.current_stream().synchronize()
+            out = [[x.clone() for x in self.m], [x.clone() for x in self.v],
+                   [x.clone() for x in self.m_scale], [x.clone() for x in self.v_scale]]
+            if self.amax_history[0] is not None:
+                out.append([x.clone() for x in self.amax_history])
+        return out
+
     def step(self, *, lr: float, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
              weight_decay: float = 0.0, step: int) -> None:
         with torch.cuda.device(self.device):

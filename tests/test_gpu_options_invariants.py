@@ -89,10 +89,8 @@ def test_resume_with_options_is_bit_exact(case):
         _load(grads, t, scale_of(amp), inf_at=2 if amp_on else None)
         call(opt, amp, t, grads)
     torch.cuda.synchronize()
-    state = [[x.clone() for x in opt.m], [x.clone() for x in opt.v], [x.clone() for x in opt.m_scale],
-             [x.clone() for x in opt.v_scale]]
-    if kw["scaling"] == "delayed":
-        state.append([x.clone() for x in opt.amax_history])
+    state = opt.checkpoint()
+    assert len(state) == (5 if kw["scaling"] == "delayed" else 4)
     p2 = [p.clone() for p in params]
     amp2 = amp.clone() if amp_on else None
     opt.close()
