@@ -51,6 +51,7 @@ class Config(ctypes.Structure):
         ("history_len", ctypes.c_int), ("margin", ctypes.c_int), ("delayed_from", ctypes.c_int64),
         ("grad_factor", ctypes.c_float), ("sched_step", ctypes.c_int64),
         ("stochastic", ctypes.c_int), ("tensor_index", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+        ("update_from_codes", ctypes.c_int),
     ]
 
 
@@ -190,13 +191,16 @@ class Hyper:
 def make_config(h: Hyper, m_fmt=E4M3, v_fmt=E5M2, block: int = 0,
                 scale_mode: int = SCALE_POW2, master_bf16: bool = False, l2_coupled: bool = False,
                 history_len: int = 0, margin: int = 0, delayed_from: int = 2, grad_factor: float = 1.0,
-                sched_step: int = 0, stochastic: bool = False, tensor_index: int = 0, seed: int = 0) -> Config:
+                sched_step: int = 0, stochastic: bool = False, tensor_index: int = 0, seed: int = 0,
+                update_from_codes: bool = False) -> Config:
     """history_len > 0 selects delayed scaling (per-tensor scales only); grad_factor
     multiplies every gradient first; sched_step (0: h.step) is the step number
-    compared with delayed_from."""
+    compared with delayed_from; update_from_codes selects the other reading of the
+    update order (p from the new codes instead of the fresh moments; study only)."""
     return Config(h.lr, h.beta1, h.beta2, h.eps, h.weight_decay, h.step,
                   fmt_id(m_fmt), fmt_id(v_fmt), block, scale_mode, int(master_bf16), int(l2_coupled),
-                  history_len, margin, delayed_from, grad_factor, sched_step, int(stochastic), tensor_index, seed)
+                  history_len, margin, delayed_from, grad_factor, sched_step, int(stochastic), tensor_index, seed,
+                  int(update_from_codes))
 
 
 def step(cfg: Config, p: np.ndarray, g_bits: np.ndarray, cm: np.ndarray, cv: np.ndarray,

@@ -321,6 +321,9 @@ typedef struct {
     int stochastic;       /* 0: round to nearest even; 1: stochastic rounding of both moments */
     uint32_t tensor_index;/* stochastic: the tensor's position in its list (part of the counter) */
     uint64_t seed;        /* stochastic: the generator's key */
+    int update_from_codes;/* 0 (the contract): p is updated from the fresh fp32 m', v'.  1 (the
+                             other reading of the update order, for study only): from the new
+                             codes dequantized with the new scales */
 } ref_config;
 
 typedef struct {
@@ -478,13 +481,18 @@ int ref_step_hist(const ref_config *c, int64_t n, void *p, const uint16_t *g,
             if (fabsf(qv) > fmax_v) s.saturated_v++;
             if (!isfinite(m1[i]) || !isfinite(v1[i])) s.nonfinite++;
 
+            float um = m1[i], uv = v1[i];
+            if (c->update_from_codes) {
+                um = ref_decode(c->m_fmt, cm[i]) * nsm;
+                uv = ref_decode(c->v_fmt, cv[i]) * nsv;
+            }
             if (c->master_bf16) {
                 uint16_t *pb = (uint16_t *)p;
-                double np = param_update(&k, (double)bf16_to_f32(pb[i]), m1[i], v1[i]);
+                double np = param_update(&k, (double)bf16_to_f32(pb[i]), um, uv);
                 pb[i] = ref_double_to_bf16(np);
             } else {
                 float *pf = (float *)p;
-                pf[i] = (float)param_update(&k, (double)pf[i], m1[i], v1[i]);
+                pf[i] = (float)param_update(&k, (double)pf[i], um, uv);
             }
         }
 

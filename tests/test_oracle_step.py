@@ -158,6 +158,45 @@ def test_exact_fp8_trajectory_dyadic():
     assert seen[5][4]["amax_v"] == 1.0
 
 
+def test_update_from_codes_reading_on_the_dyadic_trajectory():
+    """The other reading of the update order (an oracle flag for study, outside
+    the contract): p moves with the stored moments, code x new scale, instead
+    of the fresh m', v'.  On the dyadic trajectory above the stored values are
+    known by hand (m: 0.5, 0.75, 0.875, 0.9375, 1.0; v: 0.5, 0.75, 0.875, 1.0,
+    1.0), so each update is lr * (m/(1-2^-t)) / (sqrt(v/(1-2^-t)) + eps); it
+    equals the contract's reading while the moments are stored exactly (t <= 3)
+    and departs from it once a tie rounds v (t = 4) and then m (t = 5)."""
+    lr, eps = 1e-3, 1e-8
+    stored_m = [0.5, 0.75, 0.875, 0.9375, 1.0]
+    stored_v = [0.5, 0.75, 0.875, 1.0, 1.0]
+    # the fresh moments: 0.5 * (stored value of the step before) + 0.5
+    fresh_m = [0.5, 0.75, 0.875, 0.9375, 0.96875]
+    fresh_v = [0.5, 0.75, 0.875, 0.9375, 1.0]
+    runs = {}
+    for flag in (False, True):
+        h = oracle.Hyper(lr=lr, beta1=0.5, beta2=0.5, eps=eps, weight_decay=0.0)
+        p = np.zeros(1, np.float32)
+        g = bf16_bits([1.0])
+        cm, cv = np.zeros(1, np.uint8), np.zeros(1, np.uint8)
+        sm, sv = np.ones(1, np.float32), np.ones(1, np.float32)
+        deltas = []
+        for t in range(1, 6):
+            h.step = t
+            before = float(p[0])
+            oracle.step(oracle.make_config(h, update_from_codes=flag), p, g, cm, cv, sm, sv)
+            deltas.append(before - float(p[0]))
+        runs[flag] = deltas
+    for t in range(1, 6):
+        bc = 1.0 - 0.5 ** t
+        want_b = lr * (stored_m[t - 1] / bc) / (math.sqrt(stored_v[t - 1] / bc) + eps)
+        want_a = lr * (fresh_m[t - 1] / bc) / (math.sqrt(fresh_v[t - 1] / bc) + eps)
+        assert runs[True][t - 1] == pytest.approx(want_b, rel=1e-5), t
+        assert runs[False][t - 1] == pytest.approx(want_a, rel=1e-5), t
+    assert runs[True][:3] == pytest.approx(runs[False][:3], rel=1e-6)
+    assert abs(runs[True][3] - runs[False][3]) > 0.02 * lr   # t = 4: v rounded up by a tie
+    assert abs(runs[True][4] - runs[False][4]) > 0.01 * lr   # t = 5: m rounded up by a tie
+
+
 # --------------------------------------------------- exact-rational referee
 
 def _rand_case(n, seed, m_fmt, v_fmt, block, amax_mode, bf16_master):
