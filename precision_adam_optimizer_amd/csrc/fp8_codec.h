@@ -14,15 +14,55 @@
 namespace fp8adam {
 
 // FMAX = 0.875 * 2^kMaxExp for both formats: 448 = 0.875 * 2^9, 57344 = 0.875 * 2^16.
+// kMantBits: mantissa field width; kMaxCode: the code of +FMAX.
 template <int FMT> struct Format;
 template <> struct Format<0> {  // E4M3
   static constexpr float kMax = 448.0f;
   static constexpr int kMaxExp = 9;
+  static constexpr int kMantBits = 3;
+  static constexpr uint32_t kMaxCode = 0x7Eu;
 };
 template <> struct Format<1> {  // E5M2
   static constexpr float kMax = 57344.0f;
   static constexpr int kMaxExp = 16;
+  static constexpr int kMantBits = 2;
+  static constexpr uint32_t kMaxCode = 0x7Bu;
 };
+
+// Re-express four codes quantized with the power-of-two scale 2^a in the scale
+// 2^b (d = b - a, nonzero) by moving each exponent field down by d.  Where the
+// code lies strictly between the smallest normal and FMAX, before and after the
+// move, the unrounded value was a normal FP8 number at both scales (only the
+// smallest-normal code can come from a subnormal value rounded up, and a code
+// above it after the move leaves the value normal even if it was rounded up
+// from the binade below), and multiplying by a power of two keeps the
+// significand: rounding to nearest even, or stochastic rounding with the same
+// random bits, then keeps the same mantissa bits in the other binade.  With
+// zero_ok (the values shrink, d > 0, under round-to-nearest) a zero code stays
+// itself: the value was at most half the smallest subnormal and only gets
+// smaller.  Returns false if any of the four needs the value itself: a zero
+// (unless zero_ok), subnormal or smallest-normal code, the FMAX code (which may
+// hold a saturated value), a NaN/Inf code, or a result outside that range.
+template <int FMT>
+__device__ __forceinline__ bool shift_codes4(uint32_t w, int d, bool zero_ok, uint32_t& out) {
+  constexpr int kMinNormal = 1 << Format<FMT>::kMantBits;
+  constexpr int kTop = (int)Format<FMT>::kMaxCode;
+  const int step = d * kMinNormal;  // d in exponent units, as a code difference
+  bool ok = true;
+  uint32_t r = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint32_t b = (w >> (8 * j)) & 0xFFu;
+    const int mag = (int)(b & 0x7Fu);
+    const int nm = mag - step;
+    const bool keep_zero = zero_ok && mag == 0;
+    const bool normal = mag > kMinNormal && mag < kTop && nm > kMinNormal && nm < kTop;
+    ok = ok && (keep_zero || normal);
+    r |= ((b & 0x80u) | (keep_zero ? 0u : ((uint32_t)nm & 0x7Fu))) << (8 * j);
+  }
+  out = r;
+  return ok;
+}
 
 // Four codes packed little-endian in a dword -> four floats (exact).
 template <int FMT>

@@ -893,52 +893,66 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
 }
 
 // One work-group per chunk of a flagged tensor (the others return at once):
-// recompute the mispredicted moment(s) from the gradient and the old codes in
-// the source buffer and requantize them with the true scales into the
-// destination buffer.  p is not touched: its update does not depend on the
-// scales.  Flag bit 0: m, bit 1: v.
+// bring the mispredicted moment(s) in the destination buffer to the true
+// scale.  Both scales are powers of two, so most codes only need their
+// exponent field moved (shift_codes4: 1 byte read and written per element);
+// a group of four with a code that cannot be moved exactly (zero, subnormal,
+// FMAX) is recomputed from the gradient and the old codes still intact in the
+// source buffer and requantized with the true scale.  p is not touched: its
+// update does not depend on the scales.  Flag bit 0: m, bit 1: v.
+template <int FMT, bool STATS, bool IS_V, bool SR>
+__device__ __forceinline__ uint32_t recompute4(const StepConsts& c, int tid, const TensorDesc& d, int64_t i,
+                                               float s_old, float inv_new, uint32_t& under, uint32_t& sat) {
+  const vu2 gg = ld_global<vu2>(d.g + i);
+  const uint32_t cc = ld_global<uint32_t>((IS_V ? d.v : d.m) + i);
+  const float g[4] = {bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
+  float x[4], q[4];
+  decode4<FMT>(cc, x);
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    float m1, v1;
+    // moment_update computes both moments; only the one being fixed is used
+    moment_update(c, g[j] * c.gfac, x[j] * s_old, x[j] * s_old, m1, v1);
+    x[j] = IS_V ? v1 : m1;
+    q[j] = x[j] * inv_new;
+  }
+  uint32_t rw[4];
+  sr_words<SR>(c, tid, i, rw);
+  const uint32_t w = quant4<FMT, SR, IS_V>(q, rw);
+  if constexpr (STATS) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      under += (x[j] != 0.0f && ((w >> (8 * j)) & 0x7Fu) == 0u);
+      sat += (fabsf(q[j]) > Format<FMT>::kMax);
+    }
+  }
+  return w;
+}
+
 template <int FMT, bool STATS, bool IS_V, bool SR>
 __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const TensorDesc& d, uint8_t* dst,
-                                             int64_t start, int64_t end, float s_old, float inv_new,
-                                             uint32_t& under, uint32_t& sat) {
-  const uint8_t* src = IS_V ? d.v : d.m;
+                                             int64_t start, int64_t end, float s_old, uint32_t pred_bits,
+                                             float s_new, float inv_new, uint32_t& under, uint32_t& sat) {
+  // exponent difference of the two powers of two; zero codes stay zero when the
+  // values shrink, except where a zero must be checked against its value (the
+  // underflow count) or may round up stochastically
+  const int dexp = (int)(__float_as_uint(s_new) >> 23) - (int)(pred_bits >> 23);
+  const bool zero_ok = !SR && !STATS && dexp > 0;
   const int64_t gend = start + ((end - start) & ~(int64_t)3);
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
-    vu2 gg[kAmaxUnroll];
     uint32_t cc[kAmaxUnroll];
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        gg[u] = ld_stream<vu2, FP8ADAM_NT_AMAX != 0>(d.g + i);
-        cc[u] = ld_stream<uint32_t, FP8ADAM_NT_AMAX != 0>(src + i);
-      }
+      if (i < gend) cc[u] = ld_stream<uint32_t, FP8ADAM_NT_AMAX != 0>(dst + i);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
       if (i < gend) {
-        const float g[4] = {bf16_lo(gg[u].x), bf16_hi(gg[u].x), bf16_lo(gg[u].y), bf16_hi(gg[u].y)};
-        float x[4], q[4];
-        decode4<FMT>(cc[u], x);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          float m1, v1;
-          // moment_update computes both moments; only the one being fixed is used
-          moment_update(c, g[j] * c.gfac, x[j] * s_old, x[j] * s_old, m1, v1);
-          x[j] = IS_V ? v1 : m1;
-          q[j] = x[j] * inv_new;
-        }
-        uint32_t rw[4];
-        sr_words<SR>(c, tid, i, rw);
-        const uint32_t w = quant4<FMT, SR, IS_V>(q, rw);
-        if constexpr (STATS) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            under += (x[j] != 0.0f && ((w >> (8 * j)) & 0x7Fu) == 0u);
-            sat += (fabsf(q[j]) > Format<FMT>::kMax);
-          }
-        }
+        uint32_t w;
+        if (!shift_codes4<FMT>(cc[u], dexp, zero_ok, w))
+          w = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i, s_old, inv_new, under, sat);
         st_global<uint32_t>(dst + i, w);
       }
     }
@@ -946,7 +960,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
     const float g = load_g1(d, i) * c.gfac;
-    const float x0 = decode1<FMT>(ld_global<uint8_t>(src + i)) * s_old;
+    const float x0 = decode1<FMT>(ld_global<uint8_t>((IS_V ? d.v : d.m) + i)) * s_old;
     float m1, v1;
     moment_update(c, g, x0, x0, m1, v1);
     const float x = IS_V ? v1 : m1;
@@ -981,14 +995,14 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
   if (f & 1) {
     float s, inv;
     choose_scale<MF, 0>(amax[2 * tid], s, inv);
-    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[4 * tid], inv, cnt[kUnderM],
-                                   cnt[kSatM]);
+    fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[4 * tid],
+                                       __float_as_uint(old_scale[4 * tid + 2]), s, inv, cnt[kUnderM], cnt[kSatM]);
   }
   if (f & 2) {
     float s, inv;
     choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
-    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[4 * tid + 1], inv, cnt[kUnderV],
-                                  cnt[kSatV]);
+    fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[4 * tid + 1],
+                                      __float_as_uint(old_scale[4 * tid + 3]), s, inv, cnt[kUnderV], cnt[kSatV]);
   }
   flush_counters<STATS>(counters, tid, cnt);
 }

@@ -27,20 +27,34 @@ def drifting_grad(n, seed, t, i, dev):
     return (random_grad(n, seed * 7 + t * 13 + i, dev).float() * 2.0 ** shift).to(torch.bfloat16)
 
 
-def _run(schedule, sizes, steps, seed, master=torch.float32, spec_from=2):
+def sparse_drifting_grad(n, seed, t, i, dev):
+    """drifting_grad with a wide spread of magnitudes (a factor 10^U(-6, 0) per
+    element) and 2% exact zeros, so the moments hold zero, subnormal and
+    smallest-normal codes as well as ordinary ones."""
+    g = torch.Generator()
+    g.manual_seed(seed * 1000 + t * 37 + i + 5)
+    spread = torch.pow(10.0, -6.0 * torch.rand(n, generator=g))
+    keep = (torch.rand(n, generator=g) >= 0.02).float()
+    return (drifting_grad(n, seed, t, i, dev).float() * (spread * keep).to(dev)).to(torch.bfloat16)
+
+
+def _run(schedule, sizes, steps, seed, master=torch.float32, spec_from=2, collect_stats=True, grad_fn=None,
+         rounding="nearest"):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     params = [(torch.randn(n, generator=gen, device=dev) * 0.02).to(master) for n in sizes]
     grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in sizes]
-    opt = pk.FP8AdamW(params, grads, collect_stats=True, schedule=schedule, speculate_from_step=spec_from)
+    opt = pk.FP8AdamW(params, grads, collect_stats=collect_stats, schedule=schedule, speculate_from_step=spec_from,
+                      rounding=rounding, seed=11)
+    grad_fn = grad_fn or drifting_grad
     hist = []
     for t in range(1, steps + 1):
         for i, n in enumerate(sizes):
-            grads[i].copy_(drifting_grad(n, seed, t, i, dev))
+            grads[i].copy_(grad_fn(n, seed, t, i, dev))
         opt.step(step=t, **HP)
         torch.cuda.synchronize()
-        st = opt.stats()
+        st = opt.stats() if collect_stats else None
         hist.append(([np_host(p) for p in params], [np_host(m) for m in opt.m], [np_host(v) for v in opt.v],
                      [np_host(s) for s in opt.m_scale], [np_host(s) for s in opt.v_scale], st))
     opt.close()
@@ -69,6 +83,32 @@ def test_speculative_equals_two_pass_bitwise(master):
             clean_steps += rq < 2 * sum(sizes)  # (element, moment) pairs
     # both paths of the speculative schedule ran
     assert requant_steps > 0 and clean_steps > 0
+
+
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+@pytest.mark.parametrize("master", [torch.float32, torch.bfloat16])
+def test_speculative_equals_two_pass_without_stats(master, rounding):
+    """The fix-up without the stats counters (where a zero code of a shrinking
+    moment is kept as it is under round-to-nearest), on moments full of zero,
+    subnormal and smallest-normal codes: bit-identical to the two-pass
+    schedule in every step."""
+    sizes = SIZES + [300_001, 65_536]
+    a = _run("two_pass", sizes, 10, seed=8, master=master, collect_stats=False, grad_fn=sparse_drifting_grad,
+             rounding=rounding)
+    b = _run("speculative", sizes, 10, seed=8, master=master, collect_stats=False, grad_fn=sparse_drifting_grad,
+             rounding=rounding)
+    moved = 0
+    for t, (x, y) in enumerate(zip(a, b), start=1):
+        for kind, xs, ys in zip(("p", "m", "v", "m_scale", "v_scale"), x[:5], y[:5]):
+            for i, (u, w) in enumerate(zip(xs, ys)):
+                assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), f"step {t}: {kind} of tensor {i} differs"
+        if t >= 2:  # scales that changed from step to step: the fix-up's cases
+            moved += sum(int(x[3][i][0] != a[t - 2][3][i][0]) + int(x[4][i][0] != a[t - 2][4][i][0])
+                         for i in range(len(sizes)))
+    assert moved > 0
+    # the moments hold the codes the fix-up must recompute rather than move
+    m_all = np.concatenate(b[-1][1])
+    assert (m_all & 0x7F == 0).any() and ((m_all & 0x7F) < 8).any()
 
 
 SPEC_COMBOS = list(itertools.product(FORMATS, ["fp32", "bf16"]))
