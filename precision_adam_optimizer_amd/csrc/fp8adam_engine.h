@@ -938,24 +938,41 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
   // underflow count) or may round up stochastically
   const int dexp = (int)(__float_as_uint(s_new) >> 23) - (int)(pred_bits >> 23);
   const bool zero_ok = !SR && !STATS && dexp > 0;
-  const int64_t gend = start + ((end - start) & ~(int64_t)3);
-  for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
-    uint32_t cc[kAmaxUnroll];
+  // 16 codes per lane per access (a byte stream: wide accesses), then groups
+  // of 4 and single elements for the last < 16 of the tensor
+  constexpr int kWide = 16;
+  constexpr int kWideUnroll = 4;
+  const int64_t wend = start + ((end - start) & ~(int64_t)(kWide - 1));
+  for (int64_t base = start + kWide * threadIdx.x; base < wend; base += (int64_t)kWide * kThreads * kWideUnroll) {
+    vu4 cc[kWideUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) cc[u] = ld_stream<uint32_t, FP8ADAM_NT_AMAX != 0>(dst + i);
+    for (int u = 0; u < kWideUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kWide * kThreads;
+      if (i < wend) cc[u] = ld_stream<vu4, FP8ADAM_NT_AMAX != 0>(dst + i);
     }
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; u++) {
-      const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) {
-        uint32_t w;
-        if (!shift_codes4<FMT>(cc[u], dexp, zero_ok, w))
-          w = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i, s_old, inv_new, under, sat);
-        st_global<uint32_t>(dst + i, w);
+    for (int u = 0; u < kWideUnroll; u++) {
+      const int64_t i = base + (int64_t)u * kWide * kThreads;
+      if (i < wend) {
+        vu4 w;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          uint32_t x;
+          if (!shift_codes4<FMT>(cc[u][k], dexp, zero_ok, x))
+            x = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i + 4 * k, s_old, inv_new, under, sat);
+          w[k] = x;
+        }
+        st_global<vu4>(dst + i, w);
       }
     }
+  }
+  const int64_t gend = wend + ((end - wend) & ~(int64_t)3);
+  if (threadIdx.x < kWide / 4 && wend + 4 * (int64_t)threadIdx.x < gend) {
+    const int64_t i = wend + 4 * (int64_t)threadIdx.x;
+    uint32_t w;
+    if (!shift_codes4<FMT>(ld_global<uint32_t>(dst + i), dexp, zero_ok, w))
+      w = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i, s_old, inv_new, under, sat);
+    st_global<uint32_t>(dst + i, w);
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
