@@ -225,7 +225,7 @@ struct StepConsts {
   float step_size;     // lr / (1 - beta1^t)
   float inv_bc2;       // 1 / (1 - beta2^t)
   float eps;
-  float grow_m, grow_v; // speculative schedule: expected amax growth (1-beta^t)/(1-beta^(t-1))
+  float grow_m, grow_v; // speculative schedule: predicted amax growth from step t-1 to t
   float gfac;          // factor applied to every bf16 gradient first (1; loss-scale unscaling and clipping)
   uint32_t seed_lo, seed_hi;  // stochastic rounding: the generator's key
   uint32_t rng_t;      // stochastic rounding: the step t in the generator's counter

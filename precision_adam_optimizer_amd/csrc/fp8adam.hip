@@ -39,6 +39,21 @@ int hip_fail(hipError_t e, const char* what) {
 
 namespace {
 
+// Speculative schedule: the predicted growth of a tensor's amax from step t-1
+// to step t (t >= 2; 1 at t = 1), the geometric mean of two models of a moving
+// average with factor beta: its mean under a steady gradient grows as
+// (1 - beta^t) / (1 - beta^(t-1)); its spread under independent noise grows as
+// the square root of the same ratio taken at beta^2.  Gradients lie between
+// the two; the blend keeps the share of mispredicted scales low for both.
+__host__ __device__ inline float amax_growth(double beta, double t) {
+  const double mean_prev = 1.0 - pow(beta, t - 1.0);
+  const double var_prev = 1.0 - pow(beta * beta, t - 1.0);
+  if (!(mean_prev > 0.0) || !(var_prev > 0.0)) return 1.0f;
+  const double mean_growth = (1.0 - pow(beta, t)) / mean_prev;
+  const double spread_growth = sqrt((1.0 - pow(beta * beta, t)) / var_prev);
+  return (float)sqrt(mean_growth * spread_growth);
+}
+
 // ------------------------------------------- loss scaling and clipping
 //
 // k_gradnorm: one work-group per chunk reads the bf16 gradients only (2 bytes
@@ -178,13 +193,12 @@ __global__ __launch_bounds__(kReduceThreads) void k_gradctl(const double* __rest
     st_global(&st->growth_tracker, next);
   }
   const double bc1 = 1.0 - pow((double)beta1, (double)t), bc2 = 1.0 - pow((double)beta2, (double)t);
-  const double bc1p = 1.0 - pow((double)beta1, (double)(t - 1)), bc2p = 1.0 - pow((double)beta2, (double)(t - 1));
   st_global(&ctl->skip, 0);
   st_global(&ctl->gfac, gfac);
   st_global(&ctl->step_size, (float)((double)lr / bc1));
   st_global(&ctl->inv_bc2, (float)(1.0 / bc2));
-  st_global(&ctl->grow_m, bc1p > 0.0 ? (float)(bc1 / bc1p) : 1.0f);
-  st_global(&ctl->grow_v, bc2p > 0.0 ? (float)(bc2 / bc2p) : 1.0f);
+  st_global(&ctl->grow_m, amax_growth((double)beta1, (double)t));
+  st_global(&ctl->grow_v, amax_growth((double)beta2, (double)t));
   st_global(&ctl->hist_slot, hist_len > 0 ? (int32_t)((t - 1) % hist_len) : 0);
   st_global(&ctl->t, (uint32_t)t);
 }
@@ -538,12 +552,9 @@ int step_consts(const fp8adam_ctx* ctx, const fp8adam_hparams* hp, StepConsts& k
     k.step_size = (float)((double)hp->lr / bc1);
     k.inv_bc2 = (float)(1.0 / bc2);
     k.eps = hp->eps;
-    // growth of a moving average's bias (1 - beta^t) from step t-1 to t: the
-    // speculative schedule's prediction of how the amax moves
-    const double bc1_prev = 1.0 - pow((double)hp->beta1, (double)(hp->step - 1));
-    const double bc2_prev = 1.0 - pow((double)hp->beta2, (double)(hp->step - 1));
-    k.grow_m = bc1_prev > 0.0 ? (float)(bc1 / bc1_prev) : 1.0f;
-    k.grow_v = bc2_prev > 0.0 ? (float)(bc2 / bc2_prev) : 1.0f;
+    // the speculative schedule's prediction of how each tensor's amax moves
+    k.grow_m = amax_growth((double)hp->beta1, (double)hp->step);
+    k.grow_v = amax_growth((double)hp->beta2, (double)hp->step);
     k.margin_scale = ctx->margin_scale;
     k.hist_len = ctx->hist_len;
     k.hist_slot = ctx->hist_len > 0 ? (int)((hp->step - 1) % ctx->hist_len) : 0;

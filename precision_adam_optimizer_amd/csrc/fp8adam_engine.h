@@ -424,8 +424,8 @@ __device__ __forceinline__ void store_p1(const TensorDesc& d, int64_t i, float x
 }
 
 // Speculative schedule: the predicted scale is the POW2 scale of the previous
-// step's amax times the growth a stationary gradient would give the moving
-// average, (1-beta^t)/(1-beta^(t-1)).  Without a usable previous amax (zero or
+// step's amax times the predicted growth of the moving average from step t-1
+// to t (StepConsts::grow_m / grow_v).  Without a usable previous amax (zero or
 // non-finite) it is the power of two with the exponent of the tensor's current
 // scale (1 if that is zero, subnormal, Inf or NaN).  The update pass and the
 // check evaluate exactly the same expression, so they agree on the prediction.
