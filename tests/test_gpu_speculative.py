@@ -155,6 +155,18 @@ def test_speculative_resume_is_bit_exact():
 
 
 @pytest.mark.timeout(900)
+def test_llama2_7b_bench_configuration_full_size():
+    """The 7B list exactly as the benchmark runs it: speculative schedule from
+    step 4 (steps 1-3 two-pass), stats off (the kernels without counters, where
+    the fix-up keeps a shrinking zero code as it is), fresh gradients per step;
+    sampled tensors against the oracle at every step."""
+    w = workloads.llama2_7b()
+    n = len(w.shapes)
+    sample = [0] + list(range(1 + 9 * 15, 1 + 9 * 16)) + [n - 2, n - 1]
+    run_full(w, steps=7, sample=sample, collect_stats=False, schedule="speculative", speculate_from_step=4)
+
+
+@pytest.mark.timeout(900)
 def test_llama2_7b_speculative_full_size():
     w = workloads.llama2_7b()
     n = len(w.shapes)
