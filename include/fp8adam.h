@@ -180,7 +180,10 @@ typedef struct fp8adam_ctx fp8adam_ctx;
 /* Build a context over n tensors: validates them (EINVAL / EALIGN), builds the
  * multi-tensor chunk table and the per-tensor descriptors on the device
  * (allocates; ENOMEM / EHIP), and synchronizes `stream` before returning.
- * *out receives the handle (NULL on failure).  The device is the current one. */
+ * *out receives the handle (NULL on failure).  The device is the current one.
+ * A context holds at most 16,777,208 * 1024 (about 1.7e10) elements, each tensor
+ * counted in whole chunks, so that every launch fits one grid dimension; a
+ * larger list is split over several contexts (EINVAL otherwise). */
 int fp8adam_init(fp8adam_ctx **out, const fp8adam_tensor *tensors, int32_t n,
                  const fp8adam_config *cfg, hipStream_t stream);
 

@@ -409,8 +409,20 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
 
     // Chunk size: the largest power of two in [2^kMinChunkLog2, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
+    // Every launch must fit one grid dimension of at most 2^32 - 1 work-items:
+    // kMaxGroups work-groups of kThreads (XCD-ordered grids round up to 8), and
+    // the widest grid has one work-group per 2^kUPartLog2Min elements of every
+    // chunk.  That caps a context at about 1.7e10 elements; larger lists are
+    // split over several contexts.
+    constexpr int64_t kMaxGroups = ((int64_t)UINT32_MAX / kThreads) & ~(int64_t)7;
+    constexpr int64_t kMaxElements = kMaxGroups << std::min(kPartLog2, kUPartLog2Min);
     int64_t total = 0;
-    for (int32_t t = 0; t < n; t++) total += tensors[t].numel > 0 ? tensors[t].numel : 0;
+    for (int32_t t = 0; t < n; t++) {
+      total += tensors[t].numel > 0 ? std::min(tensors[t].numel, kMaxElements + 1) : 0;
+      if (total > kMaxElements)
+        return fail(FP8ADAM_EINVAL, "too many elements for one context (at most " + std::to_string(kMaxElements) +
+                                        "); split the tensor list over several contexts");
+    }
     int chunk_log2 = kMaxChunkLog2;
     while (chunk_log2 > kMinChunkLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
     const int64_t chunk = (int64_t)1 << chunk_log2;
@@ -451,8 +463,9 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         desc[(size_t)n + t].m = T.m_alt;
         desc[(size_t)n + t].v = T.v_alt;
       }
-      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2Min))) > (int64_t)INT32_MAX)
-        return fail(FP8ADAM_EINVAL, "too many elements for one context");
+      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2Min))) > kMaxGroups)
+        return fail(FP8ADAM_EINVAL, "too many elements for one context once each tensor is rounded up to whole "
+                                    "chunks; split the tensor list over several contexts");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
       nchunks += nc;
     }

@@ -79,6 +79,15 @@ def test_error_paths_without_a_gpu():
     assert L.fp8adam_num_chunks(None) == -1
     amp = pk.AmpConfigArg(1.0, 2.0, 0.5, 2000)
     assert L.fp8adam_step_amp(None, ctypes.byref(hp), ctypes.byref(amp), 64, None) == -1
+    # a context whose widest launch would exceed one grid dimension (2^32 - 1
+    # work-items): one huge tensor, or a sum of large ones, or one that only
+    # overflows once every tensor is rounded up to whole chunks
+    max_elems = (((1 << 32) - 1) // 256 & ~7) * 1024
+    for sizes in ([max_elems + 1], [max_elems // 2, max_elems // 2 + 64], [1 << 62, 1 << 62],
+                  [32769] * (max_elems // 32769)):  # each rounds up to two 32768-element chunks
+        big = (pk.TensorArg * len(sizes))(*[pk.TensorArg(16, 32, 48, 64, 80, 96, k) for k in sizes])
+        assert L.fp8adam_init(ctypes.byref(h), big, len(sizes), ctypes.byref(cfg), None) == -1
+        assert "too many elements" in pk.fp8adam_last_error()
 
 
 def test_product_path_does_not_import_the_oracle():
