@@ -315,3 +315,51 @@ def test_chunk_size_choice_and_parity(sizes, chunk):
             run_pool(check, list(range(len(sizes))))
     finally:
         opt.close()
+
+
+@pytest.mark.timeout(600)
+def test_flat_block128_tensor_past_2_to_32_elements():
+    """One flat tensor of 2^32 + 2^20 + 333 elements with per-128 block scales
+    (a flat optimizer buffer, as sharded optimizers keep one): element, block,
+    part and chunk indices all pass 2^31 and 2^32.  Block scales are local, so
+    a block-aligned window is an exact sub-problem: windows at the start,
+    around 2^31 and from just below 2^32 to the ragged end are checked
+    against the oracle over two steps; the stats counters cover the whole
+    tensor (no saturation with power-of-two scales)."""
+    dev = torch.device("cuda")
+    n = (1 << 32) + (1 << 20) + 333
+    piece = 1 << 28
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(21)
+    param = torch.empty(n, device=dev)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for k, a in enumerate(range(0, n, piece)):
+        b = min(n, a + piece)
+        param[a:b].normal_(0.0, 0.02, generator=gen)
+    windows = [(0, 1 << 20), ((1 << 31) - (1 << 19), (1 << 31) + (1 << 19)), ((1 << 32) - (1 << 19), n)]
+    host = [OracleState(np_host(param[a:b]), np.zeros(b - a, np.uint8), np.zeros(b - a, np.uint8),
+                        np.ones(-(-(b - a) // 128), np.float32), np.ones(-(-(b - a) // 128), np.float32))
+            for a, b in windows]
+    opt = pk.FP8AdamW([param], [grad], granularity="block128", collect_stats=True)
+    try:
+        for t in (1, 2):
+            for k, a in enumerate(range(0, n, piece)):
+                b = min(n, a + piece)
+                grad[a:b].copy_(random_grad(b - a, 1000 * t + k, dev))
+            opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            torch.cuda.synchronize()
+            h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            cfg = oracle_config(h, "e4m3", "e5m2", "block128", "pow2", "fp32")
+            for (a, b), st in zip(windows, host):
+                st.step(cfg, np_host(grad[a:b]))
+                compare_tensor(f"window [{a}, {b}) step {t}", st, np_host(param[a:b]), np_host(opt.m[0][a:b]),
+                               np_host(opt.v[0][a:b]), np_host(opt.m_scale[0][a // 128:-(-b // 128)]),
+                               np_host(opt.v_scale[0][a // 128:-(-b // 128)]), "fp32")
+                st.p = np_host(param[a:b]).copy()  # continue from the device's weights (within the bar)
+            s = opt.stats()[0]
+            assert s["saturated_m"] == 0 and s["saturated_v"] == 0 and s["nonfinite"] == 0
+            assert s["underflow_m"] > 0  # the gradients span 8 decades: some moments flush in every step
+    finally:
+        opt.close()
+        del param, grad
+        torch.cuda.empty_cache()
