@@ -363,3 +363,49 @@ def test_flat_block128_tensor_past_2_to_32_elements():
         opt.close()
         del param, grad
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("schedule", ["two_pass", "speculative"])
+def test_flat_per_tensor_past_2_to_32_elements(schedule):
+    """One flat tensor of 2^32 + 2^20 + 333 elements with one scale per moment,
+    in both schedules (stats off, as benchmarked).  The same large gradient
+    (2^13, far above every other one) is planted at the first element of each
+    checked window in every step, so each window's amax of the new moments is
+    the whole tensor's: each window is then an exact sub-problem for the
+    oracle, which is checked over three steps (the speculative schedule from
+    step 2, with the fix-up of the moments whose predicted scale was off)."""
+    dev = torch.device("cuda")
+    n = (1 << 32) + (1 << 20) + 333
+    piece = 1 << 28
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(22)
+    param = torch.empty(n, device=dev)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    for a in range(0, n, piece):
+        param[a:min(n, a + piece)].normal_(0.0, 0.02, generator=gen)
+    windows = [(0, 1 << 20), ((1 << 31) - (1 << 19), (1 << 31) + (1 << 19)), ((1 << 32) - (1 << 19), n)]
+    host = [OracleState(np_host(param[a:b]), np.zeros(b - a, np.uint8), np.zeros(b - a, np.uint8),
+                        np.ones(1, np.float32), np.ones(1, np.float32)) for a, b in windows]
+    opt = pk.FP8AdamW([param], [grad], schedule=schedule, speculate_from_step=2)
+    try:
+        for t in (1, 2, 3):
+            for k, a in enumerate(range(0, n, piece)):
+                b = min(n, a + piece)
+                grad[a:b].copy_(random_grad(b - a, 2000 * t + k, dev))
+            for a, _ in windows:
+                grad[a] = 8192.0
+            opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            torch.cuda.synchronize()
+            h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            cfg = oracle_config(h, "e4m3", "e5m2", "tensor", "pow2", "fp32")
+            for (a, b), st in zip(windows, host):
+                st.step(cfg, np_host(grad[a:b]))
+                compare_tensor(f"{schedule} window [{a}, {b}) step {t}", st, np_host(param[a:b]),
+                               np_host(opt.m[0][a:b]), np_host(opt.v[0][a:b]), np_host(opt.m_scale[0]),
+                               np_host(opt.v_scale[0]), "fp32")
+                st.p = np_host(param[a:b]).copy()  # continue from the device's weights (within the bar)
+    finally:
+        opt.close()
+        del param, grad
+        torch.cuda.empty_cache()
