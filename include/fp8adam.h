@@ -171,8 +171,9 @@ typedef struct {
     int64_t underflow_m, underflow_v; /* nonzero moment stored as a +-0 code */
     int64_t saturated_m, saturated_v; /* |x * inv_s| > FMAX before clamping */
     int64_t nonfinite;                /* elements with a non-finite m' or v' */
-    int64_t requantized;              /* speculative schedule: elements re-quantized because the
-                                         tensor's scale changed (numel or 0); else 0 */
+    int64_t requantized;              /* speculative schedule: (element, moment) pairs brought to the
+                                         true scale because the predicted one was off: numel per
+                                         mispredicted moment (0, numel or 2 numel); else 0 */
 } fp8adam_stats_t;
 
 typedef struct fp8adam_ctx fp8adam_ctx;
