@@ -409,3 +409,46 @@ def test_flat_per_tensor_past_2_to_32_elements(schedule):
         opt.close()
         del param, grad
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["two_pass", "speculative", "block128"])
+def test_zero_gradient_tensors_and_transitions(mode):
+    """Degenerate amax cases in one list, against the oracle at every step:
+    a tensor whose gradient is zero in every step (amax 0: scale 1, zero
+    codes, weights only decayed), one whose gradient is zero for steps 1-4 and
+    random afterwards (under the speculative schedule, from step 2, the first
+    nonzero step is predicted from an amax of 0, so the fix-up recomputes the
+    zero codes), and one that is random for steps 1-3 and zero afterwards (the
+    moments decay)."""
+    dev = torch.device("cuda")
+    sizes = [4099, 70001, 1000]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    params = [torch.randn(n, generator=gen, device=dev) * 0.02 for n in sizes]
+    grads = [torch.zeros(n, dtype=torch.bfloat16, device=dev) for n in sizes]
+    gran = "block128" if mode == "block128" else "tensor"
+    nb = [1 if gran == "tensor" else -(-n // 128) for n in sizes]
+    host = [OracleState(np_host(p), np.zeros(n, np.uint8), np.zeros(n, np.uint8), np.ones(k, np.float32),
+                        np.ones(k, np.float32)) for p, n, k in zip(params, sizes, nb)]
+    opt = pk.FP8AdamW(params, grads, granularity=gran, collect_stats=True,
+                      schedule="speculative" if mode == "speculative" else "two_pass", speculate_from_step=2)
+    try:
+        for t in range(1, 8):
+            grads[0].zero_()
+            grads[1].copy_(random_grad(sizes[1], 500 + t, dev) if t >= 5 else torch.zeros_like(grads[1]))
+            grads[2].copy_(random_grad(sizes[2], 600 + t, dev) if t <= 3 else torch.zeros_like(grads[2]))
+            opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            torch.cuda.synchronize()
+            h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+            cfg = oracle_config(h, "e4m3", "e5m2", gran, "pow2", "fp32")
+            gstats = opt.stats()
+            for i, n in enumerate(sizes):
+                host[i].step(cfg, np_host(grads[i]))
+                name = f"{mode} tensor {i} step {t}"
+                compare_tensor(name, host[i], np_host(params[i]), np_host(opt.m[i]), np_host(opt.v[i]),
+                               np_host(opt.m_scale[i]), np_host(opt.v_scale[i]), "fp32")
+                _compare_stats(name, gstats[i], host[i].stats, gran)
+                upload_params(params[i], host[i])
+            assert (opt.m_scale[0] == 1.0).all() and not opt.m[0].any() and not opt.v[0].any()
+    finally:
+        opt.close()
