@@ -249,8 +249,8 @@ def main():
     # the counters are per kernel instantiation: stochastic rounding has its own
     traffic = load_traffic(w.name, kernel + ("_sr" if args.rounding == "stochastic" else ""))
     # bytes the whole step moved: + the amax pass (g, m, v; and p with coupled L2) in the
-    # two-pass schedule, + the fix-up (g, m, v read, m, v written) of re-quantized tensors
-    # in the speculative one
+    # two-pass schedule; the speculative schedule's fix-up (the codes of mispredicted moments
+    # read and written) is timed separately and reported as fixup_avg_us
     fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
     amax_bpp = 4.0 + ((4.0 if w.master == "fp32" else 2.0) if w.decay_mode == "l2" else 0.0)
     step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass"

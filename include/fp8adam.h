@@ -66,14 +66,15 @@ typedef enum { FP8ADAM_SCALE_POW2 = 0, FP8ADAM_SCALE_AMAX = 1 } fp8adam_scale_mo
 typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master;
 /* How a per-tensor-scaled step is scheduled on the device.  Both give bit-identical results.
  * TWO_PASS: an amax pass over (g, m, v), then the update pass (18 bytes per fp32 parameter).
- * SPECULATIVE: one update pass that quantizes with the power-of-two scale the tensor had
- *   before the step and writes the codes into the other of two code buffers (m/v and
- *   m_alt/v_alt, alternating every step); a per-tensor check then re-quantizes, from the old
- *   codes, only the tensors whose true scale differs (14 bytes per fp32 parameter plus 6 per
- *   re-quantized one).  Needs per-tensor POW2 scales, decoupled decay (the re-quantization
- *   recomputes moments after p is overwritten, and coupled L2 would need the old p) and
- *   m_alt/v_alt; steps with t < speculate_from_step run TWO_PASS in place on the current
- *   buffer. */
+ * SPECULATIVE: one update pass that quantizes with a predicted power-of-two scale (the
+ *   previous step's amax times its expected growth) and writes the codes into the other of
+ *   two code buffers (m/v and m_alt/v_alt, alternating every step); a per-tensor check then
+ *   brings only the moments whose true scale differs to it: most codes just have their
+ *   exponent field moved (2 bytes per element and moment), the few that cannot be moved
+ *   exactly are recomputed from the gradient and the old codes (4 more).  14 bytes per fp32
+ *   parameter plus that.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment
+ *   is formed after p is overwritten, and coupled L2 would need the old p) and m_alt/v_alt;
+ *   steps with t < speculate_from_step run TWO_PASS in place on the current buffer. */
 typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 } fp8adam_schedule;
 /* How weight_decay enters the step.
  * DECOUPLED (AdamW, the zyxy.net code example): p' = p*(1 - lr*wd) - (Adam update).
@@ -293,7 +294,7 @@ int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 /* Per-kernel timing since the last call (or since timing was enabled):
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
- * 6 = speculative scale check, 7 = re-quantization fix-up, 8 = delayed-scaling pass,
+ * 6 = speculative scale check, 7 = speculative fix-up, 8 = delayed-scaling pass,
  * 9 = delayed-scaling commit, 10 = gradient-norm pass, 11 = loss-scale decision,
  * 12 = scale preparation of the speculative and delayed passes),
  * total_ms[k] and count[k].

@@ -1,7 +1,8 @@
-"""The speculative schedule (one update pass quantizing with the previous
+"""The speculative schedule (one update pass quantizing with a predicted
 power-of-two scale into the other code buffer, then a per-tensor check and a
-re-quantization of the tensors whose scale changed) against the two-pass
-schedule (bit for bit) and against the CPU oracle."""
+fix-up that brings the moments whose true scale differs to it, by moving
+exponent fields or recomputing) against the two-pass schedule (bit for bit)
+and against the CPU oracle."""
 import itertools
 
 import numpy as np
