@@ -318,7 +318,8 @@ def test_chunk_size_choice_and_parity(sizes, chunk):
 
 
 @pytest.mark.timeout(600)
-def test_flat_block128_tensor_past_2_to_32_elements():
+@pytest.mark.parametrize("master", ["fp32", "bf16"])
+def test_flat_block128_tensor_past_2_to_32_elements(master):
     """One flat tensor of 2^32 + 2^20 + 333 elements with per-128 block scales
     (a flat optimizer buffer, as sharded optimizers keep one): element, block,
     part and chunk indices all pass 2^31 and 2^32.  Block scales are local, so
@@ -331,7 +332,7 @@ def test_flat_block128_tensor_past_2_to_32_elements():
     piece = 1 << 28
     gen = torch.Generator(device=dev)
     gen.manual_seed(21)
-    param = torch.empty(n, device=dev)
+    param = torch.empty(n, device=dev, dtype=torch.bfloat16 if master == "bf16" else torch.float32)
     grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
     for k, a in enumerate(range(0, n, piece)):
         b = min(n, a + piece)
@@ -349,12 +350,12 @@ def test_flat_block128_tensor_past_2_to_32_elements():
             opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
             torch.cuda.synchronize()
             h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
-            cfg = oracle_config(h, "e4m3", "e5m2", "block128", "pow2", "fp32")
+            cfg = oracle_config(h, "e4m3", "e5m2", "block128", "pow2", master)
             for (a, b), st in zip(windows, host):
                 st.step(cfg, np_host(grad[a:b]))
                 compare_tensor(f"window [{a}, {b}) step {t}", st, np_host(param[a:b]), np_host(opt.m[0][a:b]),
                                np_host(opt.v[0][a:b]), np_host(opt.m_scale[0][a // 128:-(-b // 128)]),
-                               np_host(opt.v_scale[0][a // 128:-(-b // 128)]), "fp32")
+                               np_host(opt.v_scale[0][a // 128:-(-b // 128)]), master)
                 st.p = np_host(param[a:b]).copy()  # continue from the device's weights (within the bar)
             s = opt.stats()[0]
             assert s["saturated_m"] == 0 and s["saturated_v"] == 0 and s["nonfinite"] == 0
@@ -366,8 +367,8 @@ def test_flat_block128_tensor_past_2_to_32_elements():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("schedule", ["two_pass", "speculative"])
-def test_flat_per_tensor_past_2_to_32_elements(schedule):
+@pytest.mark.parametrize("schedule,master", [("two_pass", "fp32"), ("speculative", "fp32"), ("speculative", "bf16")])
+def test_flat_per_tensor_past_2_to_32_elements(schedule, master):
     """One flat tensor of 2^32 + 2^20 + 333 elements with one scale per moment,
     in both schedules (stats off, as benchmarked).  The same large gradient
     (2^13, far above every other one) is planted at the first element of each
@@ -380,7 +381,7 @@ def test_flat_per_tensor_past_2_to_32_elements(schedule):
     piece = 1 << 28
     gen = torch.Generator(device=dev)
     gen.manual_seed(22)
-    param = torch.empty(n, device=dev)
+    param = torch.empty(n, device=dev, dtype=torch.bfloat16 if master == "bf16" else torch.float32)
     grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
     for a in range(0, n, piece):
         param[a:min(n, a + piece)].normal_(0.0, 0.02, generator=gen)
@@ -398,12 +399,12 @@ def test_flat_per_tensor_past_2_to_32_elements(schedule):
             opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
             torch.cuda.synchronize()
             h = oracle.Hyper(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
-            cfg = oracle_config(h, "e4m3", "e5m2", "tensor", "pow2", "fp32")
+            cfg = oracle_config(h, "e4m3", "e5m2", "tensor", "pow2", master)
             for (a, b), st in zip(windows, host):
                 st.step(cfg, np_host(grad[a:b]))
-                compare_tensor(f"{schedule} window [{a}, {b}) step {t}", st, np_host(param[a:b]),
+                compare_tensor(f"{schedule} {master} window [{a}, {b}) step {t}", st, np_host(param[a:b]),
                                np_host(opt.m[0][a:b]), np_host(opt.v[0][a:b]), np_host(opt.m_scale[0]),
-                               np_host(opt.v_scale[0]), "fp32")
+                               np_host(opt.v_scale[0]), master)
                 st.p = np_host(param[a:b]).copy()  # continue from the device's weights (within the bar)
     finally:
         opt.close()
