@@ -145,7 +145,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama2_7b",
                     choices=["flat_1m", "llama2_100m", "llama2_7b", "llama2_7b_block128", "llama2_7b_l2",
-                             "llama2_13b_bf16"])
+                             "llama2_13b_bf16", "llama2_7b_rank0_of_8"])
     ap.add_argument("--schedule", default="speculative", choices=["two_pass", "speculative"])
     ap.add_argument("--scaling", default="just_in_time", choices=["just_in_time", "delayed"],
                     help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")

@@ -209,3 +209,15 @@ def test_llama2_7b_speculative_equals_two_pass_over_60_steps():
         b.close()
         del pa, pb, grads
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_llama2_7b_rank0_of_8_bench_configuration():
+    """One data-parallel rank's real share of the 7B list (842M parameters,
+    ending in a cut piece of layers.3.w_gate), speculative from step 4 with
+    stats off as benchmarked; the embedding, a whole layer tensor and the cut
+    piece against the oracle at every step."""
+    w = workloads.llama2_7b_rank0_of_8()
+    n = len(w.shapes)
+    run_full(w, steps=6, sample=[0, 10, n - 1], collect_stats=False, schedule="speculative",
+             speculate_from_step=4)

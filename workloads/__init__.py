@@ -120,6 +120,36 @@ def llama2_13b_bf16() -> Workload:
                     grad_scale=(1e-7, 1.0), steps=5)
 
 
+def shard_shapes(shapes: list, rank: int, world: int, align: int = 128) -> list:
+    """One data-parallel rank's share of a tensor list: the list flattened in
+    order and cut into `world` contiguous slices at multiples of `align`
+    elements (the last slice takes the rest).  A tensor cut by a slice boundary
+    contributes the 1-D piece inside the slice, named name[a:b]."""
+    total = sum(numel(s) for _, s in shapes)
+    cut = [(total * r // world) // align * align for r in range(world)] + [total]
+    lo, hi = cut[rank], cut[rank + 1]
+    out, off = [], 0
+    for name, s in shapes:
+        n = numel(s)
+        a, b = max(lo, off), min(hi, off + n)
+        if a < b:
+            out.append((name, s) if (a, b) == (off, off + n) else (f"{name}[{a - off}:{b - off}]", (b - a,)))
+        off += n
+    return out
+
+
+def llama2_7b_rank0_of_8() -> Workload:
+    """Rank 0's share of the 7B per-tensor list when eight data-parallel ranks
+    each own a contiguous eighth of the flattened parameters (842,301,952
+    params: the embedding, layers 0-2, and layer 3 up to part of w_gate).  The
+    cut piece of w_gate carries its own scales here; across ranks its amax
+    would be reduced first."""
+    w = llama2_7b()
+    w.name = "llama2_7b_rank0_of_8"
+    w.shapes = shard_shapes(w.shapes, 0, 8)
+    return w
+
+
 def scaled_llama(base: dict, **over) -> list:
     """A smaller list with the same structure, for tests that must run on a CPU."""
     kw = dict(base)
@@ -134,6 +164,7 @@ WORKLOADS = {
     "llama2_7b_block128": llama2_7b_block128,
     "llama2_7b_l2": llama2_7b_l2,
     "llama2_13b_bf16": llama2_13b_bf16,
+    "llama2_7b_rank0_of_8": llama2_7b_rank0_of_8,
 }
 
 
