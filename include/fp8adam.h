@@ -71,7 +71,7 @@ typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master
  *   two code buffers (m/v and m_alt/v_alt, alternating every step); a per-tensor check then
  *   brings only the moments whose true scale differs to it: most codes just have their
  *   exponent field moved (2 bytes per element and moment), the few that cannot be moved
- *   exactly are recomputed from the gradient and the old codes (4 more).  14 bytes per fp32
+ *   exactly are recomputed from the gradient and the old codes (3 more).  14 bytes per fp32
  *   parameter plus that.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment
  *   is formed after p is overwritten, and coupled L2 would need the old p) and m_alt/v_alt;
  *   steps with t < speculate_from_step run TWO_PASS in place on the current buffer. */
