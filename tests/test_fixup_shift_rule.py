@@ -103,3 +103,28 @@ def test_refused_cases_are_needed(fmt):
     assert oracle.encode(fmt, [np.float32(big / 2)])[0] != TOP[fmt] - (1 << mb)
     ok, _ = shift_rule(np.array([TOP[fmt]], np.uint8), fmt, 1, zero_ok=True)
     assert not ok[0]
+
+
+def _loose_rule(codes: np.ndarray, fmt: str, d: int, zero_ok: bool):
+    """The rule with the smallest-normal code accepted (a plausible mistake)."""
+    mn, top = 1 << MANT[fmt], TOP[fmt]
+    mag = (codes & 0x7F).astype(np.int64)
+    nm = mag - d * mn
+    keep_zero = zero_ok & (mag == 0)
+    normal = (mag >= mn) & (mag < top) & (nm >= mn) & (nm < top)
+    moved = (codes & 0x80) | np.where(keep_zero, 0, nm & 0x7F)
+    return keep_zero | normal, moved.astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_the_check_rejects_a_looser_rule(fmt):
+    """Accepting the smallest-normal code (or moving codes into it) gives wrong
+    codes when the values grow by a binade: the comparison above catches it."""
+    rng = np.random.default_rng(7)
+    x = sample_values(fmt, rng)
+    y = (x.astype(np.float64) * 2.0).astype(np.float32)
+    ca, cb = oracle.encode(fmt, x), oracle.encode(fmt, y)
+    ok, moved = _loose_rule(ca, fmt, -1, zero_ok=False)
+    assert (ok & (moved != cb)).any()
+    ok, moved = shift_rule(ca, fmt, -1, zero_ok=False)
+    assert not (ok & (moved != cb)).any()
