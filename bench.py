@@ -154,8 +154,6 @@ def main():
     ap.add_argument("--amp", action="store_true",
                     help="loss-scaled gradients (scale 2^16) through the fused unscale / Inf-NaN skip / "
                          "global-norm clip (max_norm 1.0) step")
-    ap.add_argument("--code-layout", default="split", choices=["split", "paired"],
-                    help="paired: each tensor's m and v codes in one buffer, per 1024 elements m then v")
     ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -189,7 +187,7 @@ def main():
                                  and scaling == "just_in_time") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
                       schedule=schedule, decay_mode=w.decay_mode, scaling=scaling, rounding=args.rounding,
-                      seed=1234, code_layout=args.code_layout)
+                      seed=1234)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
@@ -311,7 +309,7 @@ def main():
                    "weight_decay": w.weight_decay, "decay_mode": w.decay_mode, "schedule": schedule,
                    "scaling": scaling if scaling == "just_in_time" else "delayed (amax history 16, margin 0)",
                    "loss_scaling": "scale 2^16, Inf/NaN skip, clip to global norm 1.0" if args.amp else None,
-                   "rounding": args.rounding, "code_layout": args.code_layout,
+                   "rounding": args.rounding,
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,

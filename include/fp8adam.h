@@ -103,15 +103,6 @@ typedef enum { FP8ADAM_SCALING_JUST_IN_TIME = 0, FP8ADAM_SCALING_DELAYED = 1 } f
  *   low 16 bits for m, high 16 bits for v.  Deterministic for a given seed and t; every
  *   schedule gives the same codes. */
 typedef enum { FP8ADAM_ROUND_NEAREST = 0, FP8ADAM_ROUND_STOCHASTIC = 1 } fp8adam_rounding;
-/* Where a tensor's moment codes live.
- * SPLIT: m and v (and m_alt, v_alt) are separate arrays of numel bytes, code i at offset i.
- * PAIRED: m (and m_alt) point to one array of 2 * ceil(numel/1024) * 1024 bytes holding, for each
- *   run of 1024 consecutive elements, their 1024 m codes and then their 1024 v codes (the last run
- *   padded to 1024); v and v_alt are ignored and may be NULL.  Element i's m code is at offset
- *   i + (i & ~1023) and its v code 1024 bytes further.  The step reads and writes one contiguous
- *   2 KiB run of codes per 1024 elements instead of two 1 KiB runs in separate arrays (fewer HBM
- *   streams).  The padding bytes are never read as codes. */
-typedef enum { FP8ADAM_CODES_SPLIT = 0, FP8ADAM_CODES_PAIRED = 1 } fp8adam_code_layout;
 
 typedef struct {
     int32_t m_format;      /* fp8adam_format of the first moment (default E4M3) */
@@ -133,7 +124,6 @@ typedef struct {
                                   caller's buffers (m, v codes 0; every scale 1.0; the amax
                                   history 0), so they may start with any content; 0: the caller
                                   provides the state (fresh, or restored from a checkpoint) */
-    int32_t code_layout;       /* fp8adam_code_layout (0: SPLIT) */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,

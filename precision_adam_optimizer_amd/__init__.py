@@ -33,14 +33,6 @@ _DECAY = {"decoupled": DECAY_DECOUPLED, "l2": DECAY_L2}
 SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
 ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
 _ROUNDING = {"nearest": ROUND_NEAREST, "stochastic": ROUND_STOCHASTIC}
-CODES_SPLIT, CODES_PAIRED = 0, 1
-_LAYOUT = {"split": CODES_SPLIT, "paired": CODES_PAIRED}
-PAIR_RUN = 1024  # paired layout: per run of 1024 elements, their m codes then their v codes
-
-
-def paired_code_bytes(numel: int) -> int:
-    """Bytes of one tensor's code buffer in the paired layout (both moments, last run padded)."""
-    return 2 * -(-numel // PAIR_RUN) * PAIR_RUN
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
@@ -75,7 +67,7 @@ class ConfigArg(ctypes.Structure):
                 ("decay_mode", ctypes.c_int32), ("scaling", ctypes.c_int32),
                 ("amax_history_len", ctypes.c_int32), ("margin", ctypes.c_int32),
                 ("delayed_from_step", ctypes.c_int32), ("rounding", ctypes.c_int32),
-                ("seed", ctypes.c_uint64), ("zero_state", ctypes.c_int32), ("code_layout", ctypes.c_int32)]
+                ("seed", ctypes.c_uint64), ("zero_state", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -302,12 +294,8 @@ class FP8AdamW:
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
                  speculate_from_step=0, decay_mode="decoupled", scaling="just_in_time",
-                 amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0,
-                 code_layout="split"):
+                 amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0):
         params, grads = list(params), list(grads)
-        self.paired = _LAYOUT[code_layout] == CODES_PAIRED
-        if self.paired and state is not None:
-            raise ValueError("the paired code layout starts from a fresh state (state=None)")
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
         master = params[0].dtype
@@ -316,13 +304,7 @@ class FP8AdamW:
         self.granularity = _GRAN[granularity]
         self.params, self.grads = params, grads
         fresh = state is None  # the library writes the fresh state (zero_state) into these buffers
-        if fresh and self.paired:  # one buffer per tensor holds both moments' codes; v is unused
-            m = [torch.empty(paired_code_bytes(p.numel()), dtype=torch.uint8, device=p.device) for p in params]
-            v = [None] * len(params)
-            ms = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
-            vs = [torch.ones(self.num_scales(p.numel()), dtype=torch.float32, device=p.device) for p in params]
-            state = (m, v, ms, vs)
-        elif fresh:
+        if fresh:
             m = [torch.empty(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
             v = [torch.empty(p.numel(), dtype=torch.uint8, device=p.device) for p in params]
             # (the scales are written too; ones keep an empty tensor's unused slot defined)
@@ -341,23 +323,18 @@ class FP8AdamW:
             self.amax_history = [None] * len(params)
         spec = _SCHED[schedule] == SCHEDULE_SPECULATIVE
         m_alt = [torch.empty_like(x) for x in m] if spec else [None] * len(m)
-        v_alt = [None if x is None else torch.empty_like(x) for x in v] if spec else [None] * len(v)
+        v_alt = [torch.empty_like(x) for x in v] if spec else [None] * len(v)
         self._m, self._v = (m, m_alt), (v, v_alt)
         args = []
         for i, (p, g) in enumerate(zip(params, grads)):
             if p.dtype != master or g.dtype != torch.bfloat16 or p.numel() != g.numel():
                 raise ValueError(f"tensor {i}: dtype or size mismatch")
             for t in (p, g, m[i], v[i], self.m_scale[i], self.v_scale[i]):
-                if t is None and self.paired:
-                    continue
                 if not t.is_contiguous() or t.device != p.device:
                     raise ValueError(f"tensor {i}: every buffer must be contiguous on one device")
             # the kernels read and write these sizes through plain pointers: check them here
             n, ns = p.numel(), self.num_scales(p.numel())
-            if self.paired:
-                if m[i].dtype != torch.uint8 or m[i].numel() != paired_code_bytes(n):
-                    raise ValueError(f"tensor {i}: paired codes must be {paired_code_bytes(n)} uint8")
-            elif any(x.dtype != torch.uint8 or x.numel() != n for x in (m[i], v[i])):
+            if any(x.dtype != torch.uint8 or x.numel() != n for x in (m[i], v[i])):
                 raise ValueError(f"tensor {i}: moment codes must be uint8 with one byte per element")
             if any(x.dtype != torch.float32 or x.numel() < ns for x in (self.m_scale[i], self.v_scale[i])):
                 raise ValueError(f"tensor {i}: scales must be float32, at least {ns} of them")
@@ -365,15 +342,14 @@ class FP8AdamW:
             if delayed and (h.dtype != torch.float32 or h.numel() != 2 * amax_history_len
                             or not h.is_contiguous() or h.device != p.device):
                 raise ValueError(f"tensor {i}: amax_history must be {2 * amax_history_len} contiguous float32")
-            args.append(TensorArg(p.data_ptr(), g.data_ptr(), m[i].data_ptr(), _ptr(v[i]),
+            args.append(TensorArg(p.data_ptr(), g.data_ptr(), m[i].data_ptr(), v[i].data_ptr(),
                                   self.m_scale[i].data_ptr(), self.v_scale[i].data_ptr(), p.numel(),
                                   _ptr(m_alt[i]), _ptr(v_alt[i]), _ptr(self.amax_history[i])))
         self.cfg = ConfigArg(_FORMATS[m_format], _FORMATS[v_format], self.granularity, _SMODE[scale_mode],
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
                              _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode],
                              _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step),
-                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, int(fresh),
-                             _LAYOUT[code_layout])
+                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, int(fresh))
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):
@@ -390,29 +366,17 @@ class FP8AdamW:
 
     @property
     def m(self) -> list:
-        """The first moment's codes per tensor (with the paired layout: copies
-        gathered from the shared code buffers)."""
-        if self.paired:
-            return [self._gather(b, p.numel(), 0) for b, p in zip(self._m[self.current_buffer], self.params)]
         return self._m[self.current_buffer]
 
     @property
     def v(self) -> list:
-        if self.paired:
-            return [self._gather(b, p.numel(), 1) for b, p in zip(self._m[self.current_buffer], self.params)]
         return self._v[self.current_buffer]
-
-    @staticmethod
-    def _gather(buf: torch.Tensor, n: int, which: int) -> torch.Tensor:
-        return buf.view(-1, 2, PAIR_RUN)[:, which, :].reshape(-1)[:n].clone()
 
     def checkpoint(self) -> list:
         """Copies of the whole optimizer state in the form ``state=`` takes:
         [m, v, m_scale, v_scale] (m and v from the pair that holds the moments),
         plus the amax histories with delayed scaling.  Together with the master
-        weights (and, for step_amp, the loss-scaler state) it resumes bit for bit.
-        With the paired code layout m and v come back as separate arrays, from
-        which an optimizer with the split layout resumes."""
+        weights (and, for step_amp, the loss-scaler state) it resumes bit for bit."""
         with torch.cuda.device(self.device):
             torch.cuda.current_stream().synchronize()
             out = [[x.clone() for x in self.m], [x.clone() for x in self.v],

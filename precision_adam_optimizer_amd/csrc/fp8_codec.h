@@ -232,7 +232,6 @@ struct StepConsts {
   float margin_scale;  // delayed scaling: 2^margin
   int hist_len;        // delayed scaling: H (0: no history)
   int hist_slot;       // delayed scaling: (t-1) mod H, the slot this step's amax goes to
-  int64_t pair_mask;   // code layout: 0 (split m and v arrays) or ~1023 (paired runs of 1024)
 };
 
 // Moment update (daoxuan.cc explainer, "Adam's update makes the needs

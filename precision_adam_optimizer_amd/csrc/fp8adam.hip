@@ -398,9 +398,6 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       return fail(FP8ADAM_EINVAL, "the speculative schedule cannot be combined with coupled L2 decay");
     if (cfg->scaling != FP8ADAM_SCALING_JUST_IN_TIME && cfg->scaling != FP8ADAM_SCALING_DELAYED)
       return fail(FP8ADAM_EINVAL, "bad scaling");
-    if (cfg->code_layout != FP8ADAM_CODES_SPLIT && cfg->code_layout != FP8ADAM_CODES_PAIRED)
-      return fail(FP8ADAM_EINVAL, "bad code_layout");
-    const bool paired = cfg->code_layout == FP8ADAM_CODES_PAIRED;
     const bool delayed = cfg->scaling == FP8ADAM_SCALING_DELAYED;
     const int hist_len = cfg->amax_history_len > 0 ? cfg->amax_history_len : 16;
     if (delayed) {
@@ -437,13 +434,12 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
       const fp8adam_tensor& T = tensors[t];
       if (T.numel < 0) return fail(FP8ADAM_EINVAL, "numel of tensor " + std::to_string(t) + " is negative");
       if (T.numel > 0) {
-        if (!T.param || !T.grad || !T.m || (!paired && !T.v) || !T.m_scale || !T.v_scale)
+        if (!T.param || !T.grad || !T.m || !T.v || !T.m_scale || !T.v_scale)
           return fail(FP8ADAM_EINVAL, "null pointer in tensor " + std::to_string(t));
         if (int r = check_aligned(T.param, "param", t)) return r;
         if (int r = check_aligned(T.grad, "grad", t)) return r;
         if (int r = check_aligned(T.m, "m", t)) return r;
-        if (!paired)
-          if (int r = check_aligned(T.v, "v", t)) return r;
+        if (int r = check_aligned(T.v, "v", t)) return r;
         if (((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
           return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
         if (delayed) {
@@ -453,22 +449,19 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
             return fail(FP8ADAM_EALIGN, "amax_history of tensor " + std::to_string(t) + " is not 4-byte aligned");
         }
         if (spec) {
-          if (!T.m_alt || (!paired && !T.v_alt))
+          if (!T.m_alt || !T.v_alt)
             return fail(FP8ADAM_EINVAL, "the speculative schedule needs m_alt and v_alt (tensor " + std::to_string(t) + ")");
           if (int r = check_aligned(T.m_alt, "m_alt", t)) return r;
-          if (!paired)
-            if (int r = check_aligned(T.v_alt, "v_alt", t)) return r;
+          if (int r = check_aligned(T.v_alt, "v_alt", t)) return r;
         }
       }
       const int64_t nc = (T.numel + chunk - 1) / chunk;
-      // paired codes: each run of 1024 holds the m codes, then the v codes (v = m + 1024)
-      uint8_t* const tv = paired ? (T.numel > 0 ? T.m + 1024 : nullptr) : T.v;
-      desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, tv, T.m_scale, T.v_scale,
+      desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
                            T.numel, nchunks, delayed ? T.amax_history : nullptr};
       desc[(size_t)n + t] = desc[t];
       if (spec) {
         desc[(size_t)n + t].m = T.m_alt;
-        desc[(size_t)n + t].v = paired ? (T.numel > 0 ? T.m_alt + 1024 : nullptr) : T.v_alt;
+        desc[(size_t)n + t].v = T.v_alt;
       }
       if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2Min))) > kMaxGroups)
         return fail(FP8ADAM_EINVAL, "too many elements for one context once each tensor is rounded up to whole "
@@ -512,12 +505,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (cfg->zero_state) {
       for (int32_t t = 0; e == hipSuccess && t < n; t++) {
         if (tensors[t].numel <= 0) continue;
-        if (cfg->code_layout == FP8ADAM_CODES_PAIRED) {  // both moments' codes and the padding
-          e = hipMemsetAsync(tensors[t].m, 0, (size_t)(2 * ((tensors[t].numel + 1023) / 1024) * 1024), stream);
-        } else {
-          e = hipMemsetAsync(tensors[t].m, 0, (size_t)tensors[t].numel, stream);
-          if (e == hipSuccess) e = hipMemsetAsync(tensors[t].v, 0, (size_t)tensors[t].numel, stream);
-        }
+        e = hipMemsetAsync(tensors[t].m, 0, (size_t)tensors[t].numel, stream);
+        if (e == hipSuccess) e = hipMemsetAsync(tensors[t].v, 0, (size_t)tensors[t].numel, stream);
       }
       if (e == hipSuccess) {
         hipLaunchKernelGGL(k_fresh_state, dim3((unsigned)n), dim3(kThreads), 0, stream, c->d_desc,
@@ -586,7 +575,6 @@ int step_consts(const fp8adam_ctx* ctx, const fp8adam_hparams* hp, StepConsts& k
     k.seed_lo = (uint32_t)ctx->cfg.seed;
     k.seed_hi = (uint32_t)(ctx->cfg.seed >> 32);
     k.rng_t = (uint32_t)hp->step;
-    k.pair_mask = ctx->cfg.code_layout == FP8ADAM_CODES_PAIRED ? ~(int64_t)1023 : 0;
     return 0;
 }
 

@@ -353,13 +353,6 @@ __device__ __forceinline__ void st_global(void* p, T x) {
   *(FP8ADAM_GLOBAL T*)(p) = x;
 }
 
-// Offset of element i's code in its moment's code array: i with split arrays,
-// i + (i rounded down to a multiple of 1024) with the paired layout (each run of
-// 1024 elements holds its m codes, then its v codes; the descriptor's v pointer
-// is then the m pointer + 1024).  Groups of 4 and 16 aligned elements never
-// straddle a run, so their codes stay contiguous.
-__device__ __forceinline__ int64_t code_off(const StepConsts& c, int64_t i) { return i + (i & c.pair_mask); }
-
 // Loads of one group of four consecutive elements.
 struct Group {
   vu2 g;         // 4 bf16
@@ -369,10 +362,10 @@ struct Group {
 };
 
 template <bool BF16P, bool NT>
-__device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, int64_t ci, Group& G, bool with_p) {
+__device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group& G, bool with_p) {
   G.g = ld_stream<vu2, NT>(d.g + i);
-  G.cm = ld_stream<uint32_t, NT>(d.m + ci);
-  G.cv = ld_stream<uint32_t, NT>(d.v + ci);
+  G.cm = ld_stream<uint32_t, NT>(d.m + i);
+  G.cv = ld_stream<uint32_t, NT>(d.v + i);
   if (with_p) {
     if constexpr (BF16P) {
       const vu2 pb = ld_stream<vu2, NT>(static_cast<const uint16_t*>(d.p) + i);
@@ -488,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_AMAX != 0>(d, i, code_off(c, i), G[u], L2);
+      if (i < gend) load_group<BF16P, FP8ADAM_NT_AMAX != 0>(d, i, G[u], L2);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
@@ -510,8 +503,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
     const int64_t i = gend + threadIdx.x;
     const float g = grad_in<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
     float m1, v1;
-    const int64_t ci = code_off(c, i);
-    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + ci)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + ci)) * sv, m1, v1);
+    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     am = max(am, abs_bits(m1));
     av = max(av, abs_bits(v1));
   }
@@ -618,14 +610,12 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     // the speculative schedule switches buffers regardless: carry the codes over
     if constexpr (SPEC) {
       for (int64_t i = start + kGroup * threadIdx.x; i < gend; i += kSubTile) {
-        const int64_t ci = code_off(c, i);
-        st_global<uint32_t>(dm + ci, ld_global<uint32_t>(d.m + ci));
-        st_global<uint32_t>(dv + ci, ld_global<uint32_t>(d.v + ci));
+        st_global<uint32_t>(dm + i, ld_global<uint32_t>(d.m + i));
+        st_global<uint32_t>(dv + i, ld_global<uint32_t>(d.v + i));
       }
       if (gend + threadIdx.x < end) {
-        const int64_t ci = code_off(c, gend + threadIdx.x);
-        st_global<uint8_t>(dm + ci, ld_global<uint8_t>(d.m + ci));
-        st_global<uint8_t>(dv + ci, ld_global<uint8_t>(d.v + ci));
+        st_global<uint8_t>(dm + gend + threadIdx.x, ld_global<uint8_t>(d.m + gend + threadIdx.x));
+        st_global<uint8_t>(dv + gend + threadIdx.x, ld_global<uint8_t>(d.v + gend + threadIdx.x));
       }
     }
     return;
@@ -658,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
 #pragma unroll
     for (int u = 0; u < kUpdUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_UPDATE_LD != 0>(d, i, code_off(c, i), G[u], true);
+      if (i < gend) load_group<BF16P, FP8ADAM_NT_UPDATE_LD != 0>(d, i, G[u], true);
     }
 #pragma unroll
     for (int u = 0; u < kUpdUnroll; u++) {
@@ -687,9 +677,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
             count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
         }
         store_p4<BF16P, FP8ADAM_NT_UPDATE_ST != 0>(d, i, p);
-        const int64_t ci = code_off(c, i);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dm + ci, wm);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dv + ci, wv);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dm + i, wm);
+        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dv + i, wv);
       }
     }
   }
@@ -698,8 +687,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
     const float p0 = load_p1<BF16P>(d, i);
     const float g = grad_in<L2>(c, load_g1(d, i), p0);
     float m1, v1;
-    const int64_t ci = code_off(c, i);
-    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + ci)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + ci)) * sv, m1, v1);
+    moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     const float p = param_update(c, p0, m1, v1);
     const float qm = m1 * ism, qv = v1 * isv;
     const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm), cv = quant1<VF, SR, true>(c, tid, i, qv);
@@ -709,8 +697,8 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
       av = max(av, abs_bits(v1));
     }
     store_p1<BF16P>(d, i, p);
-    st_global<uint8_t>(dm + ci, (uint8_t)cm);
-    st_global<uint8_t>(dv + ci, (uint8_t)cv);
+    st_global<uint8_t>(dm + i, (uint8_t)cm);
+    st_global<uint8_t>(dv + i, (uint8_t)cv);
   }
   flush_counters<STATS>(counters, tid, cnt);
   if constexpr (PARTS) {
@@ -917,7 +905,7 @@ template <int FMT, bool STATS, bool IS_V, bool SR>
 __device__ __forceinline__ uint32_t recompute4(const StepConsts& c, int tid, const TensorDesc& d, int64_t i,
                                                float s_old, float inv_new, uint32_t& under, uint32_t& sat) {
   const vu2 gg = ld_global<vu2>(d.g + i);
-  const uint32_t cc = ld_global<uint32_t>((IS_V ? d.v : d.m) + code_off(c, i));
+  const uint32_t cc = ld_global<uint32_t>((IS_V ? d.v : d.m) + i);
   const float g[4] = {bf16_lo(gg.x), bf16_hi(gg.x), bf16_lo(gg.y), bf16_hi(gg.y)};
   float x[4], q[4];
   decode4<FMT>(cc, x);
@@ -961,7 +949,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
 #pragma unroll
     for (int u = 0; u < kWideUnroll; u++) {
       const int64_t i = base + (int64_t)u * kWide * kThreads;
-      if (i < wend) cc[u] = ld_stream<vu4, FP8ADAM_NT_AMAX != 0>(dst + code_off(c, i));
+      if (i < wend) cc[u] = ld_stream<vu4, FP8ADAM_NT_AMAX != 0>(dst + i);
     }
 #pragma unroll
     for (int u = 0; u < kWideUnroll; u++) {
@@ -975,7 +963,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
             x = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i + 4 * k, s_old, inv_new, under, sat);
           w[k] = x;
         }
-        st_global<vu4>(dst + code_off(c, i), w);
+        st_global<vu4>(dst + i, w);
       }
     }
   }
@@ -983,14 +971,14 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
   if (threadIdx.x < kWide / 4 && wend + 4 * (int64_t)threadIdx.x < gend) {
     const int64_t i = wend + 4 * (int64_t)threadIdx.x;
     uint32_t w;
-    if (!shift_codes4<FMT>(ld_global<uint32_t>(dst + code_off(c, i)), dexp, zero_ok, w))
+    if (!shift_codes4<FMT>(ld_global<uint32_t>(dst + i), dexp, zero_ok, w))
       w = recompute4<FMT, STATS, IS_V, SR>(c, tid, d, i, s_old, inv_new, under, sat);
-    st_global<uint32_t>(dst + code_off(c, i), w);
+    st_global<uint32_t>(dst + i, w);
   }
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
     const float g = load_g1(d, i) * c.gfac;
-    const float x0 = decode1<FMT>(ld_global<uint8_t>((IS_V ? d.v : d.m) + code_off(c, i))) * s_old;
+    const float x0 = decode1<FMT>(ld_global<uint8_t>((IS_V ? d.v : d.m) + i)) * s_old;
     float m1, v1;
     moment_update(c, g, x0, x0, m1, v1);
     const float x = IS_V ? v1 : m1;
@@ -1000,7 +988,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
       under += (x != 0.0f && (code & 0x7Fu) == 0u);
       sat += (fabsf(q) > Format<FMT>::kMax);
     }
-    st_global<uint8_t>(dst + code_off(c, i), (uint8_t)code);
+    st_global<uint8_t>(dst + i, (uint8_t)code);
   }
 }
 
@@ -1126,7 +1114,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
         sm[j] = ld_global<float>(d.sm + b0[j] / kBlock);
         sv[j] = ld_global<float>(d.sv + b0[j] / kBlock);
       }
-      if (full[j]) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0[j] + 4 * hl, code_off(c, b0[j] + 4 * hl), G[j], true);
+      if (full[j]) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0[j] + 4 * hl, G[j], true);
     }
 #pragma unroll
     for (int j = 0; j < kBlkJ; j++) {
@@ -1143,8 +1131,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
           if (ex[j] && i < end) {
             q = load_p1<BF16P>(d, i);
             const float g = grad_in<L2>(c, load_g1(d, i), q);
-            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + code_off(c, i))) * sm[j],
-                          decode1<VF>(ld_global<uint8_t>(d.v + code_off(c, i))) * sv[j], a, b);
+            moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm[j],
+                          decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv[j], a, b);
           }
           m1[r] = a;
           v1[r] = b;
@@ -1188,8 +1176,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
             count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], wm >> (8 * r), wv >> (8 * r));
         }
         store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i0, p);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + code_off(c, i0), wm);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + code_off(c, i0), wv);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i0, wm);
+        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i0, wv);
       } else if (ex[j]) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -1198,8 +1186,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
             const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm[r]), cv = quant1<VF, SR, true>(c, tid, i, qv[r]);
             count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], cm, cv);
             store_p1<BF16P>(d, i, p[r]);
-            st_global<uint8_t>(d.m + code_off(c, i), (uint8_t)cm);
-            st_global<uint8_t>(d.v + code_off(c, i), (uint8_t)cv);
+            st_global<uint8_t>(d.m + i, (uint8_t)cm);
+            st_global<uint8_t>(d.v + i, (uint8_t)cv);
           }
         }
       }
