@@ -90,12 +90,16 @@ def test_resume_is_bit_exact():
     _same(ref, out)
 
 
-@pytest.mark.parametrize("granularity", ["tensor", "block128"])
+@pytest.mark.parametrize("granularity,schedule", [("tensor", "two_pass"), ("block128", "two_pass"),
+                                                  ("tensor", "speculative")])
 @pytest.mark.parametrize("master", [torch.float32, torch.bfloat16])
-def test_guard_bands_untouched(granularity, master):
+def test_guard_bands_untouched(granularity, schedule, master):
     """Every buffer is a view into a larger allocation whose bytes after the
     tensor (up to the next 16-byte boundary and 64 bytes more) hold a canary;
-    ragged sizes must not write past their end."""
+    ragged sizes must not write past their end.  Under the speculative
+    schedule the second code buffers are guarded too, and the fix-up (16 codes
+    per lane, then groups of 4, then single codes at a tensor's end) runs
+    whenever a tensor's scale moves between steps."""
     sizes = [1, 3, 129, 1025, 16387]
     pad = 128
     canary = 0x5A
@@ -121,13 +125,28 @@ def test_guard_bands_untouched(granularity, master):
         x.zero_()
     for x in ms + vs:
         x.fill_(1.0)
-    opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=True, state=(m, v, ms, vs))
-    for t in range(1, 4):
+    if schedule == "speculative":
+        # the binding makes the second code buffers with torch.empty_like: hand it guarded ones
+        alts = iter([alloc(n, torch.uint8) for n in sizes] + [alloc(n, torch.uint8) for n in sizes])
+        orig = torch.empty_like
+        torch.empty_like = lambda x, *a, **k: next(alts)
+        try:
+            opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=True, state=(m, v, ms, vs),
+                              schedule="speculative", speculate_from_step=2)
+        finally:
+            torch.empty_like = orig
+    else:
+        opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=True, state=(m, v, ms, vs))
+    requantized = 0
+    for t in range(1, 7):
         for i, n in enumerate(sizes):
-            grads[i].copy_(random_grad(n, t * 31 + i, "cuda"))
+            grads[i].copy_((random_grad(n, t * 31 + i, "cuda").float() * 4.0 ** (t % 3)).to(torch.bfloat16))
         opt.step(step=t, **HP)
+        requantized += sum(s["requantized"] for s in opt.stats())
     torch.cuda.synchronize()
     opt.close()
+    if schedule == "speculative":
+        assert requantized > 0  # the fix-up ran
     for raw, nbytes in bufs:
         tail = raw[nbytes:].cpu().numpy()
         assert (tail == canary).all(), "write past the end of a buffer"
