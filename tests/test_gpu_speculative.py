@@ -221,3 +221,14 @@ def test_llama2_7b_rank0_of_8_bench_configuration():
     n = len(w.shapes)
     run_full(w, steps=6, sample=[0, 10, n - 1], collect_stats=False, schedule="speculative",
              speculate_from_step=4)
+
+
+@pytest.mark.timeout(600)
+def test_llama2_100m_speculative_all_format_pairs():
+    """The Llama-2-100M-shaped list as benchmarked (speculative from step 4,
+    stats off) in all four (m, v) format pairs: every tensor against the oracle
+    at every one of 7 steps."""
+    for m_fmt, v_fmt in FORMATS:
+        w = workloads.llama2_100m(m_fmt, v_fmt)
+        run_full(w, steps=7, sample=list(range(len(w.shapes))), collect_stats=False, schedule="speculative",
+                 speculate_from_step=4)
