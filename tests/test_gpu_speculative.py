@@ -232,3 +232,11 @@ def test_llama2_100m_speculative_all_format_pairs():
         w = workloads.llama2_100m(m_fmt, v_fmt)
         run_full(w, steps=7, sample=list(range(len(w.shapes))), collect_stats=False, schedule="speculative",
                  speculate_from_step=4)
+
+
+@pytest.mark.timeout(300)
+def test_flat_1m_speculative_ten_steps():
+    """The 1M flat tensor (per-row gradient scales) as benchmarked: speculative
+    from step 4, stats off, ten steps against the oracle."""
+    run_full(workloads.flat_1m(), steps=10, sample=[0], collect_stats=False, schedule="speculative",
+             speculate_from_step=4)
