@@ -274,6 +274,16 @@ def test_llama2_7b_block128_full_size():
     run_full(w, steps=2, sample=sample, collect_stats=True)
 
 
+@pytest.mark.timeout(900)
+def test_llama2_7b_block128_as_benchmarked():
+    """The block-128 list in the benchmark's launch configuration (stats off:
+    the kernel instantiation the benchmark times), three steps."""
+    w = workloads.llama2_7b_block128()
+    n = len(w.shapes)
+    sample = _layer_indices(32, [5]) + [n - 1]
+    run_full(w, steps=3, sample=sample, collect_stats=False)
+
+
 @pytest.mark.timeout(1200)
 def test_llama2_13b_bf16_master_full_size():
     """The 13B list as benchmarked: bf16 master, speculative schedule (step 1
