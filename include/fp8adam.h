@@ -239,6 +239,30 @@ typedef struct {
 int fp8adam_step_amp(fp8adam_ctx *ctx, const fp8adam_hparams *hp, const fp8adam_amp_config *amp,
                      fp8adam_amp_state *state, hipStream_t stream);
 
+/* ---- allocation-free step ----
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  One step over a tensor list without a context: the
+ * same kernels, and so the same results bit for bit, as fp8adam_init (zero_state 0) followed
+ * by one fp8adam_step, for the TWO_PASS schedule with just-in-time scaling and stats off, in
+ * either granularity, scale mode, master dtype, decay mode and rounding.  Arguments as for
+ * fp8adam_init and fp8adam_step; the caller provides the state (codes and scales).  Calls
+ * nothing that allocates: what the step needs beyond the caller's buffers (descriptors, chunk
+ * table, amax partials, staged scales) lives in one file-scope device array of
+ * FP8ADAM_NOALLOC_SCRATCH_BYTES bytes, which every GPU the library runs on holds until the
+ * process ends; the descriptors reach it through a kernel's arguments (no host-to-device copy).
+ * Limits: n <= FP8ADAM_NOALLOC_MAX_TENSORS and the element limit of a context (about 1.7e10);
+ * the chunk table holds FP8ADAM_NOALLOC_MAX_CHUNKS chunks, which any such list fits once its
+ * chunks grow (up to 2^18 elements; the results do not depend on the chunk size).  Beyond the
+ * limits, or for another schedule, scaling, stats or zero_state: EINVAL before anything is
+ * enqueued.  The stream must belong to the current device.  Every call on one GPU shares
+ * that GPU's array and leaves its contents behind (each call rewrites what it reads), so calls
+ * that overlap on one GPU (on different streams, or from several threads) race: order them. */
+#define FP8ADAM_NOALLOC_MAX_TENSORS 4096
+#define FP8ADAM_NOALLOC_MAX_CHUNKS 131072
+#define FP8ADAM_NOALLOC_SCRATCH_BYTES 2015232
+int fp8adam_step_noalloc(const fp8adam_tensor *tensors, int32_t n, const fp8adam_config *cfg,
+                         const fp8adam_hparams *hp, hipStream_t stream);
+
 /* Copy the diagnostics of the last step into out_host[0..n) (n = the context's
  * tensor count; EINVAL otherwise).  Synchronizes `stream`. */
 int fp8adam_stats(fp8adam_ctx *ctx, fp8adam_stats_t *out_host, int32_t n, hipStream_t stream);

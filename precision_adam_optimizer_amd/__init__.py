@@ -43,7 +43,13 @@ KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "st
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
-           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy")
+           "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy",
+           "fp8adam_step_noalloc")
+
+# limits of fp8adam_step_noalloc (the header's FP8ADAM_NOALLOC_* macros)
+NOALLOC_MAX_TENSORS = 4096
+NOALLOC_MAX_CHUNKS = 131072
+NOALLOC_SCRATCH_BYTES = 2015232
 
 
 class Fp8AdamError(RuntimeError):
@@ -128,10 +134,12 @@ def load() -> ctypes.CDLL:
     L.fp8adam_encode_sr_bits_range.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, vp, vp]
     L.fp8adam_encode_sr.argtypes = [i32, vp, vp, vp, i64, vp]
     L.fp8adam_stream_copy.argtypes = [vp, vp, i64, vp]
+    L.fp8adam_step_noalloc.argtypes = [ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg),
+                                       ctypes.POINTER(HParamsArg), vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
                  "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
                  "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
-                 "fp8adam_encode_sr", "fp8adam_stream_copy"):
+                 "fp8adam_encode_sr", "fp8adam_stream_copy", "fp8adam_step_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -167,6 +175,12 @@ def fp8adam_step(ctx: int, hp: HParamsArg, stream: int | None = None) -> None:
 def fp8adam_step_amp(ctx: int, hp: HParamsArg, amp: AmpConfigArg, state: int, stream: int | None = None) -> None:
     _check(load().fp8adam_step_amp(ctx, ctypes.byref(hp), ctypes.byref(amp), state,
                                    current_stream() if stream is None else stream))
+
+
+def fp8adam_step_noalloc(tensors: list[TensorArg], cfg: ConfigArg, hp: HParamsArg, stream: int | None = None) -> None:
+    arr = (TensorArg * len(tensors))(*tensors)
+    _check(load().fp8adam_step_noalloc(arr, len(tensors), ctypes.byref(cfg), ctypes.byref(hp),
+                                       current_stream() if stream is None else stream))
 
 
 def amp_state(init_scale: float = 65536.0, device="cuda") -> torch.Tensor:

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -312,6 +313,77 @@ int check_aligned(const void* p, const char* what, int32_t t) {
   return 0;
 }
 
+// Every launch must fit one grid dimension of at most 2^32 - 1 work-items:
+// kMaxGroups work-groups of kThreads (XCD-ordered grids round up to 8), and the
+// widest grid has one work-group per 2^min(kPartLog2, kUPartLog2Min) elements of
+// every chunk.  That caps one step at about 1.7e10 elements; larger lists are
+// split over several contexts.
+constexpr int64_t kMaxGroups = ((int64_t)UINT32_MAX / kThreads) & ~(int64_t)7;
+constexpr int kNarrowPartLog2 = kPartLog2 < kUPartLog2Min ? kPartLog2 : kUPartLog2Min;
+constexpr int64_t kMaxElements = kMaxGroups << kNarrowPartLog2;
+
+// The config's enums and the combinations the step supports (fp8adam_init and
+// fp8adam_step_noalloc).
+int check_config(const fp8adam_config* cfg) {
+  if (!valid_fmt(cfg->m_format) || !valid_fmt(cfg->v_format))
+    return fail(FP8ADAM_EINVAL, "m_format / v_format must be FP8ADAM_E4M3 or FP8ADAM_E5M2");
+  if (cfg->granularity != FP8ADAM_SCALE_TENSOR && cfg->granularity != FP8ADAM_SCALE_BLOCK128)
+    return fail(FP8ADAM_EINVAL, "bad granularity");
+  if (cfg->scale_mode != FP8ADAM_SCALE_POW2 && cfg->scale_mode != FP8ADAM_SCALE_AMAX)
+    return fail(FP8ADAM_EINVAL, "bad scale_mode");
+  if (cfg->master != FP8ADAM_MASTER_FP32 && cfg->master != FP8ADAM_MASTER_BF16)
+    return fail(FP8ADAM_EINVAL, "bad master dtype");
+  if (cfg->schedule != FP8ADAM_SCHEDULE_TWO_PASS && cfg->schedule != FP8ADAM_SCHEDULE_SPECULATIVE)
+    return fail(FP8ADAM_EINVAL, "bad schedule");
+  if (cfg->decay_mode != FP8ADAM_DECAY_DECOUPLED && cfg->decay_mode != FP8ADAM_DECAY_L2)
+    return fail(FP8ADAM_EINVAL, "bad decay_mode");
+  if (cfg->rounding != FP8ADAM_ROUND_NEAREST && cfg->rounding != FP8ADAM_ROUND_STOCHASTIC)
+    return fail(FP8ADAM_EINVAL, "bad rounding");
+  const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
+  if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
+    return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
+  if (spec && cfg->decay_mode == FP8ADAM_DECAY_L2)
+    return fail(FP8ADAM_EINVAL, "the speculative schedule cannot be combined with coupled L2 decay");
+  if (cfg->scaling != FP8ADAM_SCALING_JUST_IN_TIME && cfg->scaling != FP8ADAM_SCALING_DELAYED)
+    return fail(FP8ADAM_EINVAL, "bad scaling");
+  const bool delayed = cfg->scaling == FP8ADAM_SCALING_DELAYED;
+  const int hist_len = cfg->amax_history_len > 0 ? cfg->amax_history_len : 16;
+  if (delayed) {
+    if (cfg->granularity != FP8ADAM_SCALE_TENSOR || spec)
+      return fail(FP8ADAM_EINVAL, "delayed scaling needs per-tensor scales and the TWO_PASS schedule value");
+    if (hist_len > 1024) return fail(FP8ADAM_EINVAL, "amax_history_len must be at most 1024");
+    if (cfg->margin < 0 || cfg->margin > 64) return fail(FP8ADAM_EINVAL, "margin must lie in [0, 64]");
+  }
+  return 0;
+}
+
+// One tensor's pointers and their alignment (nothing to check for an empty tensor).
+int check_tensor(const fp8adam_tensor& T, int32_t t, bool delayed, bool spec) {
+  if (T.numel < 0) return fail(FP8ADAM_EINVAL, "numel of tensor " + std::to_string(t) + " is negative");
+  if (T.numel == 0) return 0;
+  if (!T.param || !T.grad || !T.m || !T.v || !T.m_scale || !T.v_scale)
+    return fail(FP8ADAM_EINVAL, "null pointer in tensor " + std::to_string(t));
+  if (int r = check_aligned(T.param, "param", t)) return r;
+  if (int r = check_aligned(T.grad, "grad", t)) return r;
+  if (int r = check_aligned(T.m, "m", t)) return r;
+  if (int r = check_aligned(T.v, "v", t)) return r;
+  if (((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
+    return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
+  if (delayed) {
+    if (!T.amax_history)
+      return fail(FP8ADAM_EINVAL, "delayed scaling needs amax_history (tensor " + std::to_string(t) + ")");
+    if ((uintptr_t)T.amax_history & 3u)
+      return fail(FP8ADAM_EALIGN, "amax_history of tensor " + std::to_string(t) + " is not 4-byte aligned");
+  }
+  if (spec) {
+    if (!T.m_alt || !T.v_alt)
+      return fail(FP8ADAM_EINVAL, "the speculative schedule needs m_alt and v_alt (tensor " + std::to_string(t) + ")");
+    if (int r = check_aligned(T.m_alt, "m_alt", t)) return r;
+    if (int r = check_aligned(T.v_alt, "v_alt", t)) return r;
+  }
+  return 0;
+}
+
 void free_ctx(fp8adam_ctx* c) {
   if (!c) return;
   if (c->d_desc) (void)hipFree(c->d_desc);
@@ -356,6 +428,93 @@ unsigned probe_grid(int64_t n, int per_thread) {
 
 }  // namespace
 
+
+// ------------------------------------------------ allocation-free step: scratch
+//
+// fp8adam_step_noalloc keeps what the two-pass step needs beyond the caller's
+// buffers in one file-scope device array, `scratch`: the tensor descriptors,
+// the chunk table, the per-chunk amax partials, the per-tensor amax, the staged
+// old scales and the flags.  Every call writes each of them before reading it
+// (descriptors and chunk table by k_noalloc_setup, partials by the amax pass,
+// amax, old scales and flags by the reduction), so nothing is cleared between
+// calls.  In host code the array's name is only a host-side stand-in: each
+// device's copy has its own address, looked up with hipGetSymbolAddress once
+// per device (with that device current), and that address is what the kernels
+// receive.
+
+namespace {
+
+constexpr int64_t kNaMaxTensors = FP8ADAM_NOALLOC_MAX_TENSORS;
+constexpr int64_t kNaMaxChunks = FP8ADAM_NOALLOC_MAX_CHUNKS;
+// Chunks grow (up to 2^18 elements) until the table fits: any list within kMaxElements
+// then needs at most kMaxElements / 2^18 + kNaMaxTensors chunks.
+constexpr int kNaMaxChunkLog2 = 18;
+constexpr int kSetupBatch = 32;      // descriptors per set-up launch, passed by value (2.3 KB)
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t kNaDesc = 0;
+constexpr size_t kNaChunkTid = align256(kNaDesc + sizeof(TensorDesc) * kNaMaxTensors);
+constexpr size_t kNaPartial = align256(kNaChunkTid + sizeof(int32_t) * kNaMaxChunks);
+constexpr size_t kNaAmax = align256(kNaPartial + sizeof(uint2) * kNaMaxChunks);
+constexpr size_t kNaOldScale = align256(kNaAmax + sizeof(uint32_t) * 4 * kNaMaxTensors);
+constexpr size_t kNaFlags = align256(kNaOldScale + sizeof(float) * 4 * kNaMaxTensors);
+constexpr size_t kNaBytes = align256(kNaFlags + sizeof(int32_t) * kNaMaxTensors);
+static_assert(kNaBytes == FP8ADAM_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static_assert((kMaxElements >> kNaMaxChunkLog2) + 1 + kNaMaxTensors <= kNaMaxChunks,
+              "every list within the element limit fits the chunk table");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNaBytes];
+
+namespace {
+
+constexpr int kNaMaxDevices = 256;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kNaMaxDevices] = {};
+
+// Device address of `scratch` on device dev, which must be the current device.
+int scratch_of(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= kNaMaxDevices) return fail(FP8ADAM_EINVAL, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(FP8ADAM_EHIP, "hipGetSymbolAddress returned a null address for the scratch array");
+    g_scratch[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch[dev];
+  return 0;
+}
+
+// Up to kSetupBatch tensor descriptors, by value in the kernel's arguments.
+struct SetupBatch {
+  int32_t first, count;
+  TensorDesc d[kSetupBatch];
+};
+
+// One work-group per tensor of the batch: its descriptor and its entries of
+// the chunk table (chunk -> tensor) into the scratch.
+__global__ __launch_bounds__(kThreads) void k_noalloc_setup(SetupBatch b, TensorDesc* __restrict__ descs,
+                                                            int32_t* __restrict__ chunk_tid, int chunk_log2) {
+  const int j = blockIdx.x;
+  if (j >= b.count) return;
+  const int32_t t = b.first + j;
+  const TensorDesc d = b.d[j];
+  if (threadIdx.x == 0) descs[t] = d;
+  const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
+  for (int64_t k = threadIdx.x; k < nc; k += kThreads) chunk_tid[d.chunk0 + k] = t;
+}
+
+// Chunks of the list at chunk size 2^chunk_log2 (each tensor rounded up to whole chunks).
+int64_t count_chunks(const fp8adam_tensor* tensors, int32_t n, int chunk_log2) {
+  int64_t nc = 0;
+  for (int32_t t = 0; t < n; t++) nc += (tensors[t].numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
+  return nc;
+}
+
+}  // namespace
+
 // ================================================================== C ABI
 
 extern "C" {
@@ -377,45 +536,12 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     *out = nullptr;
     if (!tensors || !cfg) return fail(FP8ADAM_EINVAL, "tensors or cfg is null");
     if (n <= 0) return fail(FP8ADAM_EINVAL, "n must be positive");
-    if (!valid_fmt(cfg->m_format) || !valid_fmt(cfg->v_format))
-      return fail(FP8ADAM_EINVAL, "m_format / v_format must be FP8ADAM_E4M3 or FP8ADAM_E5M2");
-    if (cfg->granularity != FP8ADAM_SCALE_TENSOR && cfg->granularity != FP8ADAM_SCALE_BLOCK128)
-      return fail(FP8ADAM_EINVAL, "bad granularity");
-    if (cfg->scale_mode != FP8ADAM_SCALE_POW2 && cfg->scale_mode != FP8ADAM_SCALE_AMAX)
-      return fail(FP8ADAM_EINVAL, "bad scale_mode");
-    if (cfg->master != FP8ADAM_MASTER_FP32 && cfg->master != FP8ADAM_MASTER_BF16)
-      return fail(FP8ADAM_EINVAL, "bad master dtype");
-    if (cfg->schedule != FP8ADAM_SCHEDULE_TWO_PASS && cfg->schedule != FP8ADAM_SCHEDULE_SPECULATIVE)
-      return fail(FP8ADAM_EINVAL, "bad schedule");
-    if (cfg->decay_mode != FP8ADAM_DECAY_DECOUPLED && cfg->decay_mode != FP8ADAM_DECAY_L2)
-      return fail(FP8ADAM_EINVAL, "bad decay_mode");
-    if (cfg->rounding != FP8ADAM_ROUND_NEAREST && cfg->rounding != FP8ADAM_ROUND_STOCHASTIC)
-      return fail(FP8ADAM_EINVAL, "bad rounding");
+    if (int r = check_config(cfg)) return r;
     const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
-    if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
-      return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
-    if (spec && cfg->decay_mode == FP8ADAM_DECAY_L2)
-      return fail(FP8ADAM_EINVAL, "the speculative schedule cannot be combined with coupled L2 decay");
-    if (cfg->scaling != FP8ADAM_SCALING_JUST_IN_TIME && cfg->scaling != FP8ADAM_SCALING_DELAYED)
-      return fail(FP8ADAM_EINVAL, "bad scaling");
     const bool delayed = cfg->scaling == FP8ADAM_SCALING_DELAYED;
     const int hist_len = cfg->amax_history_len > 0 ? cfg->amax_history_len : 16;
-    if (delayed) {
-      if (cfg->granularity != FP8ADAM_SCALE_TENSOR || spec)
-        return fail(FP8ADAM_EINVAL, "delayed scaling needs per-tensor scales and the TWO_PASS schedule value");
-      if (hist_len > 1024) return fail(FP8ADAM_EINVAL, "amax_history_len must be at most 1024");
-      if (cfg->margin < 0 || cfg->margin > 64) return fail(FP8ADAM_EINVAL, "margin must lie in [0, 64]");
-    }
-
     // Chunk size: the largest power of two in [2^kMinChunkLog2, 2^kMaxChunkLog2] that still
     // gives the amax pass at least kMinAmaxGroups work-groups.
-    // Every launch must fit one grid dimension of at most 2^32 - 1 work-items:
-    // kMaxGroups work-groups of kThreads (XCD-ordered grids round up to 8), and
-    // the widest grid has one work-group per 2^kUPartLog2Min elements of every
-    // chunk.  That caps a context at about 1.7e10 elements; larger lists are
-    // split over several contexts.
-    constexpr int64_t kMaxGroups = ((int64_t)UINT32_MAX / kThreads) & ~(int64_t)7;
-    constexpr int64_t kMaxElements = kMaxGroups << std::min(kPartLog2, kUPartLog2Min);
     int64_t total = 0;
     for (int32_t t = 0; t < n; t++) {
       total += tensors[t].numel > 0 ? std::min(tensors[t].numel, kMaxElements + 1) : 0;
@@ -432,29 +558,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     int64_t nchunks = 0;
     for (int32_t t = 0; t < n; t++) {
       const fp8adam_tensor& T = tensors[t];
-      if (T.numel < 0) return fail(FP8ADAM_EINVAL, "numel of tensor " + std::to_string(t) + " is negative");
-      if (T.numel > 0) {
-        if (!T.param || !T.grad || !T.m || !T.v || !T.m_scale || !T.v_scale)
-          return fail(FP8ADAM_EINVAL, "null pointer in tensor " + std::to_string(t));
-        if (int r = check_aligned(T.param, "param", t)) return r;
-        if (int r = check_aligned(T.grad, "grad", t)) return r;
-        if (int r = check_aligned(T.m, "m", t)) return r;
-        if (int r = check_aligned(T.v, "v", t)) return r;
-        if (((uintptr_t)T.m_scale & 3u) || ((uintptr_t)T.v_scale & 3u))
-          return fail(FP8ADAM_EALIGN, "scale pointer of tensor " + std::to_string(t) + " is not 4-byte aligned");
-        if (delayed) {
-          if (!T.amax_history)
-            return fail(FP8ADAM_EINVAL, "delayed scaling needs amax_history (tensor " + std::to_string(t) + ")");
-          if ((uintptr_t)T.amax_history & 3u)
-            return fail(FP8ADAM_EALIGN, "amax_history of tensor " + std::to_string(t) + " is not 4-byte aligned");
-        }
-        if (spec) {
-          if (!T.m_alt || !T.v_alt)
-            return fail(FP8ADAM_EINVAL, "the speculative schedule needs m_alt and v_alt (tensor " + std::to_string(t) + ")");
-          if (int r = check_aligned(T.m_alt, "m_alt", t)) return r;
-          if (int r = check_aligned(T.v_alt, "v_alt", t)) return r;
-        }
-      }
+      if (int r = check_tensor(T, t, delayed, spec)) return r;
       const int64_t nc = (T.numel + chunk - 1) / chunk;
       desc[t] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
                            T.numel, nchunks, delayed ? T.amax_history : nullptr};
@@ -463,7 +567,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
         desc[(size_t)n + t].m = T.m_alt;
         desc[(size_t)n + t].v = T.v_alt;
       }
-      if (((nchunks + nc) << (chunk_log2 - std::min(kPartLog2, kUPartLog2Min))) > kMaxGroups)
+      if (((nchunks + nc) << (chunk_log2 - kNarrowPartLog2)) > kMaxGroups)
         return fail(FP8ADAM_EINVAL, "too many elements for one context once each tensor is rounded up to whole "
                                     "chunks; split the tensor list over several contexts");
       for (int64_t k = 0; k < nc; k++) chunk_tid.push_back(t);
@@ -615,6 +719,83 @@ int fp8adam_step_amp(fp8adam_ctx* ctx, const fp8adam_hparams* hp, const fp8adam_
   } catch (...) {
     if (ctx) ctx->gctl = nullptr;
     return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step_amp");
+  }
+}
+
+int fp8adam_step_noalloc(const fp8adam_tensor* tensors, int32_t n, const fp8adam_config* cfg,
+                         const fp8adam_hparams* hp, hipStream_t stream) {
+  try {
+    if (!tensors || !cfg || !hp) return fail(FP8ADAM_EINVAL, "tensors, cfg or hp is null");
+    if (n <= 0 || n > kNaMaxTensors)
+      return fail(FP8ADAM_EINVAL, "n must lie in [1, " + std::to_string(kNaMaxTensors) +
+                                      "] (FP8ADAM_NOALLOC_MAX_TENSORS)");
+    if (int r = check_config(cfg)) return r;
+    if (cfg->schedule != FP8ADAM_SCHEDULE_TWO_PASS || cfg->scaling != FP8ADAM_SCALING_JUST_IN_TIME)
+      return fail(FP8ADAM_EINVAL, "fp8adam_step_noalloc runs the TWO_PASS schedule with just-in-time scaling");
+    if (cfg->collect_stats || cfg->zero_state)
+      return fail(FP8ADAM_EINVAL, "fp8adam_step_noalloc takes neither collect_stats nor zero_state");
+    int64_t total = 0;
+    for (int32_t t = 0; t < n; t++) {
+      if (int r = check_tensor(tensors[t], t, false, false)) return r;
+      total += std::min(tensors[t].numel, kMaxElements + 1);
+      if (total > kMaxElements)
+        return fail(FP8ADAM_EINVAL, "too many elements for one step (at most " + std::to_string(kMaxElements) + ")");
+    }
+    // the chunk size fp8adam_init would take, raised until the chunk table fits the scratch
+    int chunk_log2 = kMaxChunkLog2;
+    while (chunk_log2 > kMinChunkLog2 && (total >> chunk_log2) < kMinAmaxGroups) chunk_log2--;
+    int64_t nchunks = count_chunks(tensors, n, chunk_log2);
+    while (nchunks > kNaMaxChunks && chunk_log2 < kNaMaxChunkLog2) nchunks = count_chunks(tensors, n, ++chunk_log2);
+    if (nchunks > kNaMaxChunks)
+      return fail(FP8ADAM_EINVAL, "the list needs " + std::to_string(nchunks) + " chunks, more than the scratch holds (" +
+                                      std::to_string(kNaMaxChunks) + ", FP8ADAM_NOALLOC_MAX_CHUNKS)");
+    if ((nchunks << (chunk_log2 - kNarrowPartLog2)) > kMaxGroups)
+      return fail(FP8ADAM_EINVAL, "too many elements for one step once each tensor is rounded up to whole chunks");
+    fp8adam_ctx c;  // on the stack: every buffer it names lies in the scratch array
+    c.cfg = *cfg;
+    c.n = n;
+    c.nchunks = nchunks;
+    c.chunk_log2 = chunk_log2;
+    c.nparts = nchunks << (chunk_log2 - kPartLog2);
+    c.nuparts = nchunks << (chunk_log2 - kUPartLog2Min);
+    StepConsts k;
+    if (int r = step_consts(&c, hp, k)) return r;
+
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    hipDevice_t sdev = -1;
+    HIP_TRY(hipStreamGetDevice(stream, &sdev));
+    if (sdev != dev)
+      return fail(FP8ADAM_EINVAL, "the stream belongs to device " + std::to_string(sdev) + ", not the current device " +
+                                      std::to_string(dev));
+    unsigned char* base = nullptr;
+    if (int r = scratch_of(dev, &base)) return r;
+    c.device = dev;
+    c.d_desc = reinterpret_cast<TensorDesc*>(base + kNaDesc);
+    c.d_chunk_tid = reinterpret_cast<int32_t*>(base + kNaChunkTid);
+    c.d_partial = reinterpret_cast<uint2*>(base + kNaPartial);
+    c.d_amax = reinterpret_cast<uint32_t*>(base + kNaAmax);
+    c.d_old_scale = reinterpret_cast<float*>(base + kNaOldScale);
+    c.d_flags = reinterpret_cast<int32_t*>(base + kNaFlags);
+
+    SetupBatch b;
+    int64_t chunk0 = 0;
+    for (int32_t t0 = 0; t0 < n; t0 += kSetupBatch) {
+      b.first = t0;
+      b.count = std::min<int32_t>(kSetupBatch, n - t0);
+      for (int32_t j = 0; j < b.count; j++) {
+        const fp8adam_tensor& T = tensors[t0 + j];
+        b.d[j] = TensorDesc{T.param, static_cast<const uint16_t*>(T.grad), T.m, T.v, T.m_scale, T.v_scale,
+                            T.numel, chunk0, nullptr};
+        chunk0 += (T.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
+      }
+      hipLaunchKernelGGL(k_noalloc_setup, dim3((unsigned)b.count), dim3(kThreads), 0, stream, b, c.d_desc,
+                         c.d_chunk_tid, chunk_log2);
+      HIP_TRY(hipGetLastError());
+    }
+    return run_step(&c, k, hp->step, stream);
+  } catch (...) {
+    return fail(FP8ADAM_EINVAL, "unexpected error in fp8adam_step_noalloc");
   }
 }
 

@@ -187,3 +187,41 @@ def test_binding_structs_match_the_header_layout(tmp_path):
     assert got[("fp8adam_amp_state", "size")] == pk.AMP_STATE_DTYPE.itemsize
     for f in pk.AMP_STATE_DTYPE.names:
         assert got[("fp8adam_amp_state", f)] == pk.AMP_STATE_DTYPE.fields[f][1], f"fp8adam_amp_state.{f}"
+
+
+def test_noalloc_argument_errors_without_a_gpu():
+    """fp8adam_step_noalloc refuses what it cannot run, and sizes beyond its
+    limits, before any HIP call (so these run without a GPU); its limits in the
+    binding are the header's."""
+    text = open(os.path.join(ROOT, "include", "fp8adam.h")).read()
+    macros = dict(re.findall(r"#define (FP8ADAM_NOALLOC_\w+) (\d+)", text))
+    assert int(macros["FP8ADAM_NOALLOC_MAX_TENSORS"]) == pk.NOALLOC_MAX_TENSORS
+    assert int(macros["FP8ADAM_NOALLOC_MAX_CHUNKS"]) == pk.NOALLOC_MAX_CHUNKS
+    assert int(macros["FP8ADAM_NOALLOC_SCRATCH_BYTES"]) == pk.NOALLOC_SCRATCH_BYTES
+    L = pk.load()
+    hp = pk.HParamsArg(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    one = (pk.TensorArg * 1)(pk.TensorArg(16, 32, 48, 64, 80, 96, 10))
+    cfg = pk.ConfigArg(0, 1, 0, 0, 0, 0)
+    assert L.fp8adam_step_noalloc(None, 1, ctypes.byref(cfg), ctypes.byref(hp), None) == -1
+    assert L.fp8adam_step_noalloc(one, 0, ctypes.byref(cfg), ctypes.byref(hp), None) == -1
+    many = (pk.TensorArg * (pk.NOALLOC_MAX_TENSORS + 1))(
+        *[pk.TensorArg(16, 32, 48, 64, 80, 96, 10)] * (pk.NOALLOC_MAX_TENSORS + 1))
+    assert L.fp8adam_step_noalloc(many, pk.NOALLOC_MAX_TENSORS + 1, ctypes.byref(cfg), ctypes.byref(hp), None) == -1
+    assert "NOALLOC_MAX_TENSORS" in pk.fp8adam_last_error()
+    for bad, what in ((pk.ConfigArg(0, 1, 0, 0, 0, 0, pk.SCHEDULE_SPECULATIVE), "TWO_PASS"),
+                      (pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, pk.SCALING_DELAYED), "just-in-time"),
+                      (pk.ConfigArg(0, 1, 0, 0, 0, 1), "collect_stats"),
+                      (pk.ConfigArg(0, 1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1), "zero_state"),
+                      (pk.ConfigArg(0, 9, 0, 0, 0, 0), "v_format")):
+        assert L.fp8adam_step_noalloc(one, 1, ctypes.byref(bad), ctypes.byref(hp), None) == -1
+        assert what in pk.fp8adam_last_error()
+    misaligned = (pk.TensorArg * 1)(pk.TensorArg(16, 40, 48, 64, 80, 96, 10))
+    assert L.fp8adam_step_noalloc(misaligned, 1, ctypes.byref(cfg), ctypes.byref(hp), None) == -2
+    max_elems = (((1 << 32) - 1) // 256 & ~7) * 1024
+    big = (pk.TensorArg * 2)(pk.TensorArg(16, 32, 48, 64, 80, 96, max_elems // 2),
+                             pk.TensorArg(16, 32, 48, 64, 80, 96, max_elems // 2 + 64))
+    assert L.fp8adam_step_noalloc(big, 2, ctypes.byref(cfg), ctypes.byref(hp), None) == -1
+    assert "too many elements" in pk.fp8adam_last_error()
+    bad_hp = pk.HParamsArg(1e-3, 1.5, 0.999, 1e-8, 0.0, 1)
+    assert L.fp8adam_step_noalloc(one, 1, ctypes.byref(cfg), ctypes.byref(bad_hp), None) == -1
+    assert "beta" in pk.fp8adam_last_error()
