@@ -156,16 +156,24 @@ typedef struct {
     float *amax_history;
 } fp8adam_tensor;
 
-/* Hyperparameters of one step.  step is the 1-based t used for bias correction. */
+/* Hyperparameters of one step: the quantities of Adam as the daoxuan.cc explainer describes
+ * it (section on why Adam keeps m in E4M3 and v in E5M2, subsection on the asymmetry of the
+ * update: m and v moving averages of g and g^2, m in the numerator times the learning rate,
+ * the square root of v in the denominator; subsection with the numerical example: eps added
+ * after the square root) and the decoupled weight decay of the AdamW call in the zyxy.net
+ * article's code example.  step is the 1-based t used for bias correction (1 - beta^t);
+ * lr and weight_decay finite; beta1, beta2 in [0, 1); eps >= 0. */
 typedef struct {
     float lr, beta1, beta2, eps, weight_decay;
     int64_t step;
 } fp8adam_hparams;
 
-/* Per-tensor diagnostics of the most recent step (amax tracking and
- * under/overflow monitoring).  In block mode amax_* is the max over the
- * tensor's blocks and scale_* the largest block scale; both need collect_stats
- * in block mode (else 0). */
+/* Per-tensor diagnostics of the most recent step: the max-abs tracking and the
+ * underflow / overflow monitoring of the zyxy.net article's strategies section (dynamic
+ * range from the tracked max-abs value; small values lost to zero, large ones saturating),
+ * and the daoxuan.cc explainer's numerical example (a small v stored as zero in E4M3).
+ * In block mode amax_* is the max over the tensor's blocks and scale_* the largest
+ * block scale; both need collect_stats in block mode (else 0). */
 typedef struct {
     float amax_m, amax_v;   /* max |m'| and max v' over the tensor */
     float scale_m, scale_v; /* new scales */
@@ -179,7 +187,9 @@ typedef struct {
 
 typedef struct fp8adam_ctx fp8adam_ctx;
 
-/* Build a context over n tensors: validates them (EINVAL / EALIGN), builds the
+/* Quantizing the Adam moments of every tensor of a model (shd-paper.top summary, method
+ * details: both moments in FP8) as one multi-tensor step.
+ * Build a context over n tensors: validates them (EINVAL / EALIGN), builds the
  * multi-tensor chunk table and the per-tensor descriptors on the device
  * (allocates; ENOMEM / EHIP), and synchronizes `stream` before returning.
  * *out receives the handle (NULL on failure).  The device is the current one.
@@ -189,7 +199,9 @@ typedef struct fp8adam_ctx fp8adam_ctx;
 int fp8adam_init(fp8adam_ctx **out, const fp8adam_tensor *tensors, int32_t n,
                  const fp8adam_config *cfg, hipStream_t stream);
 
-/* One optimizer step over every tensor of the context, enqueued on `stream`
+/* The per-element arithmetic at the top of this header (dequantize, Adam/AdamW update from
+ * the daoxuan.cc explainer's statement of the update, new amax, requantize with saturation).
+ * One optimizer step over every tensor of the context, enqueued on `stream`
  * and returning at once.  Validates hp (EINVAL).  Allocates nothing.  After the
  * stream reaches the end of the step each tensor's (codes, scale) pair is
  * consistent.  Steps of one context must not overlap.  `stream` must belong to the
@@ -263,7 +275,9 @@ int fp8adam_step_amp(fp8adam_ctx *ctx, const fp8adam_hparams *hp, const fp8adam_
 int fp8adam_step_noalloc(const fp8adam_tensor *tensors, int32_t n, const fp8adam_config *cfg,
                          const fp8adam_hparams *hp, hipStream_t stream);
 
-/* Copy the diagnostics of the last step into out_host[0..n) (n = the context's
+/* The diagnostics of fp8adam_stats_t (the zyxy.net article, strategies: tracked max-abs,
+ * underflow and overflow).
+ * Copy the diagnostics of the last step into out_host[0..n) (n = the context's
  * tensor count; EINVAL otherwise).  Synchronizes `stream`. */
 int fp8adam_stats(fp8adam_ctx *ctx, fp8adam_stats_t *out_host, int32_t n, hipStream_t stream);
 
@@ -309,6 +323,17 @@ int fp8adam_encode_sr(int32_t fmt, const float *x, const uint16_t *r16, uint8_t 
  * compared with.  src, dst: device, 16-byte aligned, not overlapping; bytes a multiple of
  * 16 (EINVAL otherwise, EALIGN for misaligned pointers). */
 int fp8adam_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+
+/* The update pass's access pattern with trivial arithmetic, over n elements: reads p (n fp32
+ * weights, or bf16 with master FP8ADAM_MASTER_BF16), g (n bf16), m_in and v_in (n bytes each),
+ * writes p in place (p += g) and m_out, v_out (n bytes each): 14 bytes per element (10 with a
+ * bf16 master), with the pass's buffer instructions, non-temporal cache policy, one-shot
+ * work-groups (1024 elements; 2048 with a bf16 master) and XCD order.  Its rate is the
+ * practical ceiling of the pass's byte mix (4 read streams, 3 write streams) on the GPU it runs
+ * on.  n: a multiple of the work-group's elements (EINVAL otherwise); device pointers, 16-byte
+ * aligned (EALIGN), caller-owned; m_out and v_out must not overlap the inputs. */
+int fp8adam_stream_mix(int32_t master, void *p, const void *g, const void *m_in, const void *v_in,
+                       void *m_out, void *v_out, int64_t n, hipStream_t stream);
 
 /* Enable (1) or disable (0) per-kernel timing with HIP events around every
  * launch of later steps (creates the events; may allocate).  Timing records

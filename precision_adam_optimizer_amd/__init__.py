@@ -44,7 +44,7 @@ EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
            "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy",
-           "fp8adam_step_noalloc")
+           "fp8adam_step_noalloc", "fp8adam_stream_mix")
 
 # limits of fp8adam_step_noalloc (the header's FP8ADAM_NOALLOC_* macros)
 NOALLOC_MAX_TENSORS = 4096
@@ -134,12 +134,14 @@ def load() -> ctypes.CDLL:
     L.fp8adam_encode_sr_bits_range.argtypes = [i32, ctypes.c_uint32, i64, ctypes.c_uint32, vp, vp]
     L.fp8adam_encode_sr.argtypes = [i32, vp, vp, vp, i64, vp]
     L.fp8adam_stream_copy.argtypes = [vp, vp, i64, vp]
+    L.fp8adam_stream_mix.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, vp]
     L.fp8adam_step_noalloc.argtypes = [ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg),
                                        ctypes.POINTER(HParamsArg), vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
                  "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
                  "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
-                 "fp8adam_encode_sr", "fp8adam_stream_copy", "fp8adam_step_noalloc"):
+                 "fp8adam_encode_sr", "fp8adam_stream_copy", "fp8adam_step_noalloc",
+                 "fp8adam_stream_mix"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -253,6 +255,17 @@ def fp8adam_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream: int | None
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= nbytes
     _check(load().fp8adam_stream_copy(_ptr(src), _ptr(dst), nbytes, current_stream() if stream is None else stream))
+
+
+def fp8adam_stream_mix(p: torch.Tensor, g: torch.Tensor, m_in: torch.Tensor, v_in: torch.Tensor,
+                       m_out: torch.Tensor, v_out: torch.Tensor, stream: int | None = None) -> None:
+    n = p.numel()
+    assert p.dtype in (torch.float32, torch.bfloat16) and g.dtype == torch.bfloat16
+    assert all(t.is_contiguous() for t in (p, g, m_in, v_in, m_out, v_out))
+    assert g.numel() == n and all(t.dtype == torch.uint8 and t.numel() == n for t in (m_in, v_in, m_out, v_out))
+    master = MASTER_BF16 if p.dtype == torch.bfloat16 else MASTER_FP32
+    _check(load().fp8adam_stream_mix(master, _ptr(p), _ptr(g), _ptr(m_in), _ptr(v_in), _ptr(m_out), _ptr(v_out), n,
+                                     current_stream() if stream is None else stream))
 
 
 def fp8adam_set_timing(ctx: int, enable: bool) -> None:

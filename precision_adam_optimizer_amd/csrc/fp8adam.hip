@@ -41,18 +41,23 @@ int hip_fail(hipError_t e, const char* what) {
 namespace {
 
 // Speculative schedule: the predicted growth of a tensor's amax from step t-1
-// to step t (t >= 2; 1 at t = 1), the geometric mean of two models of a moving
-// average with factor beta: its mean under a steady gradient grows as
+// to step t (t >= 2; 1 at t = 1), a weighted geometric mean of two models of a
+// moving average with factor beta: its mean under a steady gradient grows as
 // (1 - beta^t) / (1 - beta^(t-1)); its spread under independent noise grows as
-// the square root of the same ratio taken at beta^2.  Gradients lie between
-// the two; the blend keeps the share of mispredicted scales low for both.
+// the square root of the same ratio taken at beta^2.  Minibatch gradients are
+// mostly noise, so the spread model gets weight 3/4: on recorded amax
+// trajectories of the 7B, 13B and 100M lists (steps 4-23) the mispredicted
+// share of (element, moment) pairs is 6.8 / 7.1 / 7.9% against 7.6 / 7.9 /
+// 8.1% with equal weights; on simulated gradients with a per-element mean of
+// one and of three noise standard deviations it mispredicts 7.0% and 4.0%
+// (equal weights 5.8% and 2.2%, the mean model alone 5.9% and 1.2%).
 __host__ __device__ inline float amax_growth(double beta, double t) {
   const double mean_prev = 1.0 - pow(beta, t - 1.0);
   const double var_prev = 1.0 - pow(beta * beta, t - 1.0);
   if (!(mean_prev > 0.0) || !(var_prev > 0.0)) return 1.0f;
   const double mean_growth = (1.0 - pow(beta, t)) / mean_prev;
   const double spread_growth = sqrt((1.0 - pow(beta * beta, t)) / var_prev);
-  return (float)sqrt(mean_growth * spread_growth);
+  return (float)(pow(mean_growth, 0.25) * pow(spread_growth, 0.75));
 }
 
 // ------------------------------------------- loss scaling and clipping
@@ -273,6 +278,39 @@ __global__ __launch_bounds__(kThreads) void k_stream_copy(const vu4* __restrict_
   }
 }
 
+// The update pass's byte stream with trivial arithmetic (p += g, codes xor g):
+// per group of four elements it reads the weights (16 bytes fp32 / 8 bf16),
+// the gradients (8) and two code words (4 each), writes the weights back in
+// place and two code words to other buffers, with the pass's buffer
+// instructions, cache policy, one-shot work-group shape and XCD order.  Its
+// rate is the practical ceiling for the pass's access pattern on the GPU it
+// runs on.
+template <bool BF16P>
+__global__ __launch_bounds__(kThreads) void k_stream_mix(void* p, const uint16_t* __restrict__ g,
+                                                         const uint8_t* __restrict__ m, const uint8_t* __restrict__ v,
+                                                         uint8_t* __restrict__ m_out, uint8_t* __restrict__ v_out,
+                                                         int64_t nparts) {
+  const int64_t w = work_index<kXcdStreams>(nparts);
+  if (w < 0) return;
+  constexpr int PL = upd_part_log2<BF16P>();
+  constexpr int64_t kLen = (int64_t)1 << PL;
+  const int64_t start = w << PL;
+  const TensorDesc d{p, g, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr};
+  const PartBufs B = part_bufs<BF16P>(d, m, v, start, kLen);
+  const Rsrc bdm = rsrc(m_out + start, kLen), bdv = rsrc(v_out + start, kLen);
+  for (uint32_t o = kGroup * threadIdx.x; o < (uint32_t)kLen; o += kSubTile) {
+    Group G;
+    load_group_buf<BF16P>(B, o, G, true);
+    float x[4];
+    unpack_p<BF16P>(G, x);
+    x[0] += bf16_lo(G.g.x);
+    x[1] += bf16_hi(G.g.x);
+    x[2] += bf16_lo(G.g.y);
+    x[3] += bf16_hi(G.g.y);
+    store_group_buf<BF16P>(B.p, bdm, bdv, o, x, G.cm ^ G.g.x, G.cv ^ G.g.y);
+  }
+}
+
 // A fresh optimizer state's scales and history (fp8adam_config.zero_state): one
 // work-group per tensor writes 1.0 into every scale slot of m and v and zeroes
 // the 2H-entry amax history; the codes are cleared with a memset.
@@ -392,6 +430,8 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_partial) (void)hipFree(c->d_partial);
   if (c->d_part_amax) (void)hipFree(c->d_part_amax);
   if (c->d_flags) (void)hipFree(c->d_flags);
+  if (c->d_fix_count) (void)hipFree(c->d_fix_count);
+  if (c->d_fix_list) (void)hipFree(c->d_fix_list);
   if (c->d_old_scale) (void)hipFree(c->d_old_scale);
   if (c->d_counters) (void)hipFree(c->d_counters);
   if (c->d_gpart) (void)hipFree(c->d_gpart);
@@ -591,6 +631,8 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * 2 * (size_t)n);
     if (e == hipSuccess && (spec || delayed)) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nuparts));
     if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
+    if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_count, sizeof(uint32_t));
+    if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_list, sizeof(uint32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
@@ -957,6 +999,34 @@ int fp8adam_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
   if (groups > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "copy too large");
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)groups), dim3(kThreads), 0, stream, static_cast<const vu4*>(src),
                      static_cast<vu4*>(dst), n16);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_stream_mix(int32_t master, void* p, const void* g, const void* m_in, const void* v_in, void* m_out,
+                       void* v_out, int64_t n, hipStream_t stream) {
+  if (master != FP8ADAM_MASTER_FP32 && master != FP8ADAM_MASTER_BF16) return fail(FP8ADAM_EINVAL, "bad master dtype");
+  const bool bf16 = master == FP8ADAM_MASTER_BF16;
+  const int pl = bf16 ? upd_part_log2<true>() : upd_part_log2<false>();
+  if (n < 0 || (n & (((int64_t)1 << pl) - 1)))
+    return fail(FP8ADAM_EINVAL, "n must be a non-negative multiple of " + std::to_string(1 << pl));
+  if (n > 0 && (!p || !g || !m_in || !v_in || !m_out || !v_out)) return fail(FP8ADAM_EINVAL, "null pointer");
+  for (const void* q : {(const void*)p, g, m_in, v_in, (const void*)m_out, (const void*)v_out})
+    if ((uintptr_t)q & 15u) return fail(FP8ADAM_EALIGN, "every buffer must be 16-byte aligned");
+  const int64_t nparts = n >> pl;
+  if (nparts > kMaxGroups) return fail(FP8ADAM_EINVAL, "n too large for one launch");
+  if (nparts == 0) return 0;
+  const auto* gg = static_cast<const uint16_t*>(g);
+  const auto* mi = static_cast<const uint8_t*>(m_in);
+  const auto* vi = static_cast<const uint8_t*>(v_in);
+  auto* mo = static_cast<uint8_t*>(m_out);
+  auto* vo = static_cast<uint8_t*>(v_out);
+  if (bf16)
+    hipLaunchKernelGGL(k_stream_mix<true>, dim3(grid_for<kXcdStreams>(nparts)), dim3(kThreads), 0, stream, p, gg, mi, vi,
+                       mo, vo, nparts);
+  else
+    hipLaunchKernelGGL(k_stream_mix<false>, dim3(grid_for<kXcdStreams>(nparts)), dim3(kThreads), 0, stream, p, gg, mi,
+                       vi, mo, vo, nparts);
   HIP_TRY(hipGetLastError());
   return 0;
 }

@@ -102,20 +102,16 @@ using namespace fp8adam;
 #ifndef FP8ADAM_NT_AMAX
 #define FP8ADAM_NT_AMAX 1
 #endif
-#ifndef FP8ADAM_NT_UPDATE_LD
-#define FP8ADAM_NT_UPDATE_LD 1
+// Cache-policy operand of the streamed buffer loads and stores of the amax,
+// update and block passes (gfx950: bit 0 sc0, bit 1 nt, bit 4 sc1); 2 = nt.
+#ifndef FP8ADAM_BUF_LOAD_POLICY
+#define FP8ADAM_BUF_LOAD_POLICY 2
 #endif
-#ifndef FP8ADAM_NT_UPDATE_ST
-#define FP8ADAM_NT_UPDATE_ST 1
-#endif
-#ifndef FP8ADAM_NT_BLOCK_LD
-#define FP8ADAM_NT_BLOCK_LD 1
+#ifndef FP8ADAM_BUF_STORE_POLICY
+#define FP8ADAM_BUF_STORE_POLICY 2
 #endif
 #ifndef FP8ADAM_XCD_ORDER
 #define FP8ADAM_XCD_ORDER 1  // update / block passes: each XCD walks its own contiguous eighth
-#endif
-#ifndef FP8ADAM_NT_BLOCK_ST
-#define FP8ADAM_NT_BLOCK_ST 1
 #endif
 
 constexpr int kThreads = 256;                     // 4 waves of 64
@@ -361,19 +357,67 @@ struct Group {
   vf4 p;         // fp32 master (or 4 bf16 in .x/.y)
 };
 
-template <bool BF16P, bool NT>
-__device__ __forceinline__ void load_group(const TensorDesc& d, int64_t i, Group& G, bool with_p) {
-  G.g = ld_stream<vu2, NT>(d.g + i);
-  G.cm = ld_stream<uint32_t, NT>(d.m + i);
-  G.cv = ld_stream<uint32_t, NT>(d.v + i);
+// Buffer instructions for the streamed accesses of the amax, update and block
+// passes.  A work-group addresses its own part of a tensor through buffer
+// resources based at the part's first element (64-bit base in scalar
+// registers, 32-bit offsets within the part).  On the update pass's byte mix
+// (read 16 + 8 + 4 + 4, write 16 + 4 + 4 bytes per lane, one-shot 1024-element
+// work-groups, non-temporal) buffer loads and stores streamed 6.42-6.49 TB/s
+// against 6.02-6.08 TB/s for global ones (three runs each, one box).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit data format
+constexpr int kLdPol = FP8ADAM_BUF_LOAD_POLICY;
+constexpr int kStPol = FP8ADAM_BUF_STORE_POLICY;
+
+// Resource over [base, base + bytes); bytes < 2^31 (a part or a chunk).
+__device__ __forceinline__ Rsrc rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+// The four input streams of elements [start, start + len) of a tensor (m, v:
+// the code buffers read).
+struct PartBufs {
+  Rsrc p, g, m, v;
+};
+
+template <bool BF16P>
+__device__ __forceinline__ PartBufs part_bufs(const TensorDesc& d, const uint8_t* m, const uint8_t* v, int64_t start,
+                                              int64_t len) {
+  constexpr int64_t PB = BF16P ? 2 : 4;
+  return PartBufs{rsrc(static_cast<const char*>(d.p) + PB * start, PB * len), rsrc(d.g + start, 2 * len),
+                  rsrc(m + start, len), rsrc(v + start, len)};
+}
+
+// Loads of the group of four elements at offset o (elements) of the part.
+template <bool BF16P>
+__device__ __forceinline__ void load_group_buf(const PartBufs& B, uint32_t o, Group& G, bool with_p) {
+  G.g = __builtin_amdgcn_raw_buffer_load_b64(B.g, 2 * o, 0, kLdPol);
+  G.cm = __builtin_amdgcn_raw_buffer_load_b32(B.m, o, 0, kLdPol);
+  G.cv = __builtin_amdgcn_raw_buffer_load_b32(B.v, o, 0, kLdPol);
   if (with_p) {
     if constexpr (BF16P) {
-      const vu2 pb = ld_stream<vu2, NT>(static_cast<const uint16_t*>(d.p) + i);
+      const vu2 pb = __builtin_amdgcn_raw_buffer_load_b64(B.p, 2 * o, 0, kLdPol);
       G.p = vf4{__uint_as_float(pb.x), __uint_as_float(pb.y), 0.0f, 0.0f};
     } else {
-      G.p = ld_stream<vf4, NT>(static_cast<const float*>(d.p) + i);
+      const vu4 x = __builtin_amdgcn_raw_buffer_load_b128(B.p, 4 * o, 0, kLdPol);
+      G.p = vf4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
     }
   }
+}
+
+// Stores of the group at offset o: the four weights and the two code words.
+template <bool BF16P>
+__device__ __forceinline__ void store_group_buf(Rsrc bp, Rsrc bm, Rsrc bv, uint32_t o, const float (&p)[4],
+                                                uint32_t wm, uint32_t wv) {
+  if constexpr (BF16P) {
+    __builtin_amdgcn_raw_buffer_store_b64(vu2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])}, bp, 2 * o, 0, kStPol);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        vu4{__float_as_uint(p[0]), __float_as_uint(p[1]), __float_as_uint(p[2]), __float_as_uint(p[3])}, bp, 4 * o, 0,
+        kStPol);
+  }
+  __builtin_amdgcn_raw_buffer_store_b32(wm, bm, o, 0, kStPol);
+  __builtin_amdgcn_raw_buffer_store_b32(wv, bv, o, 0, kStPol);
 }
 
 // Unpack 4 grads, 4 dequantized moments, and the fresh moments.  p (the
@@ -396,15 +440,6 @@ __device__ __forceinline__ void unpack_p(const Group& G, float (&p)[4]) {
     p[0] = bf16_lo(a); p[1] = bf16_hi(a); p[2] = bf16_lo(b); p[3] = bf16_hi(b);
   } else {
     p[0] = G.p.x; p[1] = G.p.y; p[2] = G.p.z; p[3] = G.p.w;
-  }
-}
-
-template <bool BF16P, bool NT>
-__device__ __forceinline__ void store_p4(const TensorDesc& d, int64_t i, const float (&p)[4]) {
-  if constexpr (BF16P) {
-    st_stream<vu2, NT>(static_cast<uint16_t*>(d.p) + i, vu2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-  } else {
-    st_stream<vf4, NT>(static_cast<float*>(d.p) + i, vf4{p[0], p[1], p[2], p[3]});
   }
 }
 
@@ -474,6 +509,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
   const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
   const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
   const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
+  const PartBufs B = part_bufs<BF16P>(d, d.m, d.v, start, end - start);
   uint32_t am = 0, av = 0;
 
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
@@ -481,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_AMAX != 0>(d, i, G[u], L2);
+      if (i < gend) load_group_buf<BF16P>(B, (uint32_t)(i - start), G[u], L2);
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; u++) {
@@ -642,13 +678,15 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
   }
   uint32_t am = 0, av = 0;  // speculative / delayed: this part's amax
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
+  const PartBufs B = part_bufs<BF16P>(d, d.m, d.v, start, end - start);
+  const Rsrc bdm = rsrc(dm + start, end - start), bdv = rsrc(dv + start, end - start);
 
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kUpdUnroll) {
     Group G[kUpdUnroll];
 #pragma unroll
     for (int u = 0; u < kUpdUnroll; u++) {
       const int64_t i = base + (int64_t)u * kSubTile;
-      if (i < gend) load_group<BF16P, FP8ADAM_NT_UPDATE_LD != 0>(d, i, G[u], true);
+      if (i < gend) load_group_buf<BF16P>(B, (uint32_t)(i - start), G[u], true);
     }
 #pragma unroll
     for (int u = 0; u < kUpdUnroll; u++) {
@@ -676,9 +714,7 @@ __global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restric
           for (int j = 0; j < 4; j++)
             count_element<MF, VF, STATS>(cnt, m1[j], v1[j], qm[j], qv[j], wm >> (8 * j), wv >> (8 * j));
         }
-        store_p4<BF16P, FP8ADAM_NT_UPDATE_ST != 0>(d, i, p);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dm + i, wm);
-        st_stream<uint32_t, FP8ADAM_NT_UPDATE_ST != 0>(dv + i, wv);
+        store_group_buf<BF16P>(B.p, bdm, bdv, (uint32_t)(i - start), p, wm, wv);
       }
     }
   }
@@ -816,8 +852,9 @@ template <int MF, int VF>
 __global__ __launch_bounds__(64) void k_spec_prepare(const TensorDesc* __restrict__ descs,
                                                      const uint32_t* __restrict__ amax, StepConsts c,
                                                      const GradCtl* __restrict__ gctl, float* __restrict__ prep,
-                                                     int32_t n) {
+                                                     int32_t n, uint32_t* __restrict__ fix_count) {
   const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t == 0) st_global<uint32_t>(fix_count, 0u);  // k_spec_reduce appends this step's fix-up work
   if (t >= n || amp_apply(gctl, c)) return;
   const TensorDesc d = descs[t];
   if (d.numel == 0) return;
@@ -836,7 +873,9 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
                                                                 int32_t* __restrict__ flags,
                                                                 unsigned long long* __restrict__ counters,
                                                                 int chunk_log2, int part_log2, StepConsts c,
-                                                                const GradCtl* __restrict__ gctl) {
+                                                                const GradCtl* __restrict__ gctl,
+                                                                uint32_t* __restrict__ fix_count,
+                                                                uint32_t* __restrict__ fix_list) {
   const int t = blockIdx.x;
   if (amp_apply(gctl, c)) {  // skipped step: scales and amax stay, nothing to fix up
     if (threadIdx.x == 0) flags[t] = 0;
@@ -849,6 +888,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
   parts_max(part_amax + part0, nparts, am, av);
   __shared__ uint32_t red[2][kReduceThreads / 64];
   __shared__ int32_t flag;
+  __shared__ uint32_t list_base;
   am = wave_max(am);
   av = wave_max(av);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -878,8 +918,15 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     amax[2 * t + 1] = av;
     flags[t] = f;
     flag = f;
+    // room for the tensor's chunks in the fix-up's work list (the order of the
+    // tensors there does not matter: every chunk is fixed up on its own)
+    list_base = f ? atomicAdd(fix_count, (uint32_t)((d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2)) : 0u;
   }
   __syncthreads();
+  if (flag) {
+    const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
+    for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) fix_list[list_base + k] = (uint32_t)(d.chunk0 + k);
+  }
   if constexpr (STATS) {
     // the fix-up recounts the underflow / saturation counts of a re-quantized moment
     if (threadIdx.x == 0 && (flag & 1)) {
@@ -992,16 +1039,15 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
   }
 }
 
-// Chunks per fix-up work-group.  Most chunks belong to tensors whose scale
-// was predicted right; a work-group finds the flags of its chunks with one
-// round of loads and returns at once if none is set.  Measured on the 7B list
-// (two runs each, one box): 1 chunk 449/456 us per fix-up, 2 chunks 444/440,
-// 4 chunks 454/448, 8 chunks 476/478 (fewer, longer work-groups on the
-// flagged tensors).
-#ifndef FP8ADAM_FIX_CHUNKS
-#define FP8ADAM_FIX_CHUNKS 2
+// Work-groups of the fix-up: a fixed grid striding over the work list of the
+// flagged chunks, which k_spec_reduce builds, so no work-group is launched for
+// the (most) chunks whose tensor was predicted right.  Measured on the 7B list
+// (steps 4-23, 6.8% of the (element, moment) pairs moved, one box): 1024
+// work-groups 497 us per fix-up, 2048 459, 4096 395, 8192 369, 16384 359.
+#ifndef FP8ADAM_FIX_GROUPS
+#define FP8ADAM_FIX_GROUPS 16384
 #endif
-constexpr int kFixChunks = FP8ADAM_FIX_CHUNKS;
+constexpr int64_t kFixGroups = FP8ADAM_FIX_GROUPS;
 
 template <int MF, int VF, bool STATS, bool SR>
 __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict__ descs,
@@ -1011,26 +1057,17 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
                                                     const float* __restrict__ old_scale,
                                                     const int32_t* __restrict__ flags, StepConsts c,
                                                     unsigned long long* __restrict__ counters, int chunk_log2,
-                                                    int64_t nchunks, const GradCtl* __restrict__ gctl) {
+                                                    const uint32_t* __restrict__ fix_count,
+                                                    const uint32_t* __restrict__ fix_list,
+                                                    const GradCtl* __restrict__ gctl) {
   if (amp_apply(gctl, c)) return;
-  const int64_t w0 = (int64_t)blockIdx.x * kFixChunks;
-  int tids[kFixChunks];
-  int32_t fl[kFixChunks];
-  bool any = false;
-#pragma unroll
-  for (int k = 0; k < kFixChunks; k++) tids[k] = w0 + k < nchunks ? chunk_tid[w0 + k] : -1;
-#pragma unroll
-  for (int k = 0; k < kFixChunks; k++) {
-    fl[k] = tids[k] >= 0 ? flags[tids[k]] : 0;
-    any = any || fl[k] != 0;
-  }
-  if (!any) return;  // uniform for the work-group
-  for (int k = 0; k < kFixChunks; k++) {
-    const int32_t f = fl[k];
-    if (!f) continue;
-    const int tid = tids[k];
+  const int64_t nwork = ld_global<uint32_t>(fix_count);
+  for (int64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
+    const int64_t chunk = ld_global<uint32_t>(fix_list + w);
+    const int tid = chunk_tid[chunk];
+    const int32_t f = flags[tid];
     const TensorDesc d = descs[tid];
-    const int64_t start = (w0 + k - d.chunk0) << chunk_log2;
+    const int64_t start = (chunk - d.chunk0) << chunk_log2;
     const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
     uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
     if (f & 1) {
@@ -1097,6 +1134,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
   uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
   uint32_t tam = 0, tav = 0;
   float tsm = 0.0f, tsv = 0.0f;
+  const PartBufs B = part_bufs<BF16P>(d, d.m, d.v, start, end - start);
 
   for (int64_t tile = start; tile < end; tile += (int64_t)kBlock * 8 * kBlkJ) {
     int64_t b0[kBlkJ];
@@ -1114,7 +1152,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
         sm[j] = ld_global<float>(d.sm + b0[j] / kBlock);
         sv[j] = ld_global<float>(d.sv + b0[j] / kBlock);
       }
-      if (full[j]) load_group<BF16P, FP8ADAM_NT_BLOCK_LD != 0>(d, b0[j] + 4 * hl, G[j], true);
+      if (full[j]) load_group_buf<BF16P>(B, (uint32_t)(b0[j] + 4 * hl - start), G[j], true);
     }
 #pragma unroll
     for (int j = 0; j < kBlkJ; j++) {
@@ -1175,9 +1213,7 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
           for (int r = 0; r < 4; r++)
             count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], wm >> (8 * r), wv >> (8 * r));
         }
-        store_p4<BF16P, FP8ADAM_NT_BLOCK_ST != 0>(d, i0, p);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.m + i0, wm);
-        st_stream<uint32_t, FP8ADAM_NT_BLOCK_ST != 0>(d.v + i0, wv);
+        store_group_buf<BF16P>(B.p, B.m, B.v, (uint32_t)(i0 - start), p, wm, wv);
       } else if (ex[j]) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -1253,6 +1289,8 @@ struct fp8adam_ctx {
   uint2* d_part_amax = nullptr;     // speculative / delayed: [<= nuparts] per-part amax of m', v'
   float* d_old_scale = nullptr;     // tensor mode: [n][4]: scales before the step (+ prepared ones)
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
+  uint32_t* d_fix_count = nullptr;  // speculative: chunks in the fix-up's work list this step
+  uint32_t* d_fix_list = nullptr;   // speculative: [<= nchunks] the chunks of the flagged tensors
   unsigned long long* d_counters = nullptr;  // [n][5]
   double* d_gpart = nullptr;        // loss scaling: [norm groups][2] sum of squares and Inf/NaN count of g
   fp8adam_engine::GradCtl* d_gctl = nullptr;       // loss scaling: the decision of the step in flight
@@ -1321,22 +1359,22 @@ void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 template <int MF, int VF>
 void launch_spec_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_prepare<MF, VF>), dim3((unsigned)((c->n + 63) / 64)), dim3(64), 0, s, descs_of(c, c->cur),
-                     c->d_amax, k, c->gctl, c->d_old_scale, c->n);
+                     c->d_amax, k, c->gctl, c->d_old_scale, c->n, c->d_fix_count);
 }
 
 template <int MF, int VF, bool STATS>
 void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
                      descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, part_log2, k, c->gctl);
+                     c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list);
 }
 
 template <int MF, int VF, bool STATS, bool SR>
 void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_fixup<MF, VF, STATS, SR>), dim3((unsigned)((c->nchunks + kFixChunks - 1) / kFixChunks)),
-                     dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax, c->d_old_scale, c->d_flags, k,
-                     c->d_counters, c->chunk_log2, c->nchunks, c->gctl);
+  hipLaunchKernelGGL((k_fixup<MF, VF, STATS, SR>), dim3((unsigned)std::min<int64_t>(c->nchunks, kFixGroups)),
+                     dim3(kThreads), 0, s, descs_of(c, c->cur), descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax,
+                     c->d_old_scale, c->d_flags, k, c->d_counters, c->chunk_log2, c->d_fix_count, c->d_fix_list,
+                     c->gctl);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
