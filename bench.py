@@ -1,18 +1,26 @@
 """Benchmark of the FP8-moment AdamW step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2_7b]
-                    [--schedule two_pass|speculative]
+                    [--schedule two_pass|speculative] [--m-format e4m3|e5m2] [--v-format e4m3|e5m2]
 
 Times K whole optimizer steps (every tensor of the list, one fp8adam_step
 each) after W warm-up steps, with inputs resident in HBM, and prints one JSON
-line: params updated/s, the roofline of the dominant kernel (algorithmic
-bytes / its HIP-event duration, against 8 TB/s, and beside it against a plain
-2 GiB device copy timed on the same GPU), and the CPU oracle timed on a
-bounded sample of the same workload.  Every step gets a fresh gradient draw
-(generated into the bound gradient buffers between steps, outside the timed
-events), so the moments and their scales evolve as in training.
+line: params updated/s; the roofline of the dominant kernel (algorithmic bytes
+/ its HIP-event duration, against 8 TB/s, and beside it against the pass's own
+byte mix streamed with trivial arithmetic by fp8adam_stream_mix on the same
+GPU); the bytes and rate of the whole step, the speculative fix-up included;
+and the CPU oracle timed on the same workload (the whole list for the flat 1M
+tensor and the Llama-2-100M list, a bounded sample of the larger lists).  Every
+step gets a fresh gradient draw (generated into the bound gradient buffers
+between steps, outside the timed events), so the moments and their scales
+evolve as in training.
 
-Other modes (used to make the committed profiles):
+Other modes:
+    --format-sweep     Llama-2-100M list: all four (m, v) format pairs over 20 steps with the
+                       stats counters on; one JSON line with each pair's underflow and
+                       saturation counts (the pages' Fig. 5 format experiment)
+    --collect-stats    count underflow / saturation in the timed steps too (another kernel
+                       instantiation than the default line's)
     --calibrate-copy   a plain device copy of 2 GiB, for HBM counter scaling
     --same-grad        reuse step 1's gradient every step (profiler runs: drawing
                        fresh gradients under counter collection is very slow; the
@@ -105,6 +113,41 @@ def copy_bandwidth(stream) -> float:
     return gbps
 
 
+def mix_bandwidth(stream, master: str) -> tuple[float, float]:
+    """GB/s of the update pass's own byte mix (fp8adam_stream_mix: read p, g and two
+    code streams, write p and two code streams, with the pass's instructions,
+    work-group shape and order, trivial arithmetic) over 2^29 elements (7.5 GB per
+    launch with an fp32 master), timed with HIP events on this GPU.  Where the six
+    buffers land in HBM moves the rate by a few percent, so each of three rounds
+    allocates them anew and times five launches: (best, median) of the rounds."""
+    import torch
+
+    import precision_adam_optimizer_amd as pk
+    n = 1 << 29
+    pdt = torch.bfloat16 if master == "bf16" else torch.float32
+    bpe = 10.0 if master == "bf16" else 14.0
+    rates = []
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            p = torch.zeros(n, dtype=pdt, device="cuda")
+            g = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+            codes = [torch.zeros(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+            for _ in range(2):
+                pk.fp8adam_stream_mix(p, g, *codes, stream=stream.cuda_stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                pk.fp8adam_stream_mix(p, g, *codes, stream=stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            rates.append(bpe * n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+            del p, g, codes
+            torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    rates.sort()
+    return rates[-1], rates[1]
+
+
 def cpu_baseline(w, shapes, idx, threads: int = 1):
     """The oracle on step 1 of the tensors `idx` (inputs drawn with the same
     generators on the GPU, copied to the host): one oracle call per tensor, on
@@ -138,6 +181,59 @@ def cpu_baseline(w, shapes, idx, threads: int = 1):
     return sum(j[0].size for j in jobs), time.perf_counter() - t0
 
 
+FORMATS = [("e4m3", "e5m2"), ("e5m2", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e4m3")]
+
+
+def format_sweep(args):
+    """The Llama-2-100M list in all four (m, v) format pairs, 20 steps each from a
+    fresh state with the stats counters on: per pair, the underflow and saturation
+    counts summed over the steps and at the last step, and the share of moments
+    stored as zero although nonzero (the pages' Fig. 5 format experiment: v in
+    E4M3 loses small second moments to zero)."""
+    import torch
+
+    import precision_adam_optimizer_amd as pk
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pairs = {}
+    for m_fmt, v_fmt in FORMATS:
+        w = workloads.llama2_100m(m_fmt, v_fmt)
+        shapes = w.shapes
+        params = [workloads.make_param(w, i, s, dev) for i, (_, s) in enumerate(shapes)]
+        grads = [workloads.make_grad(w, i, s, 1, dev) for i, (_, s) in enumerate(shapes)]
+        opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, collect_stats=True,
+                          schedule=args.schedule)
+        keys = ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite")
+        total = dict.fromkeys(keys, 0)
+        last = None
+        for t in range(1, w.steps + 1):
+            for i, (_, shp) in enumerate(shapes):
+                grads[i].copy_(workloads.make_grad(w, i, shp, t, dev))
+            opt.step(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, step=t)
+            st = opt.stats()
+            last = {k: sum(x[k] for x in st) for k in keys}
+            for k in keys:
+                total[k] += last[k]
+        opt.close()
+        n = w.total_params
+        pairs[f"{m_fmt}/{v_fmt}"] = {
+            "steps": w.steps, "params": n, "total_over_steps": total, "at_last_step": last,
+            "underflow_v_share_last_step": round(last["underflow_v"] / n, 6),
+            "underflow_m_share_last_step": round(last["underflow_m"] / n, 6)}
+        log(f"{m_fmt}/{v_fmt}: over {w.steps} steps {total}; last step {last}")
+        del params, grads, opt
+        torch.cuda.empty_cache()
+    out = {"metric": "underflow and saturation counts of the FP8 moments, Llama-2-100M list, four format pairs",
+           "unit": "elements", "n_gpus": 1, "data": "synthetic",
+           "config": {"workload": "llama2_100m", "tensors": len(workloads.llama2_100m().shapes),
+                      "params": workloads.llama2_100m().total_params, "steps": 20, "schedule": args.schedule,
+                      "grad": "fresh bf16 draw per step, per-tensor scale 10^U(-7,-1)"},
+           "pairs": pairs}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,9 +247,15 @@ def main():
                     help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="stochastic: moments rounded with a Philox4x32-10 stream (seed 1234)")
+    ap.add_argument("--m-format", choices=["e4m3", "e5m2"], default=None,
+                    help="format of the first moment (default: the workload's, E4M3)")
+    ap.add_argument("--v-format", choices=["e4m3", "e5m2"], default=None,
+                    help="format of the second moment (default: the workload's, E5M2)")
     ap.add_argument("--amp", action="store_true",
                     help="loss-scaled gradients (scale 2^16) through the fused unscale / Inf-NaN skip / "
                          "global-norm clip (max_norm 1.0) step")
+    ap.add_argument("--collect-stats", action="store_true")
+    ap.add_argument("--format-sweep", action="store_true")
     ap.add_argument("--same-grad", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -166,6 +268,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.format_sweep:
+        format_sweep(args)
+        return
 
     import torch
 
@@ -173,6 +278,13 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]()
+    if args.m_format or args.v_format:
+        w.m_fmt = args.m_format or w.m_fmt
+        w.v_fmt = args.v_format or w.v_fmt
+        if args.workload == "llama2_100m":
+            w.name = f"llama2_100m_{w.m_fmt}_{w.v_fmt}"
+        else:
+            w.name = f"{w.name}_{w.m_fmt}_{w.v_fmt}"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     shapes = w.shapes
@@ -187,7 +299,7 @@ def main():
                                  and scaling == "just_in_time") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
                       schedule=schedule, decay_mode=w.decay_mode, scaling=scaling, rounding=args.rounding,
-                      seed=1234)
+                      seed=1234, collect_stats=args.collect_stats)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
 
@@ -218,6 +330,9 @@ def main():
 
     opt.set_timing(True)
     evs = []
+    requant = []  # per timed step: (element, moment) pairs brought to the true scale by the fix-up
+    stat_keys = ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite")
+    stat_sum = dict.fromkeys(stat_keys, 0)
     wall0 = time.perf_counter()
     for _ in range(args.steps):
         t += 1
@@ -227,6 +342,12 @@ def main():
         opt_step(t)
         e1.record(stream)
         evs.append((e0, e1))
+        # read outside the events (this synchronizes the stream between steps)
+        st = opt.stats()
+        requant.append(sum(x["requantized"] for x in st))
+        if args.collect_stats:
+            for k in stat_keys:
+                stat_sum[k] += sum(x[k] for x in st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = sum(a.elapsed_time(b) for a, b in evs)
@@ -248,47 +369,75 @@ def main():
     achieved = alg_bytes / kavg_s / 1e9
     # the counters are per kernel instantiation: stochastic rounding has its own
     traffic = load_traffic(w.name, kernel + ("_sr" if args.rounding == "stochastic" else ""))
-    # bytes the whole step moved: + the amax pass (g, m, v; and p with coupled L2) in the
-    # two-pass schedule; the speculative schedule's fix-up (the codes of mispredicted moments
-    # read and written) is timed separately and reported as fixup_avg_us
-    fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
+    # bytes the whole step moved:
+    #   the dominant pass (algorithmic bytes);
+    #   + the amax pass (g, m, v; and p with coupled L2) in the two-pass schedule;
+    #   + the per-part amax partials the speculative and delayed passes write and the
+    #     check / commit reads (8 bytes each way per part of 1024 elements, 2048 with bf16);
+    #   + the fix-up: the codes of every mispredicted moment, read and written (2 bytes per
+    #     (element, moment) pair; the rare groups it recomputes read 3 bytes more, not counted);
+    #   + the gradient-norm pass with loss scaling (g read once).
+    two_pass = w.granularity == "tensor" and schedule == "two_pass" and scaling == "just_in_time"
     amax_bpp = 4.0 + ((4.0 if w.master == "fp32" else 2.0) if w.decay_mode == "l2" else 0.0)
-    step_bytes = alg_bytes + (amax_bpp * total if (w.granularity == "tensor" and schedule == "two_pass"
-                                                   and scaling == "just_in_time") else 0.0)
-    if args.amp:  # + the gradient-norm pass (g read once)
+    part = 2048 if w.master == "bf16" else 1024
+    step_bytes = alg_bytes + (amax_bpp * total if two_pass else 0.0)
+    if schedule == "speculative" or scaling == "delayed":
+        step_bytes += 16.0 * -(-total // part)
+    fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
+    fix_pairs = sum(requant) / max(len(requant), 1)
+    fix_bytes = 2.0 * fix_pairs
+    step_bytes += fix_bytes
+    if args.amp:
         step_bytes += 2.0 * total
+    step_gbps = step_bytes / (ms_per_step / 1e3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
                 "kernel_avg_us": round(kavg_s * 1e6, 2), "algorithmic_bytes_per_launch": alg_bytes,
                 "bytes_per_param": bpp,
-                "whole_step_GBps_excluding_fixup": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1)}
+                "whole_step_bytes": round(step_bytes), "whole_step_GBps": round(step_gbps, 1),
+                "whole_step_frac": round(step_gbps / HBM_PEAK_GBS, 4)}
     if schedule == "speculative":
-        roofline["fixup_avg_us"] = round(fix_ms / max(fix_n, 1) * 1e3, 2)
+        fix_us = fix_ms / max(fix_n, 1) * 1e3
+        roofline.update({
+            "fixup_avg_us": round(fix_us, 2),
+            "fixup_pairs_per_step": round(fix_pairs),
+            "fixup_pair_share": round(fix_pairs / (2.0 * total), 5),
+            "fixup_bytes_per_step": round(fix_bytes),
+            "fixup_GBps": round(fix_bytes / (fix_us / 1e6) / 1e9, 1) if fix_us > 0 else None,
+            "fixup_pairs_each_step": requant})
 
+    mix_best, mix_med = mix_bandwidth(stream, w.master)
     copy_gbps = copy_bandwidth(stream)
-    log(f"device copy: {copy_gbps:.0f} GB/s (read + write); {kernel} at {achieved / copy_gbps:.1%} of it")
+    log(f"pass byte mix: {mix_med:.0f} GB/s (median; best {mix_best:.0f}); {kernel} at {achieved / mix_med:.1%} of it; "
+        f"device copy {copy_gbps:.0f} GB/s")
+    roofline["mix_GBps"] = round(mix_med, 1)
+    roofline["mix_GBps_best"] = round(mix_best, 1)
+    roofline["frac_of_mix"] = round(achieved / mix_med, 4)
     roofline["copy_GBps"] = round(copy_gbps, 1)
-    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
-        # step 1 of layer 0 (its nine tensors) on one thread, then of layers 0-3 on the
-        # host's cores, one oracle call per tensor (the box gives a job 16 cores)
-        layered = any(n.startswith("layers.0.") for n, _ in shapes)
-        idx1 = [i for i, (n, _) in enumerate(shapes) if n.startswith("layers.0.")] or [0]
+        threads = max(1, min(16, os.cpu_count() or 1))
+        if total <= 250_000_000:
+            # small lists: step 1 of the whole list, on one thread and on the host's cores
+            idx1 = idxn = list(range(len(shapes)))
+            what = f"step 1 of the whole list ({len(shapes)} tensors, {total} params)"
+            what1 = "single thread on the whole list"
+        else:
+            # step 1 of layer 0 (its nine tensors) on one thread, then of layers 0-3 on the
+            # host's cores, one oracle call per tensor (the box gives a job 16 cores)
+            idx1 = [i for i, (n, _) in enumerate(shapes) if n.startswith("layers.0.")] or [0]
+            idxn = [i for i, (n, _) in enumerate(shapes)
+                    if any(n.startswith(f"layers.{k}.") for k in range(4))] or [0]
+            what = f"step 1 of the {len(idxn)} tensors of layers 0-3 of the same list"
+            what1 = "single thread on layer 0"
         n1, s1 = cpu_baseline(w, shapes, idx1, threads=1)
         log(f"cpu oracle, 1 thread: {n1 / s1:.3e} params/s over {n1} params")
-        threads = max(1, min(16, os.cpu_count() or 1))
-        idxn = [i for i, (n, _) in enumerate(shapes)
-                if any(n.startswith(f"layers.{k}.") for k in range(4))] or [0]
         nn, sn = cpu_baseline(w, shapes, idxn, threads=threads)
         log(f"cpu oracle, {threads} threads: {nn / sn:.3e} params/s over {nn} params")
         cpu = {"value": round(nn / sn, 1), "unit": "params/s", "cores": threads, "kind": "oracle",
-               "sample": (f"step 1 of the {len(idxn)} tensors of layers 0-3 ({nn} params) of the same list, "
-                          if layered else f"step 1 of the whole list ({len(idxn)} tensor, {nn} params), ") +
-                         f"C oracle, one call per tensor on {threads} threads, {sn:.1f} s wall; " +
-                         (f"single thread on layer 0 ({n1} params)" if layered else "single thread") +
-                         f": {n1 / s1:.4g} params/s",
+               "sample": f"{what} ({nn} params), C oracle, one call per tensor on {threads} threads, "
+                         f"{sn:.1f} s wall; {what1} ({n1} params): {n1 / s1:.4g} params/s",
                "value_1_thread": round(n1 / s1, 1)}
 
     out = {
@@ -315,6 +464,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.collect_stats:
+        out["stats_over_timed_steps"] = stat_sum
     opt.close()
     print(json.dumps(out), flush=True)
 

@@ -234,20 +234,26 @@ def test_flat_1m_ten_steps():
     run_full(workloads.flat_1m(), steps=10, sample=[0], collect_stats=True)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_llama2_100m_all_format_pairs():
-    """Every tensor of the Llama-2-100M-shaped list checked against the oracle;
-    20 steps for (E4M3, E5M2), 3 for the other pairs; underflow and
-    saturation counts equal; v in E4M3 underflows far more than v in E5M2."""
+    """The Llama-2-100M-shaped list in all four (m, v) format pairs, 20 steps
+    each, stats on: every tensor against the oracle at every step (codes,
+    scales, weights, and the underflow / saturation counts equal); v in E4M3
+    underflows far more than v in E5M2 over the 20 steps and in each of the
+    first three (with fresh zero-mean gradients every step, a moment that once
+    held a representable value rarely falls back below the smallest code, so the
+    E4M3 underflow of v dies out after a few steps)."""
     under_v = {}
     for m_fmt, v_fmt in FORMATS:
         w = workloads.llama2_100m(m_fmt, v_fmt)
-        steps = 20 if (m_fmt, v_fmt) == ("e4m3", "e5m2") else 3
-        stats = run_full(w, steps=steps, sample=list(range(len(w.shapes))), collect_stats=True)
-        under_v[(m_fmt, v_fmt)] = sum(s["underflow_v"] for s in stats[2])
+        print(f"llama2_100m {m_fmt}/{v_fmt}: 20 steps, every tensor", flush=True)
+        stats = run_full(w, steps=20, sample=list(range(len(w.shapes))), collect_stats=True)
+        under_v[(m_fmt, v_fmt)] = [sum(s["underflow_v"] for s in st) for st in stats]
         assert all(s["saturated_m"] == 0 and s["saturated_v"] == 0 for st in stats for s in st)
-    assert under_v[("e4m3", "e4m3")] > 20 * max(1, under_v[("e4m3", "e5m2")])
-    assert under_v[("e5m2", "e4m3")] > 20 * max(1, under_v[("e5m2", "e5m2")])
+    for a, b in ((("e4m3", "e4m3"), ("e4m3", "e5m2")), (("e5m2", "e4m3"), ("e5m2", "e5m2"))):
+        assert sum(under_v[a]) > 20 * max(1, sum(under_v[b])), (a, under_v[a], b, under_v[b])
+        for t in range(3):
+            assert under_v[a][t] > 20 * max(1, under_v[b][t]), (t + 1, a, under_v[a], b, under_v[b])
 
 
 @pytest.mark.timeout(900)
