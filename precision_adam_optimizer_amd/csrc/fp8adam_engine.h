@@ -617,8 +617,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const TensorDesc* __r
 
 // ------------------------------------------------------------------ pass 2
 
+// Eight waves per SIMD: the buffer resources raise the stochastic-rounding
+// instantiations to 98-101 scalar registers, which leaves room for seven waves;
+// held to eight (a few scalar registers spill to vector lanes), the speculative
+// stochastic-rounding pass runs within 0.2% of the round-to-nearest one (in one
+// process on the same buffers: 15.20 against 15.18 ms on the 7B list, against
+// 15.23-15.26 ms at seven waves).
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
-__global__ __launch_bounds__(kThreads) void k_update(const TensorDesc* __restrict__ descs,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_update(const TensorDesc* __restrict__ descs,
                                                      const TensorDesc* __restrict__ dst_descs,
                                                      const int32_t* __restrict__ chunk_tid,
                                                      const uint32_t* __restrict__ amax,
@@ -1042,8 +1048,11 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
 // Work-groups of the fix-up: a fixed grid striding over the work list of the
 // flagged chunks, which k_spec_reduce builds, so no work-group is launched for
 // the (most) chunks whose tensor was predicted right.  Measured on the 7B list
-// (steps 4-23, 6.8% of the (element, moment) pairs moved, one box): 1024
-// work-groups 497 us per fix-up, 2048 459, 4096 395, 8192 369, 16384 359.
+// (steps 4-23, 6.8% of the (element, moment) pairs moved, one box per sweep):
+// 1024 work-groups 497 us per fix-up, 2048 459, 4096 395, 8192 369, 16384
+// 359, 32768 356, 65536 358; one list item per chunk (32768 elements) against
+// halves 379 us and quarters 392 us; non-temporal stores of the moved codes
+// 366 us against 360 us plain.
 #ifndef FP8ADAM_FIX_GROUPS
 #define FP8ADAM_FIX_GROUPS 16384
 #endif
