@@ -165,3 +165,36 @@ def test_stream_copy_copies_every_byte():
         torch.cuda.synchronize()
         assert torch.equal(dst[:nbytes], src), nbytes
         assert bool((dst[nbytes:] == 0xA5).all()), nbytes
+
+
+@pytest.mark.parametrize("master", ["fp32", "bf16"])
+def test_stream_mix_reads_and_writes_every_element(master):
+    """The byte-mix probe the benchmark uses as the update pass's ceiling moves
+    every byte it counts: p += g in place (fp32, or rounded to nearest-even
+    bf16), each output code word = the input code word xor the word of two bf16
+    gradients at the same position; bytes past the range stay untouched."""
+    part = 2048 if master == "bf16" else 1024
+    n = part * 37
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    pdt = torch.bfloat16 if master == "bf16" else torch.float32
+    p = torch.empty(n + 64, dtype=pdt, device="cuda")
+    p.copy_(torch.randn(n + 64, generator=gen, device="cuda"))
+    g = torch.randn(n, generator=gen, device="cuda").to(torch.bfloat16)
+    m_in = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+    v_in = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+    m_out = torch.full((n + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    v_out = torch.full((n + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    p0 = p.cpu()
+    pk.fp8adam_stream_mix(p[:n], g, m_in, v_in, m_out[:n], v_out[:n])
+    torch.cuda.synchronize()
+    want_p = (p0[:n].float() + g.cpu().float()).to(pdt)
+    assert torch.equal(p[:n].cpu().view(torch.int16 if master == "bf16" else torch.int32),
+                       want_p.view(torch.int16 if master == "bf16" else torch.int32))
+    assert torch.equal(p[n:].cpu().view(torch.uint8), p0[n:].view(torch.uint8))
+    gw = g.cpu().view(torch.int16).numpy().view(np.uint32)  # two bf16 per word, little-endian
+    cm = m_in.cpu().numpy().view(np.uint32)
+    cv = v_in.cpu().numpy().view(np.uint32)
+    assert np.array_equal(m_out[:n].cpu().numpy().view(np.uint32), cm ^ gw[0::2])
+    assert np.array_equal(v_out[:n].cpu().numpy().view(np.uint32), cv ^ gw[1::2])
+    assert bool((m_out[n:] == 0xA5).all()) and bool((v_out[n:] == 0x5A).all())
