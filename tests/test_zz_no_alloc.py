@@ -155,6 +155,16 @@ def test_noalloc_a_list_whose_chunks_grow_to_fit_the_table():
     torch.cuda.empty_cache()
 
 
+def test_noalloc_at_the_tensor_limit():
+    """FP8ADAM_NOALLOC_MAX_TENSORS (4096) small ragged tensors, some empty: 128
+    set-up launches fill the descriptor table; the same results as a context."""
+    n = pk.NOALLOC_MAX_TENSORS
+    sizes = [(k * 37) % 301 for k in range(n)]  # 0..300 elements, zeros included
+    print(f"noalloc: {n} tensors", flush=True)
+    _run_pair(sizes, "tensor", "pow2", "fp32", "decoupled", "nearest", seed=8, t=2)
+    _run_pair(sizes, "block128", "pow2", "bf16", "decoupled", "stochastic", seed=9, t=5)
+
+
 def test_noalloc_refuses_what_it_cannot_do():
     dev = torch.device("cuda")
     L = _lists([100, 200], "fp32", "tensor", 3, dev)
