@@ -1,8 +1,10 @@
 // fp8adam.hip -- FP8-moment Adam/AdamW step for AMD MI355X (gfx950): the C
 // ABI declared in include/fp8adam.h, the loss-scaling kernels (gradient norm
-// and the scaler's decision), the fresh-state kernel of zero_state, the codec
-// probes and the streaming-copy probe.  The step kernels and their dispatch
-// are in fp8adam_engine.h, instantiated in fp8adam_step_*.hip.
+// and the scaler's decision), the fresh-state kernel of zero_state, the
+// allocation-free step and its file-scope scratch, the codec probes and the
+// bandwidth probes (streaming copy, the update pass's byte mix).  The step
+// kernels and their dispatch are in fp8adam_engine.h, instantiated in
+// fp8adam_step_*.hip.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -820,7 +822,7 @@ int fp8adam_step_noalloc(const fp8adam_tensor* tensors, int32_t n, const fp8adam
     c.d_old_scale = reinterpret_cast<float*>(base + kNaOldScale);
     c.d_flags = reinterpret_cast<int32_t*>(base + kNaFlags);
 
-    SetupBatch b;
+    SetupBatch b{};  // unused slots are zero
     int64_t chunk0 = 0;
     for (int32_t t0 = 0; t0 < n; t0 += kSetupBatch) {
       b.first = t0;

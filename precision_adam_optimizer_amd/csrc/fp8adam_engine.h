@@ -25,8 +25,9 @@
 //                 updates p and records per-part amax partials
 //     k_spec_reduce : per tensor, the true scale; a mispredicted moment is
 //                 flagged
-//     k_fixup   : flagged tensors only: move the codes' exponent fields to the
-//                 true scale, recomputing the few that cannot be moved from
+//     k_fixup   : the chunks of flagged tensors only (a work list that
+//                 k_spec_reduce appends to): move the codes' exponent fields to
+//                 the true scale, recomputing the few that cannot be moved from
 //                 the old codes (still intact in the source buffer)
 //   per-tensor delayed scaling (scale from an amax history)
 //     k_delayed_prepare (scales from the history), k_update<kModeDelayed>,
@@ -42,7 +43,8 @@
 // chunk, an update-pass work-group one part of 2^upd_part_log2 elements, a
 // block-pass work-group one kPart-element part.
 // Loads and stores are dword-granular per lane and contiguous across the wave
-// (fp32 master: 16 B per lane).
+// (fp32 master: 16 B per lane); the amax, update and block passes stream
+// through buffer resources based at each work-group's part.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -98,7 +100,8 @@ using namespace fp8adam;
 #ifndef FP8ADAM_UPDATE_UNROLL
 #define FP8ADAM_UPDATE_UNROLL 1
 #endif
-// 1: non-temporal loads / stores (each byte is touched once per pass)
+// 1: non-temporal global loads of the fix-up and the gradient-norm pass (each
+// byte is touched once per pass)
 #ifndef FP8ADAM_NT_AMAX
 #define FP8ADAM_NT_AMAX 1
 #endif
