@@ -331,6 +331,7 @@ def main():
     opt.set_timing(True)
     evs = []
     requant = []  # per timed step: (element, moment) pairs brought to the true scale by the fix-up
+    probed = []   # per timed step: elements the speculative schedule's scale probe read
     stat_keys = ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite")
     stat_sum = dict.fromkeys(stat_keys, 0)
     wall0 = time.perf_counter()
@@ -345,6 +346,7 @@ def main():
         # read outside the events (this synchronizes the stream between steps)
         st = opt.stats()
         requant.append(sum(x["requantized"] for x in st))
+        probed.append(sum(x["probed"] for x in st))
         if args.collect_stats:
             for k in stat_keys:
                 stat_sum[k] += sum(x[k] for x in st)
@@ -373,7 +375,10 @@ def main():
     #   the dominant pass (algorithmic bytes);
     #   + the amax pass (g, m, v; and p with coupled L2) in the two-pass schedule;
     #   + the per-part amax partials the speculative and delayed passes write and the
-    #     check / commit reads (8 bytes each way per part of 1024 elements, 2048 with bf16);
+    #     check / commit reads (8 bytes each way per part of 1024 elements, 2048 with bf16),
+    #     and in the speculative schedule their per-chunk maxima (8 bytes each way per chunk);
+    #   + the scale probe: g and both codes of the candidate parts it reads (4 bytes per
+    #     element);
     #   + the fix-up: the codes of every mispredicted moment, read and written (2 bytes per
     #     (element, moment) pair; the rare groups it recomputes read 3 bytes more, not counted);
     #   + the gradient-norm pass with loss scaling (g read once).
@@ -383,10 +388,16 @@ def main():
     step_bytes = alg_bytes + (amax_bpp * total if two_pass else 0.0)
     if schedule == "speculative" or scaling == "delayed":
         step_bytes += 16.0 * -(-total // part)
+    if schedule == "speculative":
+        step_bytes += 16.0 * opt.num_chunks
     fix_ms, fix_n = ktimes.get("fixup", (0.0, 0))
     fix_pairs = sum(requant) / max(len(requant), 1)
     fix_bytes = 2.0 * fix_pairs
     step_bytes += fix_bytes
+    probe_ms, probe_n = ktimes.get("spec_probe", (0.0, 0))
+    probe_elems = sum(probed) / max(len(probed), 1)
+    probe_bytes = 4.0 * probe_elems
+    step_bytes += probe_bytes
     if args.amp:
         step_bytes += 2.0 * total
     step_gbps = step_bytes / (ms_per_step / 1e3) / 1e9
@@ -405,6 +416,12 @@ def main():
             "fixup_bytes_per_step": round(fix_bytes),
             "fixup_GBps": round(fix_bytes / (fix_us / 1e6) / 1e9, 1) if fix_us > 0 else None,
             "fixup_pairs_each_step": requant})
+        probe_us = probe_ms / max(probe_n, 1) * 1e3
+        roofline.update({
+            "probe_avg_us": round(probe_us, 2),
+            "probe_elements_per_step": round(probe_elems),
+            "probe_bytes_per_step": round(probe_bytes),
+            "probe_GBps": round(probe_bytes / (probe_us / 1e6) / 1e9, 1) if probe_us > 0 else None})
 
     mix_best, mix_med = mix_bandwidth(stream, w.master)
     copy_gbps = copy_bandwidth(stream)

@@ -66,16 +66,26 @@ typedef enum { FP8ADAM_SCALE_POW2 = 0, FP8ADAM_SCALE_AMAX = 1 } fp8adam_scale_mo
 typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master;
 /* How a per-tensor-scaled step is scheduled on the device.  Both give bit-identical results.
  * TWO_PASS: an amax pass over (g, m, v), then the update pass (18 bytes per fp32 parameter).
- * SPECULATIVE: one update pass that quantizes with a predicted power-of-two scale (the
- *   previous step's amax times its expected growth) and writes the codes into the other of
- *   two code buffers (m/v and m_alt/v_alt, alternating every step); a per-tensor check then
- *   brings only the moments whose true scale differs to it: most codes just have their
- *   exponent field moved (2 bytes per element and moment), the few that cannot be moved
- *   exactly are recomputed from the gradient and the old codes (3 more).  14 bytes per fp32
- *   parameter plus that.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment
- *   is formed after p is overwritten, and coupled L2 would need the old p) and m_alt/v_alt;
- *   steps with t < speculate_from_step run TWO_PASS in place on the current buffer. */
+ * SPECULATIVE: one update pass that quantizes with a predicted power-of-two scale and
+ *   writes the codes into the other of two code buffers (m/v and m_alt/v_alt, alternating
+ *   every step); a per-tensor check then brings only the moments whose true scale differs to
+ *   it: most codes just have their exponent field moved (2 bytes per element and moment), the
+ *   few that cannot be moved exactly are recomputed from the gradient and the old codes (3
+ *   more).  14 bytes per fp32 parameter plus that.  The prediction: a probe before the pass
+ *   computes the exact new amax over the parts of each tensor that held values near its amax
+ *   at the step before (about 1% of the elements, 4 bytes each) and takes its scale; a tensor
+ *   with too many such parts (more than 1/32 of them) takes the previous amax times its
+ *   expected growth.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment is
+ *   formed after p is overwritten, and coupled L2 would need the old p) and m_alt/v_alt.
+ *   Steps with t < speculate_from_step - 1 run TWO_PASS in place on the current buffer; step
+ *   speculate_from_step - 1 runs the amax pass and then the speculative pass with the true
+ *   scales (nothing to fix up; its check lists the probe's first candidates). */
 typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 } fp8adam_schedule;
+/* How the SPECULATIVE schedule predicts a tensor's scale (results are bit-identical either
+ * way; only the share of moments the fix-up moves differs).
+ * PROBE: from the probe's exact amax over the tensor's candidate parts (the default).
+ * GROWTH: always from the previous amax times its expected growth (no probe, no list). */
+typedef enum { FP8ADAM_PREDICT_PROBE = 0, FP8ADAM_PREDICT_GROWTH = 1 } fp8adam_predictor;
 /* How weight_decay enters the step.
  * DECOUPLED (AdamW, the zyxy.net code example): p' = p*(1 - lr*wd) - (Adam update).
  * L2 (Adam on an L2-regularised loss: the training objective in the set-up of Theorem 1,
@@ -124,6 +134,7 @@ typedef struct {
                                   caller's buffers (m, v codes 0; every scale 1.0; the amax
                                   history 0), so they may start with any content; 0: the caller
                                   provides the state (fresh, or restored from a checkpoint) */
+    int32_t predictor;         /* SPECULATIVE: fp8adam_predictor (ignored otherwise) */
 } fp8adam_config;
 
 /* One parameter tensor.  All pointers are device pointers owned by the caller,
@@ -183,6 +194,9 @@ typedef struct {
     int64_t requantized;              /* speculative schedule: (element, moment) pairs brought to the
                                          true scale because the predicted one was off: numel per
                                          mispredicted moment (0, numel or 2 numel); else 0 */
+    int64_t probed;                   /* speculative schedule: elements whose gradient and codes the
+                                         scale probe read before the pass (the parts that held values
+                                         near the tensor's amax at the step before); else 0 */
 } fp8adam_stats_t;
 
 typedef struct fp8adam_ctx fp8adam_ctx;

@@ -34,10 +34,12 @@ SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
 ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
 _ROUNDING = {"nearest": ROUND_NEAREST, "stochastic": ROUND_STOCHASTIC}
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
+PREDICT_PROBE, PREDICT_GROWTH = 0, 1
+_PREDICT = {"probe": PREDICT_PROBE, "growth": PREDICT_GROWTH}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
                 "spec_check", "fixup", "delayed_pass", "delayed_commit", "gradnorm_pass", "amp_decision",
-                "scale_prepare")
+                "scale_prepare", "spec_probe", "part_fold")
 
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
@@ -73,7 +75,7 @@ class ConfigArg(ctypes.Structure):
                 ("decay_mode", ctypes.c_int32), ("scaling", ctypes.c_int32),
                 ("amax_history_len", ctypes.c_int32), ("margin", ctypes.c_int32),
                 ("delayed_from_step", ctypes.c_int32), ("rounding", ctypes.c_int32),
-                ("seed", ctypes.c_uint64), ("zero_state", ctypes.c_int32)]
+                ("seed", ctypes.c_uint64), ("zero_state", ctypes.c_int32), ("predictor", ctypes.c_int32)]
 
 
 class HParamsArg(ctypes.Structure):
@@ -96,7 +98,8 @@ class StatsArg(ctypes.Structure):
                 ("scale_m", ctypes.c_float), ("scale_v", ctypes.c_float),
                 ("underflow_m", ctypes.c_int64), ("underflow_v", ctypes.c_int64),
                 ("saturated_m", ctypes.c_int64), ("saturated_v", ctypes.c_int64),
-                ("nonfinite", ctypes.c_int64), ("requantized", ctypes.c_int64)]
+                ("nonfinite", ctypes.c_int64), ("requantized", ctypes.c_int64),
+                ("probed", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -313,7 +316,10 @@ class FP8AdamW:
     then carries a float32 history of 2 * amax_history_len entries
     (``amax_history``; a fifth ``state`` list supplies it).  ``rounding="stochastic"``
     rounds the moments stochastically with a Philox4x32-10 stream keyed by ``seed``.
-    Every tensor must be
+    ``predictor`` chooses how the speculative schedule predicts each scale:
+    ``"probe"`` (the exact amax over the parts that held the tensor's largest
+    values at the step before) or ``"growth"`` (the previous amax times its
+    expected growth); the results are the same.  Every tensor must be
     contiguous and 16-byte aligned on the same device, and must stay alive with
     the same storage while this object exists.
     """
@@ -321,7 +327,8 @@ class FP8AdamW:
     def __init__(self, params, grads, *, m_format="e4m3", v_format="e5m2", granularity="tensor",
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
                  speculate_from_step=0, decay_mode="decoupled", scaling="just_in_time",
-                 amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0):
+                 amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0,
+                 predictor="probe"):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")
@@ -376,7 +383,7 @@ class FP8AdamW:
                              MASTER_BF16 if master == torch.bfloat16 else MASTER_FP32, int(collect_stats),
                              _SCHED[schedule], int(speculate_from_step), _DECAY[decay_mode],
                              _SCALING[scaling], int(amax_history_len), int(margin), int(delayed_from_step),
-                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, int(fresh))
+                             _ROUNDING[rounding], int(seed) & 0xFFFFFFFFFFFFFFFF, int(fresh), _PREDICT[predictor])
         self.n = len(params)
         self.device = params[0].device
         with torch.cuda.device(self.device):

@@ -379,6 +379,8 @@ int check_config(const fp8adam_config* cfg) {
     return fail(FP8ADAM_EINVAL, "bad decay_mode");
   if (cfg->rounding != FP8ADAM_ROUND_NEAREST && cfg->rounding != FP8ADAM_ROUND_STOCHASTIC)
     return fail(FP8ADAM_EINVAL, "bad rounding");
+  if (cfg->predictor != FP8ADAM_PREDICT_PROBE && cfg->predictor != FP8ADAM_PREDICT_GROWTH)
+    return fail(FP8ADAM_EINVAL, "bad predictor");
   const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
   if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
     return fail(FP8ADAM_EINVAL, "the speculative schedule needs per-tensor POW2 scales");
@@ -434,6 +436,12 @@ void free_ctx(fp8adam_ctx* c) {
   if (c->d_flags) (void)hipFree(c->d_flags);
   if (c->d_fix_count) (void)hipFree(c->d_fix_count);
   if (c->d_fix_list) (void)hipFree(c->d_fix_list);
+  if (c->d_cand_count) (void)hipFree(c->d_cand_count);
+  if (c->d_cand_work) (void)hipFree(c->d_cand_work);
+  if (c->d_cand_n) (void)hipFree(c->d_cand_n);
+  if (c->d_cand_len) (void)hipFree(c->d_cand_len);
+  if (c->d_lb) (void)hipFree(c->d_lb);
+  if (c->d_probed) (void)hipFree(c->d_probed);
   if (c->d_old_scale) (void)hipFree(c->d_old_scale);
   if (c->d_counters) (void)hipFree(c->d_counters);
   if (c->d_gpart) (void)hipFree(c->d_gpart);
@@ -628,6 +636,11 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->hist_len = delayed ? hist_len : 0;
     c->delayed_from = cfg->delayed_from_step > 0 ? cfg->delayed_from_step : 2;
     c->margin_scale = ldexpf(1.0f, delayed ? cfg->margin : 0);
+    // the scale probe's work list: room for cand_cap(its update-pass parts) entries per tensor
+    if (spec && cfg->predictor == FP8ADAM_PREDICT_PROBE) {
+      const int pl = cfg->master == FP8ADAM_MASTER_BF16 ? upd_part_log2<true>() : upd_part_log2<false>();
+      for (int32_t t = 0; t < n; t++) c->ncand_slots += cand_cap((tensors[t].numel + ((int64_t)1 << pl) - 1) >> pl);
+    }
     hipError_t e = hipGetDevice(&c->device);
     const size_t namax = (size_t)n * 4;
     if (e == hipSuccess) e = hipMalloc(&c->d_desc, sizeof(TensorDesc) * 2 * (size_t)n);
@@ -635,6 +648,23 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
     if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_count, sizeof(uint32_t));
     if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_list, sizeof(uint32_t) * (size_t)std::max<int64_t>(1, nchunks));
+    if (spec) {
+      const size_t ns = (size_t)std::max<int64_t>(1, c->ncand_slots);
+      if (e == hipSuccess) e = hipMalloc(&c->d_cand_count, sizeof(uint32_t));
+      if (e == hipSuccess) e = hipMalloc(&c->d_cand_work, sizeof(uint2) * ns);
+      if (e == hipSuccess) e = hipMalloc(&c->d_cand_n, sizeof(int32_t) * (size_t)n);
+      if (e == hipSuccess) e = hipMalloc(&c->d_cand_len, sizeof(int64_t) * (size_t)n);
+      if (e == hipSuccess) e = hipMalloc(&c->d_lb, sizeof(uint32_t) * 2 * (size_t)n);
+      if (e == hipSuccess) e = hipMalloc(&c->d_probed, sizeof(int64_t) * (size_t)n);
+      if (e == hipSuccess) e = hipMemsetAsync(c->d_cand_count, 0, sizeof(uint32_t), stream);
+      // the pass never writes the partials of the parts past a tensor's end: k_part_fold reads them as 0
+      if (e == hipSuccess)
+        e = hipMemsetAsync(c->d_part_amax, 0, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nuparts), stream);
+      if (e == hipSuccess) e = hipMemsetAsync(c->d_cand_n, 0, sizeof(int32_t) * (size_t)n, stream);
+      if (e == hipSuccess) e = hipMemsetAsync(c->d_cand_len, 0, sizeof(int64_t) * (size_t)n, stream);
+      if (e == hipSuccess) e = hipMemsetAsync(c->d_lb, 0, sizeof(uint32_t) * 2 * (size_t)n, stream);
+      if (e == hipSuccess) e = hipMemsetAsync(c->d_probed, 0, sizeof(int64_t) * (size_t)n, stream);
+    }
     if (e == hipSuccess) e = hipMalloc(&c->d_chunk_tid, sizeof(int32_t) * (size_t)std::max<int64_t>(1, nchunks));
     if (e == hipSuccess) e = hipMalloc(&c->d_amax, sizeof(uint32_t) * namax);
     if (e == hipSuccess) e = hipMalloc(&c->d_partial, sizeof(uint2) * (size_t)std::max<int64_t>(1, nchunks));
@@ -852,8 +882,11 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
     std::vector<unsigned long long> cnt((size_t)n * kStatsPerTensor, 0ull);
     std::vector<TensorDesc> desc((size_t)n);
     std::vector<int32_t> flags((size_t)n, 0);
+    std::vector<int64_t> probed((size_t)n, 0);
     const bool block = ctx->cfg.granularity == FP8ADAM_SCALE_BLOCK128;
     HIP_TRY(hipMemcpyAsync(flags.data(), ctx->d_flags, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
+    if (ctx->d_probed && ctx->last_spec)
+      HIP_TRY(hipMemcpyAsync(probed.data(), ctx->d_probed, sizeof(int64_t) * (size_t)n, hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipMemcpyAsync(amax.data(), ctx->d_amax,
                            sizeof(uint32_t) * (size_t)n * (block ? 4 : 2), hipMemcpyDeviceToHost, stream));
     HIP_TRY(hipMemcpyAsync(cnt.data(), ctx->d_counters, sizeof(unsigned long long) * cnt.size(),
@@ -892,6 +925,7 @@ int fp8adam_stats(fp8adam_ctx* ctx, fp8adam_stats_t* out_host, int32_t n, hipStr
       o.saturated_v = (int64_t)cnt[kStatsPerTensor * t + kSatV];
       o.nonfinite = (int64_t)cnt[kStatsPerTensor * t + kNonFinite];
       o.requantized = (int64_t)(((flags[t] & 1) ? 1 : 0) + ((flags[t] & 2) ? 1 : 0)) * desc[t].numel;
+      o.probed = probed[t];
     }
     return 0;
   } catch (...) {

@@ -19,16 +19,23 @@
 //     k_update  : recompute m', v' with the staged old scales; update p;
 //                 requantize m', v' with the new scales and saturation
 //   per-tensor scales, speculative schedule (bit-identical results)
+//     k_spec_probe : the exact amax of m', v' over each tensor's candidate
+//                 parts (those that held values near its amax at the step
+//                 before), a lower bound of the new amax
 //     k_spec_prepare : per tensor, stage the old scales and the predicted ones
+//                 (from the probe's bound, else from the growth model)
 //     k_update<kModeSpec> : one pass that quantizes with a predicted scale,
 //                 writes the codes into the other code buffer (ping-pong),
 //                 updates p and records per-part amax partials
 //     k_spec_reduce : per tensor, the true scale; a mispredicted moment is
-//                 flagged
+//                 flagged; the next step's candidate parts are listed
 //     k_fixup   : the chunks of flagged tensors only (a work list that
 //                 k_spec_reduce appends to): move the codes' exponent fields to
 //                 the true scale, recomputing the few that cannot be moved from
 //                 the old codes (still intact in the source buffer)
+//     the step before the first speculative one: k_amax, k_exact_prepare (the
+//                 true scales as the prediction), then the speculative pass
+//                 and check (which lists the first candidates)
 //   per-tensor delayed scaling (scale from an amax history)
 //     k_delayed_prepare (scales from the history), k_update<kModeDelayed>,
 //     k_delayed_reduce (commit the scales, record this step's amax)
@@ -140,6 +147,21 @@ constexpr int kBlock = 128;                       // block-scale granularity
 constexpr int kBlkJ = FP8ADAM_BLOCK_J;            // a block-pass tile is 8 half-waves x kBlkJ blocks
 constexpr int kReduceThreads = 1024;              // one work-group per tensor in k_reduce
 constexpr int kStatsPerTensor = 5;
+// Speculative schedule, scale probe: a part whose amax of |m'| (or of v') was at
+// least kCandTheta times its tensor's becomes a candidate for the next step; a
+// tensor lists at most cand_cap(its parts) of them, a 2^-kCandShift share but
+// at least kCandMin and at most kCandMax parts (with more, the probe would cost
+// more than the fix-up it saves: the tensor falls back to the growth model).
+constexpr float kCandTheta = 0.8f;
+constexpr int kCandShift = 5;
+constexpr int64_t kCandMin = 8;
+constexpr int64_t kCandMax = 4096;
+__host__ __device__ constexpr int64_t cand_cap(int64_t nparts) {
+  return nparts < kCandMin ? nparts
+                           : (nparts >> kCandShift) < kCandMin ? kCandMin
+                                                               : (nparts >> kCandShift) > kCandMax ? kCandMax
+                                                                                                   : (nparts >> kCandShift);
+}
 
 static_assert(kMaxChunkLog2 >= kMinChunkLog2 && kMinChunkLog2 >= kPartLog2 && kMinChunkLog2 >= kUPartLog2Max,
               "a chunk holds whole parts");
@@ -273,9 +295,10 @@ inline unsigned grid_for(int64_t n) {
 
 constexpr bool kXcdStreams = FP8ADAM_XCD_ORDER != 0;  // update and block passes
 
-// Work-group max of two values; result valid in thread 0.
+// Work-group max of two values over TH threads; result valid in thread 0.
+template <int TH = kThreads>
 __device__ __forceinline__ void block_max2(uint32_t& a, uint32_t& b) {
-  __shared__ uint32_t red[2][kThreads / 64];
+  __shared__ uint32_t red[2][TH / 64];
   a = wave_max(a);
   b = wave_max(b);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -286,7 +309,7 @@ __device__ __forceinline__ void block_max2(uint32_t& a, uint32_t& b) {
   __syncthreads();
   if (threadIdx.x == 0) {
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; w++) {
+    for (int w = 1; w < TH / 64; w++) {
       a = max(a, red[0][w]);
       b = max(b, red[1][w]);
     }
@@ -499,22 +522,15 @@ __device__ __forceinline__ void delayed_scale(const float* h, const StepConsts& 
 
 // ------------------------------------------------------------------ pass 1
 
+// The amax of |m'| and of v' over the elements [start, end) of tensor d (whole
+// groups of 4 through buffer loads, then a ragged tail of < 4 elements at the
+// tensor's end), each lane's share folded into am / av.
 template <int MF, int VF, bool BF16P, bool L2>
-__global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
-                                                   const int32_t* __restrict__ chunk_tid,
-                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2,
-                                                   int64_t nwork, const GradCtl* __restrict__ gctl) {
-  const int64_t w = work_index<false>(nwork);
-  if (w < 0 || amp_apply(gctl, c)) return;
-  const int tid = chunk_tid[w];
-  const TensorDesc d = descs[tid];
-  const int64_t start = (w - d.chunk0) << chunk_log2;
-  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+__device__ __forceinline__ void range_amax(const StepConsts& c, const TensorDesc& d, int64_t start, int64_t end,
+                                           uint32_t& am, uint32_t& av) {
   const int64_t gend = start + ((end - start) & ~(int64_t)3);  // end of whole groups
   const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
   const PartBufs B = part_bufs<BF16P>(d, d.m, d.v, start, end - start);
-  uint32_t am = 0, av = 0;
-
   for (int64_t base = start + kGroup * threadIdx.x; base < gend; base += (int64_t)kSubTile * kAmaxUnroll) {
     Group G[kAmaxUnroll];
 #pragma unroll
@@ -537,7 +553,6 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
       }
     }
   }
-  // ragged tail (< 4 elements at the end of a tensor)
   if (gend + threadIdx.x < end) {
     const int64_t i = gend + threadIdx.x;
     const float g = grad_in<L2>(c, load_g1(d, i), L2 ? load_p1<BF16P>(d, i) : 0.0f);
@@ -546,6 +561,21 @@ __global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict_
     am = max(am, abs_bits(m1));
     av = max(av, abs_bits(v1));
   }
+}
+
+template <int MF, int VF, bool BF16P, bool L2>
+__global__ __launch_bounds__(kThreads) void k_amax(const TensorDesc* __restrict__ descs,
+                                                   const int32_t* __restrict__ chunk_tid,
+                                                   uint2* __restrict__ partial, StepConsts c, int chunk_log2,
+                                                   int64_t nwork, const GradCtl* __restrict__ gctl) {
+  const int64_t w = work_index<false>(nwork);
+  if (w < 0 || amp_apply(gctl, c)) return;
+  const int tid = chunk_tid[w];
+  const TensorDesc d = descs[tid];
+  const int64_t start = (w - d.chunk0) << chunk_log2;
+  const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+  uint32_t am = 0, av = 0;
+  range_amax<MF, VF, BF16P, L2>(c, d, start, end, am, av);
   block_max2(am, av);
   if (threadIdx.x == 0) partial[w] = make_uint2(am, av);
 }
@@ -849,34 +879,219 @@ __global__ __launch_bounds__(kReduceThreads) void k_delayed_reduce(const TensorD
 
 // ------------------------------------------------- speculative: verify, fix up
 //
+// After the speculative pass: the max of the per-part amax partials over each
+// chunk, into chunk_amax (the amax pass's partials buffer, free in a
+// speculative step), so that the check, one work-group per tensor, reads
+// 2^(chunk_log2 - PL) times fewer values.  A chunk's partials are contiguous:
+// L lanes read them 16 bytes (two parts) each and reduce by shuffles, so a
+// wave folds 64 / L chunks.  The partials of parts past a tensor's end are
+// never written by the pass and stay 0 from init.
+template <int PL>
+__global__ __launch_bounds__(kThreads) void k_part_fold(const uint2* __restrict__ part_amax,
+                                                        uint2* __restrict__ chunk_amax, int chunk_log2,
+                                                        int64_t nchunks, StepConsts c,
+                                                        const GradCtl* __restrict__ gctl) {
+  if (amp_apply(gctl, c)) return;  // skipped step: the pass wrote no partials
+  const int split = chunk_log2 - PL;              // parts per chunk: 2^split, 2..32
+  const int lanes = split > 1 ? 1 << (split - 1) : 1;  // lanes per chunk, two parts each
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t chunk = g / lanes;
+  const int sub = (int)(g % lanes);
+  uint32_t am = 0, av = 0;
+  if (chunk < nchunks) {
+    const vu4 two = ld_global<vu4>(part_amax + (chunk << split) + 2 * sub);
+    am = max(two.x, two.z);
+    av = max(two.y, two.w);
+  }
+  for (int o = lanes >> 1; o > 0; o >>= 1) {  // within the chunk's aligned group of lanes
+    am = max(am, (uint32_t)__shfl_xor((int)am, o));
+    av = max(av, (uint32_t)__shfl_xor((int)av, o));
+  }
+  if (chunk < nchunks && sub == 0) chunk_amax[chunk] = make_uint2(am, av);
+}
+
+//
 // One work-group per tensor: the true amax from the per-part partials, the
 // true POW2 scales, and a comparison with the predicted ones.  The old scales
 // are staged for the fix-up, the true scales committed; a flagged tensor's
 // stats counters are cleared (the fix-up recounts them).
 
-// One thread per tensor, before the speculative pass: stage the old scales
-// and the predicted ones in prep[4t..4t+3] = [s_m, s_v, pred s_m, pred s_v]
-// (the pass, the check and the fix-up all read them from there).
+// Speculative schedule, first kernel of the step: the exact amax of |m'| and
+// v' over the candidate parts that the last step's k_spec_reduce listed (the
+// parts that held values near their tensor's amax), atomically maxed into
+// lb[2t], lb[2t+1].  It reads g and the old codes of those parts only (about
+// 1% of the list) and bounds this step's amax from below; k_spec_prepare
+// predicts the scale from it.  The work list holds *cand_count entries
+// (tensor, part index within the tensor), each tensor's entries adjacent.  A
+// work-group takes R consecutive entries per round and issues all their loads
+// before it computes (8 accesses of 1024 elements in flight), and folds its
+// running max into lb only where the tensor changes and at the round's end.
+// PL is the update pass's part size (log2).
+constexpr int kProbeAccesses = 8;
+
+template <int MF, int VF, int PL>
+__global__ __launch_bounds__(kThreads) void k_spec_probe(const TensorDesc* __restrict__ descs, StepConsts c,
+                                                         const uint32_t* __restrict__ cand_count,
+                                                         const uint2* __restrict__ cand_work,
+                                                         uint32_t* __restrict__ lb, const GradCtl* __restrict__ gctl) {
+  constexpr int A = (1 << PL) / kSubTile;  // accesses per entry
+  constexpr int R = kProbeAccesses / A;    // entries per round
+  static_assert(A >= 1 && R >= 1 && (1 << PL) % kSubTile == 0, "whole accesses per part");
+  if (amp_apply(gctl, c)) return;  // skipped step: nothing to predict
+  const int64_t nwork = ld_global<uint32_t>(cand_count);
+  for (int64_t w0 = (int64_t)blockIdx.x * R; w0 < nwork; w0 += (int64_t)gridDim.x * R) {
+    uint2 e[R];
+    Group G[R][A];
+    // every load of the round is issued before any is used: buffer loads bounded
+    // by the part's length (past it they read 0, so no lane branches here)
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      e[u] = w0 + u < nwork ? cand_work[w0 + u] : make_uint2(0xFFFFFFFFu, 0u);
+      if (e[u].x == 0xFFFFFFFFu) continue;  // past the list's end (uniform)
+      const TensorDesc d = descs[e[u].x];
+      const int64_t start = (int64_t)e[u].y << PL;
+      const PartBufs B = part_bufs<false>(d, d.m, d.v, start, min((int64_t)1 << PL, d.numel - start));
+#pragma unroll
+      for (int a = 0; a < A; a++) load_group_buf<false>(B, a * kSubTile + kGroup * threadIdx.x, G[u][a], false);
+    }
+    uint32_t cur = e[0].x, am = 0, av = 0;
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      if (e[u].x == 0xFFFFFFFFu) break;  // past the list's end (uniform)
+      if (e[u].x != cur) {               // uniform: every lane reads the same entries
+        block_max2(am, av);
+        if (threadIdx.x == 0) {
+          atomicMax(lb + 2 * cur, am);
+          atomicMax(lb + 2 * cur + 1, av);
+        }
+        __syncthreads();  // block_max2's LDS is written again
+        cur = e[u].x;
+        am = av = 0;
+      }
+      const TensorDesc d = descs[e[u].x];
+      const float sm = ld_global<float>(d.sm), sv = ld_global<float>(d.sv);
+      const int64_t end = min(((int64_t)e[u].y + 1) << PL, d.numel);
+#pragma unroll
+      for (int a = 0; a < A; a++) {
+        // elements past the part read as zero codes and gradients: m' = v' = 0
+        float m1[4], v1[4];
+        const float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        fresh_moments<MF, VF, false>(c, G[u][a], p, sm, sv, m1, v1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          am = max(am, abs_bits(m1[j]));
+          av = max(av, abs_bits(v1[j]));
+        }
+        // the ragged end of a tensor (< 4 elements, in a group the buffer range cuts)
+        const int64_t i = ((int64_t)e[u].y << PL) + a * kSubTile + kGroup * threadIdx.x;
+        if (i < end && i + kGroup > end) {
+          for (int64_t k = i; k < end; k++) {
+            float m1s, v1s;
+            moment_update(c, load_g1(d, k), decode1<MF>(ld_global<uint8_t>(d.m + k)) * sm,
+                          decode1<VF>(ld_global<uint8_t>(d.v + k)) * sv, m1s, v1s);
+            am = max(am, abs_bits(m1s));
+            av = max(av, abs_bits(v1s));
+          }
+        }
+      }
+    }
+    block_max2(am, av);
+    if (threadIdx.x == 0) {
+      atomicMax(lb + 2 * cur, am);
+      atomicMax(lb + 2 * cur + 1, av);
+    }
+    __syncthreads();  // block_max2's LDS is written again in the next round
+  }
+}
+
+// The POW2 scale of an amax given as fp32 bits (the rule the check applies).
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_bits_of(uint32_t amax_bits) {
+  float s, inv;
+  choose_scale<FMT, 0>(amax_bits, s, inv);
+  return __float_as_uint(s);
+}
+
+// One thread per tensor, after the probe: stage the old scales and the
+// predicted ones in prep[4t..4t+3] = [s_m, s_v, pred s_m, pred s_v] (the pass,
+// the check and the fix-up all read them from there).  A moment predicts from
+// the probe's bound when its tensor listed candidates at the last step and its
+// amax there was nonzero (then the part that held it is among them), else from
+// the last amax times the growth model.  lb is cleared for the next step, and
+// probed[t] records the elements the probe read (for the stats).
 template <int MF, int VF>
 __global__ __launch_bounds__(64) void k_spec_prepare(const TensorDesc* __restrict__ descs,
                                                      const uint32_t* __restrict__ amax, StepConsts c,
                                                      const GradCtl* __restrict__ gctl, float* __restrict__ prep,
-                                                     int32_t n, uint32_t* __restrict__ fix_count) {
+                                                     int32_t n, uint32_t* __restrict__ fix_count,
+                                                     const int32_t* __restrict__ cand_n,
+                                                     const int64_t* __restrict__ cand_len, uint32_t* __restrict__ lb,
+                                                     int64_t* __restrict__ probed, uint32_t* __restrict__ cand_count) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t == 0) st_global<uint32_t>(fix_count, 0u);  // k_spec_reduce appends this step's fix-up work
-  if (t >= n || amp_apply(gctl, c)) return;
+  if (t >= n) return;
+  if (amp_apply(gctl, c)) {  // skipped step: the candidates stay listed for the next one
+    probed[t] = 0;
+    return;
+  }
+  if (t == 0) st_global<uint32_t>(cand_count, 0u);  // the probe has read them; k_spec_reduce lists the next
   const TensorDesc d = descs[t];
+  const uint32_t lbm = lb[2 * t], lbv = lb[2 * t + 1];
+  lb[2 * t] = 0u;
+  lb[2 * t + 1] = 0u;
+  const bool listed = cand_n != nullptr && cand_n[t] > 0;  // null: the growth model only
+  probed[t] = listed ? cand_len[t] : 0;
   if (d.numel == 0) return;
   const float so_m = ld_global<float>(d.sm), so_v = ld_global<float>(d.sv);
   st_global<float>(prep + 4 * t, so_m);
   st_global<float>(prep + 4 * t + 1, so_v);
-  st_global<uint32_t>(prep + 4 * t + 2, predicted_scale_bits<MF>(amax[2 * t], so_m, c.grow_m));
-  st_global<uint32_t>(prep + 4 * t + 3, predicted_scale_bits<VF>(amax[2 * t + 1], so_v, c.grow_v));
+  st_global<uint32_t>(prep + 4 * t + 2, listed && amax[2 * t] != 0u ? scale_bits_of<MF>(lbm)
+                                                                    : predicted_scale_bits<MF>(amax[2 * t], so_m, c.grow_m));
+  st_global<uint32_t>(prep + 4 * t + 3, listed && amax[2 * t + 1] != 0u
+                                            ? scale_bits_of<VF>(lbv)
+                                            : predicted_scale_bits<VF>(amax[2 * t + 1], so_v, c.grow_v));
+}
+
+// The step before the first speculative one runs the amax pass first and then
+// the speculative pass with the true scales as its "prediction", so that its
+// check lists the probe's candidates for the next step and flags nothing.  One
+// work-group per tensor: the amax over the chunk partials of the amax pass,
+// staged in prep as [s_m, s_v, true s_m, true s_v] (the caller's slots still
+// hold the old scales; the check commits the new ones).
+template <int MF, int VF>
+__global__ __launch_bounds__(kReduceThreads) void k_exact_prepare(const TensorDesc* __restrict__ descs,
+                                                                  const uint2* __restrict__ partial, int chunk_log2,
+                                                                  StepConsts c, const GradCtl* __restrict__ gctl,
+                                                                  float* __restrict__ prep,
+                                                                  uint32_t* __restrict__ fix_count,
+                                                                  int64_t* __restrict__ probed,
+                                                                  uint32_t* __restrict__ cand_count) {
+  const int t = blockIdx.x;
+  if (t == 0 && threadIdx.x == 0) st_global<uint32_t>(fix_count, 0u);
+  if (threadIdx.x == 0) probed[t] = 0;
+  if (amp_apply(gctl, c)) return;  // skipped step: the pass carries the codes over, the check keeps the rest
+  if (t == 0 && threadIdx.x == 0) st_global<uint32_t>(cand_count, 0u);
+  const TensorDesc d = descs[t];
+  const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
+  uint32_t am = 0, av = 0;
+  for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) {
+    const uint2 pv = partial[d.chunk0 + k];
+    am = max(am, pv.x);
+    av = max(av, pv.y);
+  }
+  block_max2<kReduceThreads>(am, av);
+  if (threadIdx.x == 0 && d.numel > 0) {
+    st_global<float>(prep + 4 * t, ld_global<float>(d.sm));
+    st_global<float>(prep + 4 * t + 1, ld_global<float>(d.sv));
+    st_global<uint32_t>(prep + 4 * t + 2, scale_bits_of<MF>(am));
+    st_global<uint32_t>(prep + 4 * t + 3, scale_bits_of<VF>(av));
+  }
 }
 
 template <int MF, int VF, bool STATS>
 __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc* __restrict__ descs,
                                                                 const uint2* __restrict__ part_amax,
+                                                                const uint2* __restrict__ chunk_amax,
                                                                 uint32_t* __restrict__ amax,
                                                                 float* __restrict__ old_scale,
                                                                 int32_t* __restrict__ flags,
@@ -884,20 +1099,30 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
                                                                 int chunk_log2, int part_log2, StepConsts c,
                                                                 const GradCtl* __restrict__ gctl,
                                                                 uint32_t* __restrict__ fix_count,
-                                                                uint32_t* __restrict__ fix_list) {
+                                                                uint32_t* __restrict__ fix_list,
+                                                                int32_t* __restrict__ cand_n,
+                                                                int64_t* __restrict__ cand_len,
+                                                                uint32_t* __restrict__ cand_count,
+                                                                uint2* __restrict__ cand_work) {
   const int t = blockIdx.x;
-  if (amp_apply(gctl, c)) {  // skipped step: scales and amax stay, nothing to fix up
+  if (amp_apply(gctl, c)) {  // skipped step: scales, amax and candidates stay, nothing to fix up
     if (threadIdx.x == 0) flags[t] = 0;
     return;
   }
   const TensorDesc d = descs[t];
   const int64_t nparts = (d.numel + ((int64_t)1 << part_log2) - 1) >> part_log2;
   const int64_t part0 = d.chunk0 << (chunk_log2 - part_log2);
+  const int64_t nchunk = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
   uint32_t am = 0, av = 0;
-  parts_max(part_amax + part0, nparts, am, av);
+  parts_max(chunk_amax + d.chunk0, nchunk, am, av);  // k_part_fold's per-chunk maxima
   __shared__ uint32_t red[2][kReduceThreads / 64];
   __shared__ int32_t flag;
   __shared__ uint32_t list_base;
+  __shared__ uint32_t tensor_amax[2];
+  __shared__ uint32_t ncand, nchunks_q, cand_base;
+  __shared__ unsigned long long candlen;
+  __shared__ uint32_t cand_parts[kCandMax];
+  __shared__ uint32_t cand_chunks[kCandMax];
   am = wave_max(am);
   av = wave_max(av);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -925,6 +1150,11 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     }
     amax[2 * t] = am;
     amax[2 * t + 1] = av;
+    tensor_amax[0] = am;
+    tensor_amax[1] = av;
+    ncand = 0u;
+    nchunks_q = 0u;
+    candlen = 0ull;
     flags[t] = f;
     flag = f;
     // room for the tensor's chunks in the fix-up's work list (the order of the
@@ -935,6 +1165,47 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
   if (flag) {
     const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
     for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) fix_list[list_base + k] = (uint32_t)(d.chunk0 + k);
+  }
+  // the next step's probe candidates: the parts within kCandTheta of this
+  // step's amax of either moment (their order in the list does not matter),
+  // found among the parts of the chunks whose maximum qualifies
+  if (cand_work != nullptr) {  // (null: the growth model predicts, nothing to list)
+    const float am_t = __uint_as_float(tensor_amax[0]), av_t = __uint_as_float(tensor_amax[1]);
+    const uint32_t thr_m = tensor_amax[0] != 0u ? __float_as_uint(kCandTheta * am_t) : 0xFFFFFFFFu;
+    const uint32_t thr_v = tensor_amax[1] != 0u ? __float_as_uint(kCandTheta * av_t) : 0xFFFFFFFFu;
+    const int64_t cap = cand_cap(nparts);
+    // a chunk with a candidate part qualifies itself, so more than cap chunks means more than cap parts
+    for (int64_t k = threadIdx.x; k < nchunk; k += kReduceThreads) {
+      const uint2 cv = chunk_amax[d.chunk0 + k];
+      if (cv.x >= thr_m || cv.y >= thr_v) {
+        const uint32_t j = atomicAdd(&nchunks_q, 1u);
+        if (j < cap) cand_chunks[j] = (uint32_t)k;
+      }
+    }
+    __syncthreads();
+    const int split = chunk_log2 - part_log2;
+    const int64_t nitems = nchunks_q <= cap ? (int64_t)nchunks_q << split : 0;
+    for (int64_t j = threadIdx.x; j < nitems; j += kReduceThreads) {
+      const int64_t k = ((int64_t)cand_chunks[j >> split] << split) + (j & ((1 << split) - 1));
+      if (k >= nparts) continue;  // past the tensor's last part
+      const uint2 pv = part_amax[part0 + k];
+      if (pv.x >= thr_m || pv.y >= thr_v) {
+        const uint32_t i = atomicAdd(&ncand, 1u);
+        if (i < cap) cand_parts[i] = (uint32_t)k;
+        atomicAdd(&candlen, (unsigned long long)min((int64_t)1 << part_log2, d.numel - (k << part_log2)));
+      }
+    }
+    __syncthreads();
+    const bool fits = nchunks_q <= cap && ncand > 0u && ncand <= cap;  // uniform
+    if (threadIdx.x == 0) {
+      cand_n[t] = fits ? (int32_t)ncand : 0;
+      cand_len[t] = fits ? (int64_t)candlen : 0;
+      // room in the probe's work list (this step's k_spec_prepare emptied it)
+      cand_base = fits ? atomicAdd(cand_count, ncand) : 0u;
+    }
+    __syncthreads();
+    if (fits)
+      for (uint32_t j = threadIdx.x; j < ncand; j += kReduceThreads) cand_work[cand_base + j] = make_uint2(t, cand_parts[j]);
   }
   if constexpr (STATS) {
     // the fix-up recounts the underflow / saturation counts of a re-quantized moment
@@ -1060,6 +1331,8 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
 #define FP8ADAM_FIX_GROUPS 16384
 #endif
 constexpr int64_t kFixGroups = FP8ADAM_FIX_GROUPS;
+// Work-groups of the scale probe (a fixed grid striding over the list's slots).
+constexpr int64_t kProbeGroups = 8192;
 
 template <int MF, int VF, bool STATS, bool SR>
 __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict__ descs,
@@ -1303,6 +1576,14 @@ struct fp8adam_ctx {
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
   uint32_t* d_fix_count = nullptr;  // speculative: chunks in the fix-up's work list this step
   uint32_t* d_fix_list = nullptr;   // speculative: [<= nchunks] the chunks of the flagged tensors
+  int64_t ncand_slots = 0;          // speculative: room in the probe's work list (the tensors' caps summed)
+  uint32_t* d_cand_count = nullptr; // speculative: entries in the probe's work list
+  uint2* d_cand_work = nullptr;     // speculative: [ncand_slots] (tensor, part index within the tensor)
+  int32_t* d_cand_n = nullptr;      // speculative: [n] parts listed (0: none, the growth model predicts)
+  int64_t* d_cand_len = nullptr;    // speculative: [n] elements in the listed parts
+  uint32_t* d_lb = nullptr;         // speculative: [n][2] the probe's amax over the candidates
+  int64_t* d_probed = nullptr;      // speculative: [n] elements the probe read in the last step
+  bool last_spec = false;           // the last step ran the speculative schedule
   unsigned long long* d_counters = nullptr;  // [n][5]
   double* d_gpart = nullptr;        // loss scaling: [norm groups][2] sum of squares and Inf/NaN count of g
   fp8adam_engine::GradCtl* d_gctl = nullptr;       // loss scaling: the decision of the step in flight
@@ -1368,17 +1649,42 @@ void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
                      c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, nwork, c->gctl);
 }
 
+template <int MF, int VF, bool BF16P>
+void launch_spec_probe(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_spec_probe<MF, VF, upd_part_log2<BF16P>()>),
+                     dim3((unsigned)std::min<int64_t>(c->ncand_slots, kProbeGroups)), dim3(kThreads), 0, s,
+                     descs_of(c, c->cur), k, c->d_cand_count, c->d_cand_work, c->d_lb, c->gctl);
+}
+
 template <int MF, int VF>
 void launch_spec_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_prepare<MF, VF>), dim3((unsigned)((c->n + 63) / 64)), dim3(64), 0, s, descs_of(c, c->cur),
-                     c->d_amax, k, c->gctl, c->d_old_scale, c->n, c->d_fix_count);
+                     c->d_amax, k, c->gctl, c->d_old_scale, c->n, c->d_fix_count,
+                     c->ncand_slots > 0 ? c->d_cand_n : nullptr, c->d_cand_len, c->d_lb, c->d_probed,
+                     c->d_cand_count);
+}
+
+template <int MF, int VF>
+void launch_exact_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  hipLaunchKernelGGL((k_exact_prepare<MF, VF>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s, descs_of(c, c->cur),
+                     c->d_partial, c->chunk_log2, k, c->gctl, c->d_old_scale, c->d_fix_count, c->d_probed,
+                     c->d_cand_count);
+}
+
+template <bool BF16P>
+void launch_part_fold(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
+  const int split = c->chunk_log2 - upd_part_log2<BF16P>();
+  const int64_t lanes = split > 1 ? (int64_t)1 << (split - 1) : 1;
+  hipLaunchKernelGGL((k_part_fold<upd_part_log2<BF16P>()>), dim3((unsigned)((c->nchunks * lanes + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, c->d_part_amax, c->d_partial, c->chunk_log2, c->nchunks, k, c->gctl);
 }
 
 template <int MF, int VF, bool STATS>
 void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_part_amax, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list);
+                     descs_of(c, c->cur), c->d_part_amax, c->d_partial, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
+                     c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list, c->d_cand_n,
+                     c->d_cand_len, c->d_cand_count, c->ncand_slots > 0 ? c->d_cand_work : nullptr);
 }
 
 template <int MF, int VF, bool STATS, bool SR>
@@ -1398,7 +1704,8 @@ void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
 // 4 stats reset, 5 speculative pass, 6 speculative reduce, 7 fix-up,
 // 8 delayed pass, 9 delayed commit, 10 gradient-norm pass, 11 loss-scale decision,
-// 12 scale preparation (speculative / delayed).
+// 12 scale preparation (speculative / delayed), 13 speculative scale probe,
+// 14 speculative per-chunk fold of the part partials.
 #define TIMED(kind, call)                              \
   do {                                                 \
     int slot_;                                         \
@@ -1415,6 +1722,7 @@ inline void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
 int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   bool done = false;
+  c->last_spec = false;
   if (c->cfg.granularity == FP8ADAM_SCALE_BLOCK128) {
     if (STATS) TIMED(4, launch_reset(c, 4 * (int64_t)c->n, s));
     if (c->nchunks > 0) TIMED(3, (launch_block<MF, VF, BF16P, STATS, SMODE, L2, SR>(c, k, s)));
@@ -1423,13 +1731,23 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
   // (fp8adam_init refuses the speculative schedule with coupled L2 or AMAX scales:
   // the fix-up recomputes moments after p has been overwritten, and g_eff needs the old p)
   if constexpr (!L2 && SMODE == 0) {
-    if (!done && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from) {
+    // the step before the first speculative one: the amax pass, then the speculative
+    // pass with the true scales (its check lists the probe's first candidates)
+    if (!done && c->cfg.schedule == FP8ADAM_SCHEDULE_SPECULATIVE && t >= c->speculate_from - 1) {
       if (STATS) TIMED(4, launch_reset(c, 0, s));
-      TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
+      if (t < c->speculate_from) {
+        if (c->nchunks > 0) TIMED(0, (launch_amax<MF, VF, BF16P, false>(c, k, s)));
+        TIMED(2, (launch_exact_prepare<MF, VF>(c, k, s)));
+      } else {
+        if (c->ncand_slots > 0) TIMED(13, (launch_spec_probe<MF, VF, BF16P>(c, k, s)));
+        TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
+      }
       if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
+      if (c->nchunks > 0) TIMED(14, (launch_part_fold<BF16P>(c, k, s)));
       TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, upd_part_log2<BF16P>(), s)));
       if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
       c->cur = 1 - c->cur;
+      c->last_spec = true;
       done = true;
     }
   }

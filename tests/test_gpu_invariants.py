@@ -90,16 +90,19 @@ def test_resume_is_bit_exact():
     _same(ref, out)
 
 
-@pytest.mark.parametrize("granularity,schedule", [("tensor", "two_pass"), ("block128", "two_pass"),
-                                                  ("tensor", "speculative")])
+@pytest.mark.parametrize("granularity,schedule,predictor", [("tensor", "two_pass", None), ("block128", "two_pass", None),
+                                                            ("tensor", "speculative", "growth"),
+                                                            ("tensor", "speculative", "probe")])
 @pytest.mark.parametrize("master", [torch.float32, torch.bfloat16])
-def test_guard_bands_untouched(granularity, schedule, master):
+def test_guard_bands_untouched(granularity, schedule, predictor, master):
     """Every buffer is a view into a larger allocation whose bytes after the
     tensor (up to the next 16-byte boundary and 64 bytes more) hold a canary;
     ragged sizes must not write past their end.  Under the speculative
-    schedule the second code buffers are guarded too, and the fix-up (16 codes
-    per lane, then groups of 4, then single codes at a tensor's end) runs
-    whenever a tensor's scale moves between steps."""
+    schedule the second code buffers are guarded too; with the growth model's
+    predictions the fix-up (16 codes per lane, then groups of 4, then single
+    codes at a tensor's end) runs whenever a tensor's scale moves between
+    steps, and with the probe's the probe reads the candidate parts, ragged
+    last parts included."""
     sizes = [1, 3, 129, 1025, 16387]
     pad = 128
     canary = 0x5A
@@ -132,7 +135,7 @@ def test_guard_bands_untouched(granularity, schedule, master):
         torch.empty_like = lambda x, *a, **k: next(alts)
         try:
             opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=True, state=(m, v, ms, vs),
-                              schedule="speculative", speculate_from_step=2)
+                              schedule="speculative", speculate_from_step=2, predictor=predictor)
         finally:
             torch.empty_like = orig
     else:
@@ -145,7 +148,7 @@ def test_guard_bands_untouched(granularity, schedule, master):
         requantized += sum(s["requantized"] for s in opt.stats())
     torch.cuda.synchronize()
     opt.close()
-    if schedule == "speculative":
+    if predictor == "growth":
         assert requantized > 0  # the fix-up ran
     for raw, nbytes in bufs:
         tail = raw[nbytes:].cpu().numpy()

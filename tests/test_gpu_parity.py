@@ -44,7 +44,7 @@ def _compare_stats(name, got: dict, want: dict, granularity: str):
 
 def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init, sizes=SIZES, steps=3,
               lr=3e-4, seed=0, schedule="two_pass", speculate_from_step=0, decay_mode="decoupled", wd=0.1,
-              rounding="nearest", rng_seed=0):
+              rounding="nearest", rng_seed=0, predictor="probe"):
     m_fmt, v_fmt = fmts
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
@@ -70,7 +70,7 @@ def run_small(fmts, granularity, scale_mode, master, collect_stats, random_init,
     opt = pk.FP8AdamW(params, grads, m_format=m_fmt, v_format=v_fmt, granularity=granularity,
                       scale_mode=scale_mode, collect_stats=collect_stats, state=state, schedule=schedule,
                       speculate_from_step=speculate_from_step, decay_mode=decay_mode, rounding=rounding,
-                      seed=rng_seed)
+                      seed=rng_seed, predictor=predictor)
     requantized = 0
     try:
         for t in range(1, steps + 1):
