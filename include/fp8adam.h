@@ -71,21 +71,27 @@ typedef enum { FP8ADAM_MASTER_FP32 = 0, FP8ADAM_MASTER_BF16 = 1 } fp8adam_master
  *   every step); a per-tensor check then brings only the moments whose true scale differs to
  *   it: most codes just have their exponent field moved (2 bytes per element and moment), the
  *   few that cannot be moved exactly are recomputed from the gradient and the old codes (3
- *   more).  14 bytes per fp32 parameter plus that.  The prediction: a probe before the pass
- *   computes the exact new amax over the parts of each tensor that held values near its amax
- *   at the step before (about 1% of the elements, 4 bytes each) and takes its scale; a tensor
- *   with too many such parts (more than 1/32 of them) takes the previous amax times its
- *   expected growth.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment is
+ *   more).  14 bytes per fp32 parameter plus that.  The prediction (see fp8adam_predictor): a
+ *   probe before the pass computes the exact new amax over the parts of each tensor that held
+ *   values near its amax at the step before (about 1% of the elements, 4 bytes each) and takes
+ *   its scale; a tensor with too many such parts (more than 1/32 of them) takes the previous
+ *   amax times its expected growth.  Needs per-tensor POW2 scales, decoupled decay (a recomputed moment is
  *   formed after p is overwritten, and coupled L2 would need the old p) and m_alt/v_alt.
  *   Steps with t < speculate_from_step - 1 run TWO_PASS in place on the current buffer; step
  *   speculate_from_step - 1 runs the amax pass and then the speculative pass with the true
  *   scales (nothing to fix up; its check lists the probe's first candidates). */
 typedef enum { FP8ADAM_SCHEDULE_TWO_PASS = 0, FP8ADAM_SCHEDULE_SPECULATIVE = 1 } fp8adam_schedule;
-/* How the SPECULATIVE schedule predicts a tensor's scale (results are bit-identical either
- * way; only the share of moments the fix-up moves differs).
- * PROBE: from the probe's exact amax over the tensor's candidate parts (the default).
+/* How the SPECULATIVE schedule predicts a tensor's scale (results are bit-identical every
+ * way; only the share of moments the fix-up moves, and the time, differ).
+ * AUTO (the default): PROBE for a list of at least 2^28 elements, GROWTH for a smaller one
+ *   (whose step is short enough that the probe's two extra launches cost more than they save).
+ * PROBE: from the probe's exact amax over the tensor's candidate parts.
  * GROWTH: always from the previous amax times its expected growth (no probe, no list). */
-typedef enum { FP8ADAM_PREDICT_PROBE = 0, FP8ADAM_PREDICT_GROWTH = 1 } fp8adam_predictor;
+typedef enum {
+    FP8ADAM_PREDICT_AUTO = 0,
+    FP8ADAM_PREDICT_PROBE = 1,
+    FP8ADAM_PREDICT_GROWTH = 2
+} fp8adam_predictor;
 /* How weight_decay enters the step.
  * DECOUPLED (AdamW, the zyxy.net code example): p' = p*(1 - lr*wd) - (Adam update).
  * L2 (Adam on an L2-regularised loss: the training objective in the set-up of Theorem 1,

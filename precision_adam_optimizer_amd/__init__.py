@@ -34,8 +34,8 @@ SCALING_JUST_IN_TIME, SCALING_DELAYED = 0, 1
 ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
 _ROUNDING = {"nearest": ROUND_NEAREST, "stochastic": ROUND_STOCHASTIC}
 _SCALING = {"just_in_time": SCALING_JUST_IN_TIME, "delayed": SCALING_DELAYED}
-PREDICT_PROBE, PREDICT_GROWTH = 0, 1
-_PREDICT = {"probe": PREDICT_PROBE, "growth": PREDICT_GROWTH}
+PREDICT_AUTO, PREDICT_PROBE, PREDICT_GROWTH = 0, 1, 2
+_PREDICT = {"auto": PREDICT_AUTO, "probe": PREDICT_PROBE, "growth": PREDICT_GROWTH}
 
 KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "stats_reset", "spec_pass",
                 "spec_check", "fixup", "delayed_pass", "delayed_commit", "gradnorm_pass", "amp_decision",
@@ -318,8 +318,9 @@ class FP8AdamW:
     rounds the moments stochastically with a Philox4x32-10 stream keyed by ``seed``.
     ``predictor`` chooses how the speculative schedule predicts each scale:
     ``"probe"`` (the exact amax over the parts that held the tensor's largest
-    values at the step before) or ``"growth"`` (the previous amax times its
-    expected growth); the results are the same.  Every tensor must be
+    values at the step before), ``"growth"`` (the previous amax times its
+    expected growth) or ``"auto"`` (the probe for lists of at least 2^28
+    elements); the results are the same.  Every tensor must be
     contiguous and 16-byte aligned on the same device, and must stay alive with
     the same storage while this object exists.
     """
@@ -328,7 +329,7 @@ class FP8AdamW:
                  scale_mode="pow2", collect_stats=False, state=None, schedule="two_pass",
                  speculate_from_step=0, decay_mode="decoupled", scaling="just_in_time",
                  amax_history_len=16, margin=0, delayed_from_step=0, rounding="nearest", seed=0,
-                 predictor="probe"):
+                 predictor="auto"):
         params, grads = list(params), list(grads)
         if len(params) != len(grads) or not params:
             raise ValueError("need one gradient per parameter and at least one parameter")

@@ -379,7 +379,8 @@ int check_config(const fp8adam_config* cfg) {
     return fail(FP8ADAM_EINVAL, "bad decay_mode");
   if (cfg->rounding != FP8ADAM_ROUND_NEAREST && cfg->rounding != FP8ADAM_ROUND_STOCHASTIC)
     return fail(FP8ADAM_EINVAL, "bad rounding");
-  if (cfg->predictor != FP8ADAM_PREDICT_PROBE && cfg->predictor != FP8ADAM_PREDICT_GROWTH)
+  if (cfg->predictor != FP8ADAM_PREDICT_AUTO && cfg->predictor != FP8ADAM_PREDICT_PROBE &&
+      cfg->predictor != FP8ADAM_PREDICT_GROWTH)
     return fail(FP8ADAM_EINVAL, "bad predictor");
   const bool spec = cfg->schedule == FP8ADAM_SCHEDULE_SPECULATIVE;
   if (spec && (cfg->granularity != FP8ADAM_SCALE_TENSOR || cfg->scale_mode != FP8ADAM_SCALE_POW2))
@@ -637,7 +638,11 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     c->delayed_from = cfg->delayed_from_step > 0 ? cfg->delayed_from_step : 2;
     c->margin_scale = ldexpf(1.0f, delayed ? cfg->margin : 0);
     // the scale probe's work list: room for cand_cap(its update-pass parts) entries per tensor
-    if (spec && cfg->predictor == FP8ADAM_PREDICT_PROBE) {
+    // AUTO: the probe on lists of at least kProbeMinElements (its two launches and the fold
+    // cost about 15-20 us a step, more than the fix-up it saves on a short step)
+    const bool probe = cfg->predictor == FP8ADAM_PREDICT_PROBE ||
+                       (cfg->predictor == FP8ADAM_PREDICT_AUTO && total >= kProbeMinElements);
+    if (spec && probe) {
       const int pl = cfg->master == FP8ADAM_MASTER_BF16 ? upd_part_log2<true>() : upd_part_log2<false>();
       for (int32_t t = 0; t < n; t++) c->ncand_slots += cand_cap((tensors[t].numel + ((int64_t)1 << pl) - 1) >> pl);
     }

@@ -156,6 +156,7 @@ constexpr float kCandTheta = 0.8f;
 constexpr int kCandShift = 5;
 constexpr int64_t kCandMin = 8;
 constexpr int64_t kCandMax = 4096;
+constexpr int64_t kProbeMinElements = (int64_t)1 << 28;  // FP8ADAM_PREDICT_AUTO's threshold
 __host__ __device__ constexpr int64_t cand_cap(int64_t nparts) {
   return nparts < kCandMin ? nparts
                            : (nparts >> kCandShift) < kCandMin ? kCandMin
@@ -1114,7 +1115,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
   const int64_t part0 = d.chunk0 << (chunk_log2 - part_log2);
   const int64_t nchunk = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
   uint32_t am = 0, av = 0;
-  parts_max(chunk_amax + d.chunk0, nchunk, am, av);  // k_part_fold's per-chunk maxima
+  if (chunk_amax != nullptr) parts_max(chunk_amax + d.chunk0, nchunk, am, av);  // k_part_fold's per-chunk maxima
+  else parts_max(part_amax + part0, nparts, am, av);                            // (growth model: no fold)
   __shared__ uint32_t red[2][kReduceThreads / 64];
   __shared__ int32_t flag;
   __shared__ uint32_t list_base;
@@ -1169,7 +1171,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
   // the next step's probe candidates: the parts within kCandTheta of this
   // step's amax of either moment (their order in the list does not matter),
   // found among the parts of the chunks whose maximum qualifies
-  if (cand_work != nullptr) {  // (null: the growth model predicts, nothing to list)
+  if (cand_work != nullptr) {  // (null: the growth model predicts, nothing to list; else chunk_amax is set)
     const float am_t = __uint_as_float(tensor_amax[0]), av_t = __uint_as_float(tensor_amax[1]);
     const uint32_t thr_m = tensor_amax[0] != 0u ? __float_as_uint(kCandTheta * am_t) : 0xFFFFFFFFu;
     const uint32_t thr_v = tensor_amax[1] != 0u ? __float_as_uint(kCandTheta * av_t) : 0xFFFFFFFFu;
@@ -1682,7 +1684,7 @@ void launch_part_fold(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
 template <int MF, int VF, bool STATS>
 void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
   hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_part_amax, c->d_partial, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
+                     descs_of(c, c->cur), c->d_part_amax, c->ncand_slots > 0 ? c->d_partial : nullptr, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
                      c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list, c->d_cand_n,
                      c->d_cand_len, c->d_cand_count, c->ncand_slots > 0 ? c->d_cand_work : nullptr);
 }
@@ -1743,7 +1745,7 @@ int run_step_t(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
         TIMED(12, (launch_spec_prepare<MF, VF>(c, k, s)));
       }
       if (c->nchunks > 0) TIMED(5, (launch_update<MF, VF, BF16P, STATS, SMODE, kModeSpec, false, SR>(c, k, s)));
-      if (c->nchunks > 0) TIMED(14, (launch_part_fold<BF16P>(c, k, s)));
+      if (c->nchunks > 0 && c->ncand_slots > 0) TIMED(14, (launch_part_fold<BF16P>(c, k, s)));
       TIMED(6, (launch_spec_reduce<MF, VF, STATS>(c, k, upd_part_log2<BF16P>(), s)));
       if (c->nchunks > 0) TIMED(7, (launch_fixup<MF, VF, STATS, SR>(c, k, s)));
       c->cur = 1 - c->cur;

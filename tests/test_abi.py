@@ -61,7 +61,7 @@ def test_error_paths_without_a_gpu():
     bad = pk.ConfigArg(7, 1, 0, 0, 0, 0)
     assert L.fp8adam_init(ctypes.byref(h), arr, 1, ctypes.byref(bad), None) == -1
     bad = pk.ConfigArg(0, 1, 0, 0, 0, 0, pk.SCHEDULE_SPECULATIVE, 0)
-    bad.predictor = 2
+    bad.predictor = 3
     assert L.fp8adam_init(ctypes.byref(h), arr, 1, ctypes.byref(bad), None) == -1
     assert "predictor" in pk.fp8adam_last_error()
     arr2 = (pk.TensorArg * 1)(pk.TensorArg(16 + 4, 32, 48, 64, 80, 96, 10))

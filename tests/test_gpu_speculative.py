@@ -268,7 +268,7 @@ def test_scale_probe_lists_candidates_and_cuts_mispredictions():
     params = [torch.randn(n, generator=gen, device=dev) * 0.02 for n in sizes]
     grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in sizes]
     scales = [10.0 ** float(-6.0 + 5.0 * torch.rand(1, generator=gen, device=dev)) for _ in sizes]
-    opt = pk.FP8AdamW(params, grads, schedule="speculative", speculate_from_step=4)
+    opt = pk.FP8AdamW(params, grads, schedule="speculative", speculate_from_step=4, predictor="probe")
     moved = pairs = 0
     listed = big = 0
     try:
