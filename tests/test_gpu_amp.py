@@ -34,7 +34,7 @@ def check_amp_state(name, got: dict, want: oracle.AmpState):
 
 def run_amp(sizes, *, schedule="two_pass", granularity="tensor", scaling="just_in_time", decay_mode="decoupled",
             master="fp32", max_norm=1.0, init_scale=2.0 ** 16, overflow_at=(3,), calls=7, growth_interval=3,
-            seed=0, stats=True, speculate_from_step=2, rounding="nearest", rng_seed=0):
+            seed=0, stats=True, speculate_from_step=2, rounding="nearest", rng_seed=0, predictor="auto"):
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -48,7 +48,7 @@ def run_amp(sizes, *, schedule="two_pass", granularity="tensor", scaling="just_i
     H = 4
     opt = pk.FP8AdamW(params, grads, granularity=granularity, collect_stats=stats, state=state, schedule=schedule,
                       speculate_from_step=speculate_from_step, decay_mode=decay_mode, scaling=scaling,
-                      amax_history_len=H, rounding=rounding, seed=rng_seed)
+                      amax_history_len=H, rounding=rounding, seed=rng_seed, predictor=predictor)
     delayed = scaling == "delayed"
     host = [OracleState(np_host(params[i]), np_host(state[0][i]), np_host(state[1][i]), np_host(state[2][i]),
                         np_host(state[3][i]), np_host(opt.amax_history[i]) if delayed else None)
@@ -136,6 +136,25 @@ def test_small_amp_overflow_first_call_and_growth():
                          seed=431, speculate_from_step=2)
     assert skipped == 2
     run_amp(SIZES[:12], scaling="delayed", overflow_at=(1,), calls=5, growth_interval=2, seed=432)
+
+
+@pytest.mark.parametrize("master", ["fp32", "bf16"])
+def test_small_amp_speculative_with_the_scale_probe(master):
+    """The speculative schedule predicting from the scale probe through two
+    skipped calls: a skipped step neither probes nor lists, and the next taken
+    step probes the candidates listed before the skip."""
+    skipped, clipped = run_amp(SIZES, schedule="speculative", master=master, seed=470 + (master == "bf16"),
+                               overflow_at=(3, 6), predictor="probe")
+    assert skipped == 2 and clipped > 0
+
+
+def test_small_amp_overflow_first_call_with_the_scale_probe():
+    """An overflow at call 1, the exact-scale step that would list the probe's
+    first candidates: the first speculative step has none and takes the growth
+    model, the later ones the probe."""
+    skipped, _ = run_amp(SIZES[:12], schedule="speculative", overflow_at=(1, 5), calls=8, growth_interval=2,
+                         seed=433, speculate_from_step=2, predictor="probe")
+    assert skipped == 2
 
 
 @pytest.mark.timeout(900)

@@ -183,3 +183,44 @@ def test_noalloc_refuses_what_it_cannot_do():
     # nothing was enqueued: the state is untouched
     torch.cuda.synchronize()
     assert torch.equal(L["p"][0], _lists([100, 200], "fp32", "tensor", 3, dev)["p"][0])
+
+
+@pytest.mark.parametrize("granularity", ["tensor", "block128"])
+def test_noalloc_step_replayed_from_a_graph(granularity):
+    """The allocation-free step captured in a HIP graph (through torch's graph
+    capture) and replayed three times, with eager work and synchronizations
+    between the replays: after every replay the state equals, bit for bit, the
+    one that as many eager calls of the same step reach.  (The captured kernels
+    use no memset nodes; the scratch array's address is set up by an eager call
+    before the capture.)"""
+    dev = torch.device("cuda")
+    sizes = SMALL + [300_001]
+    A = _lists(sizes, "fp32", granularity, 91, dev)
+    B = _clone(A)
+    W = _clone(A)
+    cfg = _config(granularity, "pow2", "fp32", "decoupled", "nearest")
+    hp = pk.HParamsArg(3e-4, 0.9, 0.95, 1e-8, 0.1, 5)
+    args_a = _args(A)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pk.fp8adam_step_noalloc(_args(W), cfg, hp)  # an eager call first (sets up this device's scratch)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pk.fp8adam_step_noalloc(args_a, cfg, hp)
+    torch.cuda.synchronize()
+    for k in A:  # capture records the launches without running them
+        for x, y in zip(A[k], B[k]):
+            assert torch.equal(_bits(x), _bits(y)), f"capture changed {k}"
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        pk.fp8adam_step_noalloc(_args(B), cfg, hp)
+        torch.cuda.synchronize()
+        _ = float(torch.randn(1 << 20, device=dev).abs().sum())  # eager work between the replays
+        for k in A:
+            for i, (x, y) in enumerate(zip(A[k], B[k])):
+                assert torch.equal(_bits(x), _bits(y)), f"replay {r + 1}: {k} of tensor {i} (numel {sizes[i]})"
+    del g
+    torch.cuda.synchronize()
