@@ -147,7 +147,11 @@ __device__ __forceinline__ uint32_t encode4_sr(float a, float b, float c, float 
 // as 1, 2, 3", SC 2011): ten rounds of two 32x32->64-bit multiplies; the key
 // is bumped by the two Weyl constants between rounds.  Each round's two
 // three-way XORs are single gfx950 v_bitop3_b32 instructions (truth table 0x96),
-// which the compiler otherwise splits into two XORs each.
+// which the compiler otherwise splits into two XORs each.  The key (uniform,
+// in scalar registers) is bumped in place behind an empty asm statement each
+// round: left to itself the compiler computed all twenty round keys up front
+// and, short of scalar registers at eight waves per SIMD, spilled them to
+// vector lanes and read them back in the rounds.
 __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
@@ -166,6 +170,7 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
     c2 = n2;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
+    asm volatile("" : "+s"(k0), "+s"(k1));  // emits nothing; keeps the schedule sequential
   }
   out[0] = c0;
   out[1] = c1;

@@ -241,13 +241,23 @@ __device__ __forceinline__ uint32_t quant4(const float (&q)[4], const uint32_t (
   }
 }
 
-// One value, element i of tensor tid (the ragged tails).
-template <int FMT, bool SR, bool HIGH>
-__device__ __forceinline__ uint32_t quant1(const StepConsts& c, int tid, int64_t i, float q) {
+// The random word of element i of tensor tid alone (the ragged tails; 0 when
+// rounding to nearest).
+template <bool SR>
+__device__ __forceinline__ uint32_t sr_word1(const StepConsts& c, int tid, int64_t i) {
   if constexpr (SR) {
     uint32_t rw[4];
     sr_words<true>(c, tid, i & ~(int64_t)3, rw);
-    const uint32_t w = rw[i & 3];
+    return rw[i & 3];
+  } else {
+    return 0u;
+  }
+}
+
+// One value with its element's random word w (the ragged tails).
+template <int FMT, bool SR, bool HIGH>
+__device__ __forceinline__ uint32_t quant1(uint32_t w, float q) {
+  if constexpr (SR) {
     const uint32_t r[4] = {HIGH ? w >> 16 : w & 0xFFFFu, 0u, 0u, 0u};
     return encode4_sr<FMT>(q, 0.0f, 0.0f, 0.0f, r) & 0xFFu;
   } else {
@@ -257,16 +267,36 @@ __device__ __forceinline__ uint32_t quant1(const StepConsts& c, int tid, int64_t
 
 enum Counter { kUnderM = 0, kUnderV = 1, kSatM = 2, kSatV = 3, kNonFinite = 4 };
 
+// Wave-wide max / sum, returned to every lane (called with the whole wave
+// active): an inclusive scan by DPP moves -- row_shr 1, 2, 4, 8 within each
+// row of 16 lanes, then row_bcast 15 and 31 carry a row's last lane into the
+// next rows -- leaves the total in lane 63, which readlane broadcasts.  A lane
+// with no source in a step reads 0, the identity of both.  Six VALU
+// instructions with fused DPP operands, against about thirty for a butterfly
+// of ds_bpermute shuffles.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  x = max(x, dpp_move<0x111>(x));       // row_shr:1
+  x = max(x, dpp_move<0x112>(x));       // row_shr:2
+  x = max(x, dpp_move<0x114>(x));       // row_shr:4
+  x = max(x, dpp_move<0x118>(x));       // row_shr:8
+  x = max(x, dpp_move<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
+  x = max(x, dpp_move<0x143, 0xC>(x));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
-  return x;
+  x += dpp_move<0x111>(x);
+  x += dpp_move<0x112>(x);
+  x += dpp_move<0x114>(x);
+  x += dpp_move<0x118>(x);
+  x += dpp_move<0x142, 0xA>(x);
+  x += dpp_move<0x143, 0xC>(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // Logical work item (chunk or part) of this work-group.  Work-groups are
@@ -766,7 +796,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     moment_update(c, g, decode1<MF>(ld_global<uint8_t>(d.m + i)) * sm, decode1<VF>(ld_global<uint8_t>(d.v + i)) * sv, m1, v1);
     const float p = param_update(c, p0, m1, v1);
     const float qm = m1 * ism, qv = v1 * isv;
-    const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm), cv = quant1<VF, SR, true>(c, tid, i, qv);
+    const uint32_t w = sr_word1<SR>(c, tid, i);
+    const uint32_t cm = quant1<MF, SR, false>(w, qm), cv = quant1<VF, SR, true>(w, qv);
     count_element<MF, VF, STATS>(cnt, m1, v1, qm, qv, cm, cv);
     if constexpr (PARTS) {
       am = max(am, abs_bits(m1));
@@ -1312,7 +1343,7 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
     moment_update(c, g, x0, x0, m1, v1);
     const float x = IS_V ? v1 : m1;
     const float q = x * inv_new;
-    const uint32_t code = quant1<FMT, SR, IS_V>(c, tid, i, q);
+    const uint32_t code = quant1<FMT, SR, IS_V>(sr_word1<SR>(c, tid, i), q);
     if constexpr (STATS) {
       under += (x != 0.0f && (code & 0x7Fu) == 0u);
       sat += (fabsf(q) > Format<FMT>::kMax);
@@ -1506,7 +1537,8 @@ __global__ __launch_bounds__(kThreads) void k_block(const TensorDesc* __restrict
         for (int r = 0; r < 4; r++) {
           const int64_t i = i0 + r;
           if (i < end) {
-            const uint32_t cm = quant1<MF, SR, false>(c, tid, i, qm[r]), cv = quant1<VF, SR, true>(c, tid, i, qv[r]);
+            const uint32_t w = sr_word1<SR>(c, tid, i);
+            const uint32_t cm = quant1<MF, SR, false>(w, qm[r]), cv = quant1<VF, SR, true>(w, qv[r]);
             count_element<MF, VF, STATS>(cnt, m1[r], v1[r], qm[r], qv[r], cm, cv);
             store_p1<BF16P>(d, i, p[r]);
             st_global<uint8_t>(d.m + i, (uint8_t)cm);
