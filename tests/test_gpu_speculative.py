@@ -83,7 +83,9 @@ def test_speculative_equals_two_pass_bitwise(master, predictor):
                       "saturated_v", "nonfinite"):
                 assert np.float64(sa[k]) == np.float64(sb[k]) or (np.isnan(sa[k]) and np.isnan(sb[k])), \
                     f"step {t} tensor {i}: stat {k} {sa[k]} vs {sb[k]}"
-            assert sa["requantized"] == 0
+            assert sa["requantized"] == 0 and sa["probed"] == 0
+        if predictor == "growth":
+            assert all(sb["probed"] == 0 for sb in y[5])  # no probe runs
         rq = sum(s["requantized"] for s in y[5])
         if t >= 2:
             requant_steps += rq > 0
@@ -134,15 +136,20 @@ def test_speculative_vs_oracle_ragged(combo, predictor):
     assert rq > 0 or predictor == "probe"
 
 
-def test_speculative_resume_is_bit_exact():
+@pytest.mark.parametrize("predictor", PREDICTORS)
+def test_speculative_resume_is_bit_exact(predictor):
+    """A context rebuilt from the state after step 4 (no probe candidates yet,
+    so its first speculative step predicts from the growth model) continues
+    bit for bit like the uninterrupted run."""
     sizes = [50_001, 4096, 3]
-    ref = _run("speculative", sizes, 7, seed=5)
+    ref = _run("speculative", sizes, 7, seed=5, predictor=predictor)
     dev = torch.device("cuda")
     gen = torch.Generator(device=dev)
     gen.manual_seed(5)
     params = [torch.randn(n, generator=gen, device=dev) * 0.02 for n in sizes]
     grads = [torch.empty(n, dtype=torch.bfloat16, device=dev) for n in sizes]
-    opt = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2)
+    opt = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2,
+                      predictor=predictor)
     for t in range(1, 5):
         for i, n in enumerate(sizes):
             grads[i].copy_(drifting_grad(n, 5, t, i, dev))
@@ -151,7 +158,8 @@ def test_speculative_resume_is_bit_exact():
     state = ([m.clone() for m in opt.m], [v.clone() for v in opt.v], [s.clone() for s in opt.m_scale],
              [s.clone() for s in opt.v_scale])
     opt.close()
-    opt2 = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2, state=state)
+    opt2 = pk.FP8AdamW(params, grads, collect_stats=True, schedule="speculative", speculate_from_step=2, state=state,
+                       predictor=predictor)
     for t in range(5, 8):
         for i, n in enumerate(sizes):
             grads[i].copy_(drifting_grad(n, 5, t, i, dev))
