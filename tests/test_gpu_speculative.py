@@ -304,3 +304,45 @@ def test_scale_probe_lists_candidates_and_cuts_mispredictions():
         opt.close()
         del params, grads
         torch.cuda.empty_cache()
+
+
+def _edge_grad(n, seed, t, i, dev):
+    """Gradients that exercise the probe's candidate list: tensor 0 constant
+    (every part equal: more candidates than the cap, the growth model
+    predicts), tensor 1 zero (amax 0: no candidates), tensor 2 one spike that
+    moves every step (one candidate part, never the new maximum's), the rest
+    drifting noise."""
+    if i == 0:
+        return torch.full((n,), 0.01 * (1 + t % 3), dtype=torch.bfloat16, device=dev)
+    if i == 1:
+        return torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    g = drifting_grad(n, seed, t, i, dev)
+    if i == 2:
+        g = g.float() * 1e-3
+        g[(7919 * t + 13) % n] = 4.0
+        g = g.to(torch.bfloat16)
+    return g
+
+
+@pytest.mark.parametrize("master", [torch.float32, torch.bfloat16])
+def test_scale_probe_edge_cases_equal_two_pass(master):
+    """The probe's candidate list at its edges (a tensor over the cap, one
+    with amax 0, one whose single candidate never holds the new maximum)
+    changes predictions only: weights, codes, scales and stats stay equal to
+    the two-pass schedule's bit for bit."""
+    sizes = [300_001, 65_536, 1 << 20, 5_000, 12_289]
+    a = _run("two_pass", sizes, 9, seed=21, master=master, grad_fn=_edge_grad)
+    b = _run("speculative", sizes, 9, seed=21, master=master, grad_fn=_edge_grad, predictor="probe")
+    for t, (x, y) in enumerate(zip(a, b), start=1):
+        for kind, xs, ys in zip(("p", "m", "v", "m_scale", "v_scale"), x[:5], y[:5]):
+            for i, (u, w) in enumerate(zip(xs, ys)):
+                assert np.array_equal(u.view(np.uint8), w.view(np.uint8)), f"step {t}: {kind} of tensor {i} differs"
+        for i, (sa, sb) in enumerate(zip(x[5], y[5])):
+            for k in ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite"):
+                assert sa[k] == sb[k], f"step {t} tensor {i}: stat {k}"
+    st = b[-1][5]
+    assert st[0]["probed"] == 0  # over the cap: no list
+    assert st[1]["probed"] == 0  # amax 0: nothing to list
+    # the parts of the last few spikes (v decays by beta2 a step, and its E5M2 codes may round a decayed
+    # spike up): listed, within the cap of 1/32 of the tensor's parts
+    assert 0 < st[2]["probed"] <= (1 << 20) // 32
