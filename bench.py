@@ -1,14 +1,16 @@
 """Benchmark of the FP8-moment AdamW step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2_7b]
-                    [--schedule two_pass|speculative] [--m-format e4m3|e5m2] [--v-format e4m3|e5m2]
+                    [--schedule two_pass|speculative] [--predictor auto|probe|growth]
+                    [--m-format e4m3|e5m2] [--v-format e4m3|e5m2]
 
 Times K whole optimizer steps (every tensor of the list, one fp8adam_step
 each) after W warm-up steps, with inputs resident in HBM, and prints one JSON
 line: params updated/s; the roofline of the dominant kernel (algorithmic bytes
 / its HIP-event duration, against 8 TB/s, and beside it against the pass's own
 byte mix streamed with trivial arithmetic by fp8adam_stream_mix on the same
-GPU); the bytes and rate of the whole step, the speculative fix-up included;
+GPU); the bytes and rate of the whole step, the speculative schedule's scale
+probe and fix-up included;
 and the CPU oracle timed on the same workload (the whole list for the flat 1M
 tensor and the Llama-2-100M list, a bounded sample of the larger lists).  Every
 step gets a fresh gradient draw (generated into the bound gradient buffers
@@ -247,6 +249,9 @@ def main():
                     help="delayed: scale from a 16-step amax history, one pass (per-tensor lists)")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="stochastic: moments rounded with a Philox4x32-10 stream (seed 1234)")
+    ap.add_argument("--predictor", default="auto", choices=["auto", "probe", "growth"],
+                    help="how the speculative schedule predicts each scale (auto: the probe on lists of "
+                         "at least 2^28 elements)")
     ap.add_argument("--m-format", choices=["e4m3", "e5m2"], default=None,
                     help="format of the first moment (default: the workload's, E4M3)")
     ap.add_argument("--v-format", choices=["e4m3", "e5m2"], default=None,
@@ -299,6 +304,7 @@ def main():
                                  and scaling == "just_in_time") else "two_pass"
     opt = pk.FP8AdamW(params, grads, m_format=w.m_fmt, v_format=w.v_fmt, granularity=w.granularity,
                       schedule=schedule, decay_mode=w.decay_mode, scaling=scaling, rounding=args.rounding,
+                      predictor=args.predictor,
                       seed=1234, collect_stats=args.collect_stats)
     hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
     stream = torch.cuda.current_stream()
@@ -476,6 +482,7 @@ def main():
                    "scaling": scaling if scaling == "just_in_time" else "delayed (amax history 16, margin 0)",
                    "loss_scaling": "scale 2^16, Inf/NaN skip, clip to global norm 1.0" if args.amp else None,
                    "rounding": args.rounding,
+                   "predictor": args.predictor if schedule == "speculative" else None,
                    "grad": "bf16, step 1's draw every step" if args.same_grad else "fresh bf16 draw per step",
                    "parallelism": "single GPU"},
         "roofline": roofline,
