@@ -334,7 +334,12 @@ def main():
         torch.cuda.synchronize()
         log(f"warm-up step {t} done")
 
-    opt.set_timing(True)
+    kernel = "block128_pass" if w.granularity == "block128" else (
+        "delayed_pass" if scaling == "delayed" else "spec_pass" if schedule == "speculative" else "update_pass")
+    # HIP events around the dominant kernel's launches (the roofline's duration) and, in the
+    # speculative schedule, the fix-up's and the probe's (reported below); every timed launch adds
+    # two event records to the stream, so the small kernels that are not reported go untimed
+    opt.set_timing(True, kinds=[kernel] + (["fixup", "spec_probe"] if schedule == "speculative" else []))
     evs = []
     requant = []  # per timed step: (element, moment) pairs brought to the true scale by the fix-up
     probed = []   # per timed step: elements the speculative schedule's scale probe read
@@ -368,8 +373,6 @@ def main():
         if cnt:
             log(f"  {k}: {cnt} launches, avg {tot / cnt * 1e3:.1f} us")
 
-    kernel = "block128_pass" if w.granularity == "block128" else (
-        "delayed_pass" if scaling == "delayed" else "spec_pass" if schedule == "speculative" else "update_pass")
     ktot, kcnt = ktimes[kernel]
     kavg_s = ktot / kcnt / 1e3
     bpp = BYTES_PER_PARAM[(w.granularity, w.master)]

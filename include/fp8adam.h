@@ -360,12 +360,20 @@ int fp8adam_stream_mix(int32_t master, void *p, const void *g, const void *m_in,
  * at most 4096 launches between two fp8adam_kernel_times calls. */
 int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 
+/* As fp8adam_set_timing, for the launches of the kernel kinds whose bit is set in
+ * kinds (bit k: kind k, as numbered for fp8adam_kernel_times; 0 disables timing).
+ * Each timed launch adds two event records to the stream, a gap of a few
+ * microseconds: timing only the kind of interest keeps a step's time close to
+ * its untimed one. */
+int fp8adam_set_timing_kinds(fp8adam_ctx *ctx, uint32_t kinds);
+
 /* Per-kernel timing since the last call (or since timing was enabled):
  * for kernel kind k < max (0 = amax pass, 1 = update pass, 2 = scale reduction,
  * 3 = block-scaled single pass, 4 = stats reset, 5 = speculative pass,
  * 6 = speculative scale check, 7 = speculative fix-up, 8 = delayed-scaling pass,
  * 9 = delayed-scaling commit, 10 = gradient-norm pass, 11 = loss-scale decision,
- * 12 = scale preparation of the speculative and delayed passes),
+ * 12 = scale preparation of the speculative and delayed passes, 13 = speculative
+ * scale probe, 14 = speculative per-chunk fold of the part partials),
  * total_ms[k] and count[k].
  * Host arrays of length max.  Synchronizes the recorded events, then clears. */
 int fp8adam_kernel_times(fp8adam_ctx *ctx, double *total_ms, int32_t *count, int32_t max);

@@ -44,6 +44,7 @@ KERNEL_KINDS = ("amax_pass", "update_pass", "scale_reduce", "block128_pass", "st
 # names of every entry point the header declares
 EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "fp8adam_last_error",
            "fp8adam_encode", "fp8adam_decode", "fp8adam_encode_bits_range", "fp8adam_set_timing",
+           "fp8adam_set_timing_kinds",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
            "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy",
            "fp8adam_step_noalloc", "fp8adam_stream_mix")
@@ -128,6 +129,7 @@ def load() -> ctypes.CDLL:
     L.fp8adam_decode.argtypes = [i32, vp, vp, i64, vp]
     L.fp8adam_encode_bits_range.argtypes = [i32, ctypes.c_uint32, i64, vp, vp]
     L.fp8adam_set_timing.argtypes = [vp, i32]
+    L.fp8adam_set_timing_kinds.argtypes = [vp, ctypes.c_uint32]
     L.fp8adam_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32), i32]
     L.fp8adam_runtime_version.argtypes = [ctypes.POINTER(i32)]
     L.fp8adam_num_chunks.argtypes = [vp]
@@ -141,7 +143,8 @@ def load() -> ctypes.CDLL:
     L.fp8adam_step_noalloc.argtypes = [ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg),
                                        ctypes.POINTER(HParamsArg), vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
-                 "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_kernel_times",
+                 "fp8adam_encode_bits_range", "fp8adam_set_timing", "fp8adam_set_timing_kinds",
+                 "fp8adam_kernel_times",
                  "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
                  "fp8adam_encode_sr", "fp8adam_stream_copy", "fp8adam_step_noalloc",
                  "fp8adam_stream_mix"):
@@ -273,6 +276,14 @@ def fp8adam_stream_mix(p: torch.Tensor, g: torch.Tensor, m_in: torch.Tensor, v_i
 
 def fp8adam_set_timing(ctx: int, enable: bool) -> None:
     _check(load().fp8adam_set_timing(ctx, int(enable)))
+
+
+def fp8adam_set_timing_kinds(ctx: int, kinds) -> None:
+    """Time only the launches of the given kernel kinds (names of KERNEL_KINDS)."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check(load().fp8adam_set_timing_kinds(ctx, mask))
 
 
 def fp8adam_kernel_times(ctx: int) -> dict:
@@ -443,8 +454,12 @@ class FP8AdamW:
         with torch.cuda.device(self.device):
             return fp8adam_stats(self._ctx, self.n)
 
-    def set_timing(self, enable: bool) -> None:
-        fp8adam_set_timing(self._ctx, enable)
+    def set_timing(self, enable: bool, kinds=None) -> None:
+        """Per-kernel timing of later steps: every kind, or only ``kinds`` (names of KERNEL_KINDS)."""
+        if enable and kinds is not None:
+            fp8adam_set_timing_kinds(self._ctx, kinds)
+        else:
+            fp8adam_set_timing(self._ctx, enable)
 
     def kernel_times(self) -> dict:
         return fp8adam_kernel_times(self._ctx)

@@ -944,17 +944,26 @@ int64_t fp8adam_num_chunks(const fp8adam_ctx* ctx) { return ctx ? ctx->nchunks :
 
 int32_t fp8adam_current_buffer(const fp8adam_ctx* ctx) { return ctx ? ctx->cur : -1; }
 
-int fp8adam_set_timing(fp8adam_ctx* ctx, int32_t enable) {
+int fp8adam_set_timing_kinds(fp8adam_ctx* ctx, uint32_t kinds) {
   try {
     if (!ctx) return fail(FP8ADAM_EINVAL, "ctx is null");
-    if (enable && ctx->ev.empty()) {
+    if (kinds && ctx->ev.empty()) {
       ctx->ev.resize(2 * kMaxTimed, nullptr);
       ctx->ev_kind.resize(kMaxTimed, 0);
       for (auto& e : ctx->ev) HIP_TRY(hipEventCreate(&e));
     }
-    ctx->timing = enable != 0;
+    ctx->timing = kinds != 0;
+    ctx->timing_kinds = kinds;
     ctx->ev_used = 0;
     return 0;
+  } catch (...) {
+    return fail(FP8ADAM_ENOMEM, "host allocation failed");
+  }
+}
+
+int fp8adam_set_timing(fp8adam_ctx* ctx, int32_t enable) {
+  try {
+    return fp8adam_set_timing_kinds(ctx, enable ? 0xFFFFFFFFu : 0u);
   } catch (...) {
     return fail(FP8ADAM_ENOMEM, "host allocation failed");
   }

@@ -11,7 +11,7 @@
 // Device work per step:
 //   per-tensor scales, two passes over a chunked multi-tensor list
 //     k_amax    : dequantize, update m and v in registers, max|m'| / max v'
-//                 per chunk (wave shuffle max, then LDS) -> one partial per
+//                 per chunk (DPP wave max, then LDS) -> one partial per
 //                 chunk, no atomics
 //     k_reduce  : one work-group per tensor: max over the tensor's partials,
 //                 stage the old scales, write the new scales into the
@@ -1623,6 +1623,7 @@ struct fp8adam_ctx {
   fp8adam_engine::GradCtl* d_gctl = nullptr;       // loss scaling: the decision of the step in flight
   const fp8adam_engine::GradCtl* gctl = nullptr;   // d_gctl during fp8adam_step_amp, else null
   bool timing = false;
+  uint32_t timing_kinds = 0xFFFFFFFFu;  // the kinds timed while timing is on (bit k: kind k)
   std::vector<hipEvent_t> ev;  // pairs
   std::vector<int> ev_kind;
   int ev_used = 0;
@@ -1632,7 +1633,7 @@ namespace fp8adam_engine {
 
 inline int timed_begin(fp8adam_ctx* c, int kind, hipStream_t s, int* slot) {
   *slot = -1;
-  if (!c->timing || c->ev_used >= kMaxTimed) return 0;
+  if (!c->timing || !((c->timing_kinds >> kind) & 1u) || c->ev_used >= kMaxTimed) return 0;
   *slot = c->ev_used++;
   c->ev_kind[*slot] = kind;
   HIP_TRY(hipEventRecord(c->ev[2 * *slot], s));

@@ -81,6 +81,7 @@ def test_error_paths_without_a_gpu():
     assert L.fp8adam_stream_copy(8, 16, 32, None) == -2             # misaligned
     assert L.fp8adam_stream_copy(None, None, 0, None) == 0
     assert L.fp8adam_num_chunks(None) == -1
+    assert L.fp8adam_set_timing_kinds(None, 1) == -1
     amp = pk.AmpConfigArg(1.0, 2.0, 0.5, 2000)
     assert L.fp8adam_step_amp(None, ctypes.byref(hp), ctypes.byref(amp), 64, None) == -1
     # a context whose widest launch would exceed one grid dimension (2^32 - 1

@@ -207,3 +207,28 @@ def test_runtime_is_torchs():
 
 def test_device_is_gfx950():
     assert "gfx950" in torch.cuda.get_device_properties(0).gcnArchName
+
+
+def test_timing_only_the_chosen_kernel_kinds():
+    """fp8adam_set_timing_kinds: only launches of the chosen kinds are timed
+    (the benchmark times the dominant pass and leaves the small kernels'
+    launches free of event records)."""
+    sizes = [70_001, 4096]
+    params = [torch.randn(n, device="cuda") * 0.02 for n in sizes]
+    grads = [random_grad(n, 5 + i, "cuda") for i, n in enumerate(sizes)]
+    opt = pk.FP8AdamW(params, grads, schedule="speculative", speculate_from_step=2)
+    try:
+        opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=1)
+        opt.set_timing(True, kinds=["spec_pass", "fixup"])
+        for t in (2, 3, 4):
+            opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=t)
+        kt = opt.kernel_times()
+        assert kt["spec_pass"][1] == 3 and kt["fixup"][1] == 3
+        assert all(cnt == 0 for k, (_, cnt) in kt.items() if k not in ("spec_pass", "fixup"))
+        opt.set_timing(True)
+        opt.step(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=5)
+        kt = opt.kernel_times()
+        assert kt["spec_pass"][1] == 1 and kt["spec_check"][1] == 1 and kt["scale_prepare"][1] == 1
+        opt.set_timing(False)
+    finally:
+        opt.close()
