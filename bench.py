@@ -341,6 +341,7 @@ def main():
     # two event records to the stream, so the small kernels that are not reported go untimed
     opt.set_timing(True, kinds=[kernel] + (["fixup", "spec_probe"] if schedule == "speculative" else []))
     evs = []
+    spacer = torch.zeros(1 << 26, dtype=torch.float32, device=dev)  # 256 MB: ~0.1 ms of streaming
     requant = []  # per timed step: (element, moment) pairs brought to the true scale by the fix-up
     probed = []   # per timed step: elements the speculative schedule's scale probe read
     stat_keys = ("underflow_m", "underflow_v", "saturated_m", "saturated_v", "nonfinite")
@@ -349,6 +350,10 @@ def main():
     for _ in range(args.steps):
         t += 1
         load_grads(t)  # not timed
+        # untimed work queued ahead of the step keeps the GPU busy while the host enqueues the step's
+        # launches, as the backward pass would in training (else a short step would include the
+        # host's launch latency: the stats read below leaves the stream idle)
+        spacer.mul_(1.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         opt_step(t)
