@@ -336,9 +336,9 @@ def main():
 
     kernel = "block128_pass" if w.granularity == "block128" else (
         "delayed_pass" if scaling == "delayed" else "spec_pass" if schedule == "speculative" else "update_pass")
-    # HIP events around the dominant kernel's launches (the roofline's duration) and, in the
+    # HIP events on the dominant kernel's launches (the roofline's duration) and, in the
     # speculative schedule, the fix-up's and the probe's (reported below); every timed launch adds
-    # two event records to the stream, so the small kernels that are not reported go untimed
+    # a gap of a few microseconds to the stream, so the small kernels that are not reported go untimed
     opt.set_timing(True, kinds=[kernel] + (["fixup", "spec_probe"] if schedule == "speculative" else []))
     evs = []
     spacer = torch.zeros(1 << 26, dtype=torch.float32, device=dev)  # 256 MB: ~0.1 ms of streaming

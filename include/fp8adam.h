@@ -355,16 +355,18 @@ int fp8adam_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t s
 int fp8adam_stream_mix(int32_t master, void *p, const void *g, const void *m_in, const void *v_in,
                        void *m_out, void *v_out, int64_t n, hipStream_t stream);
 
-/* Enable (1) or disable (0) per-kernel timing with HIP events around every
- * launch of later steps (creates the events; may allocate).  Timing records
- * at most 4096 launches between two fp8adam_kernel_times calls. */
+/* Enable (1) or disable (0) per-kernel timing of every launch of later steps:
+ * each timed kernel is launched with two HIP events (hipExtLaunchKernel), which
+ * the runtime stamps with the dispatch's own start and end (creates the
+ * events; may allocate).  Timing records at most 4096 launches between two
+ * fp8adam_kernel_times calls. */
 int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 
 /* As fp8adam_set_timing, for the launches of the kernel kinds whose bit is set in
  * kinds (bit k: kind k, as numbered for fp8adam_kernel_times; 0 disables timing).
- * Each timed launch adds two event records to the stream, a gap of a few
- * microseconds: timing only the kind of interest keeps a step's time close to
- * its untimed one. */
+ * Each timed launch still adds a gap of a few microseconds to the stream:
+ * timing only the kinds of interest keeps a step's time close to its untimed
+ * one. */
 int fp8adam_set_timing_kinds(fp8adam_ctx *ctx, uint32_t kinds);
 
 /* Per-kernel timing since the last call (or since timing was enabled):

@@ -454,14 +454,14 @@ void free_ctx(fp8adam_ctx* c) {
 int64_t norm_groups(const fp8adam_ctx* c) { return std::min<int64_t>(c->nchunks, kNormGroups); }
 
 void launch_gradnorm(fp8adam_ctx* c, hipStream_t s) {
-  hipLaunchKernelGGL(k_gradnorm, dim3((unsigned)norm_groups(c)), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     c->d_chunk_tid, c->d_gpart, c->chunk_log2, c->nchunks);
+  launch_k(c, k_gradnorm, dim3((unsigned)norm_groups(c)), dim3(kThreads), s, descs_of(c, c->cur), c->d_chunk_tid,
+           c->d_gpart, c->chunk_log2, c->nchunks);
 }
 
 void launch_gradctl(fp8adam_ctx* c, const fp8adam_amp_config& amp, fp8adam_amp_state* state,
                     const fp8adam_hparams& hp, hipStream_t s) {
-  hipLaunchKernelGGL(k_gradctl, dim3(1), dim3(kReduceThreads), 0, s, c->d_gpart, norm_groups(c), state, c->d_gctl, amp,
-                     hp.lr, hp.beta1, hp.beta2, c->hist_len);
+  launch_k(c, k_gradctl, dim3(1), dim3(kReduceThreads), s, c->d_gpart, norm_groups(c), state, c->d_gctl, amp, hp.lr,
+           hp.beta1, hp.beta2, c->hist_len);
 }
 
 int run_step(fp8adam_ctx* c, const StepConsts& k, int64_t t, hipStream_t s) {
@@ -652,7 +652,7 @@ int fp8adam_init(fp8adam_ctx** out, const fp8adam_tensor* tensors, int32_t n, co
     if (e == hipSuccess && (spec || delayed)) e = hipMalloc(&c->d_part_amax, sizeof(uint2) * (size_t)std::max<int64_t>(1, c->nuparts));
     if (e == hipSuccess) e = hipMalloc(&c->d_flags, sizeof(int32_t) * (size_t)n);
     if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_count, sizeof(uint32_t));
-    if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_list, sizeof(uint32_t) * (size_t)std::max<int64_t>(1, nchunks));
+    if (e == hipSuccess && spec) e = hipMalloc(&c->d_fix_list, sizeof(uint32_t) * (size_t)std::max<int64_t>(1, 2 * nchunks));
     if (spec) {
       const size_t ns = (size_t)std::max<int64_t>(1, c->ncand_slots);
       if (e == hipSuccess) e = hipMalloc(&c->d_cand_count, sizeof(uint32_t));

@@ -54,6 +54,7 @@
 // through buffer resources based at each work-group's part.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -63,6 +64,7 @@
 #include <algorithm>
 #include <new>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/fp8adam.h"
@@ -1190,14 +1192,22 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
     candlen = 0ull;
     flags[t] = f;
     flag = f;
-    // room for the tensor's chunks in the fix-up's work list (the order of the
-    // tensors there does not matter: every chunk is fixed up on its own)
-    list_base = f ? atomicAdd(fix_count, (uint32_t)((d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2)) : 0u;
+    // room in the fix-up's work list for the tensor's chunks, once per
+    // mispredicted moment (the order there does not matter: every chunk and
+    // moment is fixed up on its own)
+    const uint32_t nc = (uint32_t)((d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2);
+    list_base = f ? atomicAdd(fix_count, nc * (uint32_t)__popc(f)) : 0u;
   }
   __syncthreads();
-  if (flag) {
+  if (flag) {  // entries: chunk * 2 + moment (0: m, 1: v)
     const int64_t nc = (d.numel + ((int64_t)1 << chunk_log2) - 1) >> chunk_log2;
-    for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads) fix_list[list_base + k] = (uint32_t)(d.chunk0 + k);
+    int64_t base = list_base;
+    for (int b = 0; b < 2; b++) {
+      if (!(flag & (1 << b))) continue;  // uniform
+      for (int64_t k = threadIdx.x; k < nc; k += kReduceThreads)
+        fix_list[base + k] = (uint32_t)(((d.chunk0 + k) << 1) | b);
+      base += nc;
+    }
   }
   // the next step's probe candidates: the parts within kCandTheta of this
   // step's amax of either moment (their order in the list does not matter),
@@ -1253,14 +1263,13 @@ __global__ __launch_bounds__(kReduceThreads) void k_spec_reduce(const TensorDesc
   }
 }
 
-// One work-group per chunk of a flagged tensor (the others return at once):
-// bring the mispredicted moment(s) in the destination buffer to the true
-// scale.  Both scales are powers of two, so most codes only need their
+// The fix-up, per listed chunk (or piece of one) and mispredicted moment of a
+// flagged tensor: bring the moment in the destination buffer to the true scale.  Both scales are powers of two, so most codes only need their
 // exponent field moved (shift_codes4: 1 byte read and written per element);
 // a group of four with a code that cannot be moved exactly (zero, subnormal,
 // FMAX) is recomputed from the gradient and the old codes still intact in the
 // source buffer and requantized with the true scale.  p is not touched: its
-// update does not depend on the scales.  Flag bit 0: m, bit 1: v.
+// update does not depend on the scales.
 template <int FMT, bool STATS, bool IS_V, bool SR>
 __device__ __forceinline__ uint32_t recompute4(const StepConsts& c, int tid, const TensorDesc& d, int64_t i,
                                                float s_old, float inv_new, uint32_t& under, uint32_t& sat) {
@@ -1353,17 +1362,26 @@ __device__ __forceinline__ void fixup_moment(const StepConsts& c, int tid, const
 }
 
 // Work-groups of the fix-up: a fixed grid striding over the work list of the
-// flagged chunks, which k_spec_reduce builds, so no work-group is launched for
-// the (most) chunks whose tensor was predicted right.  Measured on the 7B list
+// flagged chunks and moments, which k_spec_reduce builds, so no work-group is
+// launched for the (most) chunks whose tensor was predicted right.  Measured on the 7B list
 // (steps 4-23, 6.8% of the (element, moment) pairs moved, one box per sweep):
 // 1024 work-groups 497 us per fix-up, 2048 459, 4096 395, 8192 369, 16384
 // 359, 32768 356, 65536 358; one list item per chunk (32768 elements) against
-// halves 379 us and quarters 392 us; non-temporal stores of the moved codes
-// 366 us against 360 us plain.
+// halves 379 us and quarters 392 us (always split, more items than work-groups);
+// non-temporal stores of the moved codes 366 us against 360 us plain.
 #ifndef FP8ADAM_FIX_GROUPS
 #define FP8ADAM_FIX_GROUPS 16384
 #endif
 constexpr int64_t kFixGroups = FP8ADAM_FIX_GROUPS;
+// Smallest piece of a chunk the fix-up hands to one work-group: one 16-code
+// access per lane.  When the list holds fewer entries than the grid has
+// work-groups, each chunk is split into 2^s pieces, the largest s whose pieces
+// still fit the grid, so that a short list (a small model, or a step with few
+// mispredicted tensors) spreads over the chip instead of leaving a few
+// work-groups to walk whole chunks.
+constexpr int kFixPieceLog2Min = 12;
+static_assert((1 << kFixPieceLog2Min) == 16 * kThreads, "one 16-code access per lane");
+static_assert(kMinChunkLog2 >= kFixPieceLog2Min, "a chunk holds at least one piece");
 // Work-groups of the scale probe (a fixed grid striding over the list's slots).
 constexpr int64_t kProbeGroups = 8192;
 
@@ -1372,30 +1390,33 @@ __global__ __launch_bounds__(kThreads) void k_fixup(const TensorDesc* __restrict
                                                     const TensorDesc* __restrict__ dst_descs,
                                                     const int32_t* __restrict__ chunk_tid,
                                                     const uint32_t* __restrict__ amax,
-                                                    const float* __restrict__ old_scale,
-                                                    const int32_t* __restrict__ flags, StepConsts c,
+                                                    const float* __restrict__ old_scale, StepConsts c,
                                                     unsigned long long* __restrict__ counters, int chunk_log2,
                                                     const uint32_t* __restrict__ fix_count,
                                                     const uint32_t* __restrict__ fix_list,
                                                     const GradCtl* __restrict__ gctl) {
   if (amp_apply(gctl, c)) return;
-  const int64_t nwork = ld_global<uint32_t>(fix_count);
+  const int64_t nlisted = ld_global<uint32_t>(fix_count);
+  int split = 0;  // pieces per listed entry: 2^split (the same in every work-group)
+  while (split < chunk_log2 - kFixPieceLog2Min && (nlisted << (split + 1)) <= (int64_t)gridDim.x) split++;
+  const int piece_log2 = chunk_log2 - split;
+  const int64_t nwork = nlisted << split;
   for (int64_t w = blockIdx.x; w < nwork; w += gridDim.x) {
-    const int64_t chunk = ld_global<uint32_t>(fix_list + w);
+    const uint32_t e = ld_global<uint32_t>(fix_list + (w >> split));
+    const int64_t chunk = e >> 1;
     const int tid = chunk_tid[chunk];
-    const int32_t f = flags[tid];
     const TensorDesc d = descs[tid];
-    const int64_t start = (chunk - d.chunk0) << chunk_log2;
-    const int64_t end = min(start + ((int64_t)1 << chunk_log2), d.numel);
+    const int64_t start = ((chunk - d.chunk0) << chunk_log2) + ((w & (((int64_t)1 << split) - 1)) << piece_log2);
+    if (start >= d.numel) continue;  // a piece past the end of the tensor's last chunk
+    const int64_t end = min(start + ((int64_t)1 << piece_log2), d.numel);
     uint32_t cnt[kStatsPerTensor] = {0, 0, 0, 0, 0};
-    if (f & 1) {
+    if ((e & 1u) == 0u) {
       float s, inv;
       choose_scale<MF, 0>(amax[2 * tid], s, inv);
       fixup_moment<MF, STATS, false, SR>(c, tid, d, dst_descs[tid].m, start, end, old_scale[4 * tid],
                                          __float_as_uint(old_scale[4 * tid + 2]), s, inv, cnt[kUnderM],
                                          cnt[kSatM]);
-    }
-    if (f & 2) {
+    } else {
       float s, inv;
       choose_scale<VF, 0>(amax[2 * tid + 1], s, inv);
       fixup_moment<VF, STATS, true, SR>(c, tid, d, dst_descs[tid].v, start, end, old_scale[4 * tid + 1],
@@ -1608,8 +1629,8 @@ struct fp8adam_ctx {
   uint2* d_part_amax = nullptr;     // speculative / delayed: [<= nuparts] per-part amax of m', v'
   float* d_old_scale = nullptr;     // tensor mode: [n][4]: scales before the step (+ prepared ones)
   int32_t* d_flags = nullptr;       // [n]: the last step re-quantized the tensor (speculative)
-  uint32_t* d_fix_count = nullptr;  // speculative: chunks in the fix-up's work list this step
-  uint32_t* d_fix_list = nullptr;   // speculative: [<= nchunks] the chunks of the flagged tensors
+  uint32_t* d_fix_count = nullptr;  // speculative: entries in the fix-up's work list this step
+  uint32_t* d_fix_list = nullptr;   // speculative: [<= 2 nchunks] chunk * 2 + moment of the flagged tensors
   int64_t ncand_slots = 0;          // speculative: room in the probe's work list (the tensors' caps summed)
   uint32_t* d_cand_count = nullptr; // speculative: entries in the probe's work list
   uint2* d_cand_work = nullptr;     // speculative: [ncand_slots] (tensor, part index within the tensor)
@@ -1627,23 +1648,52 @@ struct fp8adam_ctx {
   std::vector<hipEvent_t> ev;  // pairs
   std::vector<int> ev_kind;
   int ev_used = 0;
+  int ev_pending = -1;  // the slot whose events the next launch takes (-1: none)
 };
 
 namespace fp8adam_engine {
 
-inline int timed_begin(fp8adam_ctx* c, int kind, hipStream_t s, int* slot) {
+// A timed launch hands its slot's two events to the kernel launch itself
+// (launch_k), which stamps them with the dispatch's own start and end: no
+// event packets of their own in the stream, so timing adds less to a step and
+// the recorded duration is the kernel's.
+inline int timed_begin(fp8adam_ctx* c, int kind, hipStream_t, int* slot) {
   *slot = -1;
   if (!c->timing || !((c->timing_kinds >> kind) & 1u) || c->ev_used >= kMaxTimed) return 0;
   *slot = c->ev_used++;
   c->ev_kind[*slot] = kind;
-  HIP_TRY(hipEventRecord(c->ev[2 * *slot], s));
+  c->ev_pending = *slot;
   return 0;
 }
 
-inline int timed_end(fp8adam_ctx* c, int slot, hipStream_t s) {
-  if (slot < 0) return 0;
-  HIP_TRY(hipEventRecord(c->ev[2 * slot + 1], s));
+inline int timed_end(fp8adam_ctx* c, int slot, hipStream_t) {
+  if (slot >= 0 && c->ev_pending == slot) {  // nothing was launched: give the slot back
+    c->ev_pending = -1;
+    c->ev_used--;
+  }
   return 0;
+}
+
+// Launch a kernel with the argument conversions of hipLaunchKernelGGL; inside a
+// timed launch through hipExtLaunchKernel with the pending slot's events.
+template <typename... Formals, typename... Actuals>
+inline void launch_k(fp8adam_ctx* c, void (*kernel)(Formals...), dim3 grid, dim3 block, hipStream_t s,
+                     Actuals... actuals) {
+  static_assert(sizeof...(Formals) == sizeof...(Actuals), "kernel argument count");
+  std::tuple<Formals...> formals{actuals...};
+  void* argv[sizeof...(Formals) > 0 ? sizeof...(Formals) : 1];
+  std::apply([&argv](auto&... f) {
+    int i = 0;
+    ((argv[i++] = static_cast<void*>(&f)), ...);
+  }, formals);
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  if (c->ev_pending >= 0) {
+    const int slot = c->ev_pending;
+    c->ev_pending = -1;
+    (void)hipExtLaunchKernel(fn, grid, block, argv, 0, s, c->ev[2 * slot], c->ev[2 * slot + 1], 0);
+  } else {
+    (void)hipLaunchKernel(fn, grid, block, argv, 0, s);
+  }
 }
 
 // ---- kernel dispatch over the template parameters ----
@@ -1652,88 +1702,90 @@ inline const TensorDesc* descs_of(const fp8adam_ctx* c, int which) { return c->d
 
 template <int MF, int VF, bool BF16P, bool L2>
 void launch_amax(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_amax<MF, VF, BF16P && L2, L2>), dim3(grid_for<false>(c->nchunks)), dim3(kThreads), 0, s, descs_of(c, c->cur),
-                     c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks, c->gctl);
+  launch_k(c, k_amax<MF, VF, BF16P && L2, L2>, dim3(grid_for<false>(c->nchunks)), dim3(kThreads), s, descs_of(c, c->cur),
+           c->d_chunk_tid, c->d_partial, k, c->chunk_log2, c->nchunks, c->gctl);
 }
 
 template <int MF, int VF, int SMODE, bool STATS>
 void launch_reduce(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce<MF, VF, SMODE, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
-                     c->d_flags, k.hist_len, k.hist_slot, c->gctl);
+  launch_k(c, k_reduce<MF, VF, SMODE, STATS>, dim3((unsigned)c->n), dim3(kReduceThreads), s,
+           descs_of(c, c->cur), c->d_partial, c->d_amax, c->d_old_scale, c->d_counters, c->chunk_log2,
+           c->d_flags, k.hist_len, k.hist_slot, c->gctl);
 }
 
 template <int MF, int VF, int SMODE>
 void launch_delayed_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_delayed_prepare<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(64), 0, s, descs_of(c, 0), k,
-                     c->d_old_scale);
+  launch_k(c, k_delayed_prepare<MF, VF, SMODE>, dim3((unsigned)c->n), dim3(64), s, descs_of(c, 0), k,
+           c->d_old_scale);
 }
 
 template <int MF, int VF, int SMODE>
 void launch_delayed_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
-  hipLaunchKernelGGL((k_delayed_reduce<MF, VF, SMODE>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, part_log2, c->gctl,
-                     c->d_old_scale);
+  launch_k(c, k_delayed_reduce<MF, VF, SMODE>, dim3((unsigned)c->n), dim3(kReduceThreads), s,
+           descs_of(c, 0), c->d_part_amax, c->d_amax, k, c->chunk_log2, part_log2, c->gctl,
+           c->d_old_scale);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, int MODE, bool L2, bool SR>
 void launch_update(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   const int64_t nwork = c->nchunks << (c->chunk_log2 - upd_part_log2<BF16P>());
-  hipLaunchKernelGGL((k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>), dim3(grid_for<kXcdStreams>(nwork)), dim3(kThreads), 0, s,
-                     descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, nwork, c->gctl);
+  launch_k(c, k_update<MF, VF, BF16P, STATS, SMODE, MODE, L2, SR>, dim3(grid_for<kXcdStreams>(nwork)), dim3(kThreads), s,
+           descs_of(c, c->cur), descs_of(c, MODE == kModeSpec ? 1 - c->cur : c->cur), c->d_chunk_tid, c->d_amax,
+           c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_part_amax, nwork, c->gctl);
 }
 
 template <int MF, int VF, bool BF16P>
 void launch_spec_probe(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_spec_probe<MF, VF, upd_part_log2<BF16P>()>),
-                     dim3((unsigned)std::min<int64_t>(c->ncand_slots, kProbeGroups)), dim3(kThreads), 0, s,
-                     descs_of(c, c->cur), k, c->d_cand_count, c->d_cand_work, c->d_lb, c->gctl);
+  launch_k(c, k_spec_probe<MF, VF, upd_part_log2<BF16P>()>,
+           dim3((unsigned)std::min<int64_t>(c->ncand_slots, kProbeGroups)), dim3(kThreads), s,
+           descs_of(c, c->cur), k, c->d_cand_count, c->d_cand_work, c->d_lb, c->gctl);
 }
 
 template <int MF, int VF>
 void launch_spec_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_spec_prepare<MF, VF>), dim3((unsigned)((c->n + 63) / 64)), dim3(64), 0, s, descs_of(c, c->cur),
-                     c->d_amax, k, c->gctl, c->d_old_scale, c->n, c->d_fix_count,
-                     c->ncand_slots > 0 ? c->d_cand_n : nullptr, c->d_cand_len, c->d_lb, c->d_probed,
-                     c->d_cand_count);
+  launch_k(c, k_spec_prepare<MF, VF>, dim3((unsigned)((c->n + 63) / 64)), dim3(64), s, descs_of(c, c->cur),
+           c->d_amax, k, c->gctl, c->d_old_scale, c->n, c->d_fix_count,
+           c->ncand_slots > 0 ? c->d_cand_n : nullptr, c->d_cand_len, c->d_lb, c->d_probed,
+           c->d_cand_count);
 }
 
 template <int MF, int VF>
 void launch_exact_prepare(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_exact_prepare<MF, VF>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s, descs_of(c, c->cur),
-                     c->d_partial, c->chunk_log2, k, c->gctl, c->d_old_scale, c->d_fix_count, c->d_probed,
-                     c->d_cand_count);
+  launch_k(c, k_exact_prepare<MF, VF>, dim3((unsigned)c->n), dim3(kReduceThreads), s, descs_of(c, c->cur),
+           c->d_partial, c->chunk_log2, k, c->gctl, c->d_old_scale, c->d_fix_count, c->d_probed,
+           c->d_cand_count);
 }
 
 template <bool BF16P>
 void launch_part_fold(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   const int split = c->chunk_log2 - upd_part_log2<BF16P>();
   const int64_t lanes = split > 1 ? (int64_t)1 << (split - 1) : 1;
-  hipLaunchKernelGGL((k_part_fold<upd_part_log2<BF16P>()>), dim3((unsigned)((c->nchunks * lanes + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, c->d_part_amax, c->d_partial, c->chunk_log2, c->nchunks, k, c->gctl);
+  launch_k(c, k_part_fold<upd_part_log2<BF16P>()>, dim3((unsigned)((c->nchunks * lanes + kThreads - 1) / kThreads)),
+           dim3(kThreads), s, c->d_part_amax, c->d_partial, c->chunk_log2, c->nchunks, k, c->gctl);
 }
 
 template <int MF, int VF, bool STATS>
 void launch_spec_reduce(fp8adam_ctx* c, const StepConsts& k, int part_log2, hipStream_t s) {
-  hipLaunchKernelGGL((k_spec_reduce<MF, VF, STATS>), dim3((unsigned)c->n), dim3(kReduceThreads), 0, s,
-                     descs_of(c, c->cur), c->d_part_amax, c->ncand_slots > 0 ? c->d_partial : nullptr, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
-                     c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list, c->d_cand_n,
-                     c->d_cand_len, c->d_cand_count, c->ncand_slots > 0 ? c->d_cand_work : nullptr);
+  launch_k(c, k_spec_reduce<MF, VF, STATS>, dim3((unsigned)c->n), dim3(kReduceThreads), s,
+           descs_of(c, c->cur), c->d_part_amax, c->ncand_slots > 0 ? c->d_partial : nullptr, c->d_amax, c->d_old_scale, c->d_flags, c->d_counters,
+           c->chunk_log2, part_log2, k, c->gctl, c->d_fix_count, c->d_fix_list, c->d_cand_n,
+           c->d_cand_len, c->d_cand_count, c->ncand_slots > 0 ? c->d_cand_work : nullptr);
 }
 
 template <int MF, int VF, bool STATS, bool SR>
 void launch_fixup(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_fixup<MF, VF, STATS, SR>), dim3((unsigned)std::min<int64_t>(c->nchunks, kFixGroups)),
-                     dim3(kThreads), 0, s, descs_of(c, c->cur), descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax,
-                     c->d_old_scale, c->d_flags, k, c->d_counters, c->chunk_log2, c->d_fix_count, c->d_fix_list,
-                     c->gctl);
+  // room for every chunk split down to the smallest piece, up to the fixed grid
+  const int64_t groups = std::min<int64_t>((2 * c->nchunks) << (c->chunk_log2 - kFixPieceLog2Min), kFixGroups);
+  launch_k(c, k_fixup<MF, VF, STATS, SR>, dim3((unsigned)groups),
+           dim3(kThreads), s, descs_of(c, c->cur), descs_of(c, 1 - c->cur), c->d_chunk_tid, c->d_amax,
+           c->d_old_scale, k, c->d_counters, c->chunk_log2, c->d_fix_count, c->d_fix_list,
+           c->gctl);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
 void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
-  hipLaunchKernelGGL((k_block<MF, VF, BF16P, STATS, SMODE, L2, SR>), dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), 0, s,
-                     descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts, c->gctl);
+  launch_k(c, k_block<MF, VF, BF16P, STATS, SMODE, L2, SR>, dim3(grid_for<kXcdStreams>(c->nparts)), dim3(kThreads), s,
+           descs_of(c, 0), c->d_chunk_tid, k, c->d_counters, c->d_amax, c->chunk_log2, c->nparts, c->gctl);
 }
 
 // Timing kinds: 0 amax pass, 1 update pass, 2 scale reduce, 3 block pass,
@@ -1750,8 +1802,8 @@ void launch_block(fp8adam_ctx* c, const StepConsts& k, hipStream_t s) {
   } while (0)
 
 inline void launch_reset(fp8adam_ctx* c, int64_t namax, hipStream_t s) {
-  hipLaunchKernelGGL(k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
-                     dim3(kThreads), 0, s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
+  launch_k(c, k_reset, dim3(std::max<int64_t>(1, std::min<int64_t>(1024, (5 * (int64_t)c->n + 255) / 256))),
+           dim3(kThreads), s, c->d_counters, (int64_t)kStatsPerTensor * c->n, c->d_amax, namax);
 }
 
 template <int MF, int VF, bool BF16P, bool STATS, int SMODE, bool L2, bool SR>
