@@ -359,7 +359,8 @@ int fp8adam_stream_mix(int32_t master, void *p, const void *g, const void *m_in,
  * each timed kernel is launched with two HIP events (hipExtLaunchKernel), which
  * the runtime stamps with the dispatch's own start and end (creates the
  * events; may allocate).  Timing records at most 4096 launches between two
- * fp8adam_kernel_times calls. */
+ * fp8adam_kernel_times calls; launches into a stream under graph capture are
+ * not timed. */
 int fp8adam_set_timing(fp8adam_ctx *ctx, int32_t enable);
 
 /* As fp8adam_set_timing, for the launches of the kernel kinds whose bit is set in

@@ -1656,10 +1656,14 @@ namespace fp8adam_engine {
 // A timed launch hands its slot's two events to the kernel launch itself
 // (launch_k), which stamps them with the dispatch's own start and end: no
 // event packets of their own in the stream, so timing adds less to a step and
-// the recorded duration is the kernel's.
-inline int timed_begin(fp8adam_ctx* c, int kind, hipStream_t, int* slot) {
+// the recorded duration is the kernel's.  Launches into a stream under graph
+// capture are not timed (a captured kernel runs when the graph is launched).
+inline int timed_begin(fp8adam_ctx* c, int kind, hipStream_t s, int* slot) {
   *slot = -1;
   if (!c->timing || !((c->timing_kinds >> kind) & 1u) || c->ev_used >= kMaxTimed) return 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone) return 0;
   *slot = c->ev_used++;
   c->ev_kind[*slot] = kind;
   c->ev_pending = *slot;

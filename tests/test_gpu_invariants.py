@@ -232,3 +232,47 @@ def test_timing_only_the_chosen_kernel_kinds():
         opt.set_timing(False)
     finally:
         opt.close()
+
+
+def test_timed_step_captured_in_a_graph_is_untimed_and_replays_exactly():
+    """A two-pass step captured in a HIP graph (torch's capture) while timing
+    is on: the captured launches are not timed (a captured kernel runs only
+    when the graph replays), and every replay, with eager work and
+    synchronizations between the replays, leaves the same state, bit for bit,
+    as the same step called eagerly on a copy."""
+    dev = torch.device("cuda")
+    sizes = [70_001, 4096, 33]
+    pa = [torch.randn(n, device=dev) * 0.02 for n in sizes]
+    pb = [x.clone() for x in pa]
+    grads = [random_grad(n, 11 + i, "cuda") for i, n in enumerate(sizes)]
+    hp = HP
+    A = pk.FP8AdamW(pa, grads)
+    B = pk.FP8AdamW(pb, grads)
+    try:
+        A.step(**hp, step=1)
+        B.step(**hp, step=1)
+        torch.cuda.synchronize()
+        A.set_timing(True)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            A.step(**hp, step=2)
+        torch.cuda.synchronize()
+        assert all(cnt == 0 for _, cnt in A.kernel_times().values())
+        for r in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            B.step(**hp, step=2)
+            torch.cuda.synchronize()
+            _ = float(torch.randn(1 << 20, device=dev).abs().sum())  # eager work between the replays
+            for name, xa, xb in (("p", pa, pb), ("m", A.m, B.m), ("v", A.v, B.v),
+                                 ("m_scale", A.m_scale, B.m_scale), ("v_scale", A.v_scale, B.v_scale)):
+                for i, (x, y) in enumerate(zip(xa, xb)):
+                    assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {r + 1}: {name} {i}"
+        A.set_timing(False)
+        del g
+        torch.cuda.synchronize()
+    finally:
+        A.close()
+        B.close()
