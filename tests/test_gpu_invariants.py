@@ -212,7 +212,7 @@ def test_device_is_gfx950():
 def test_timing_only_the_chosen_kernel_kinds():
     """fp8adam_set_timing_kinds: only launches of the chosen kinds are timed
     (the benchmark times the dominant pass and leaves the small kernels'
-    launches free of event records)."""
+    launches untimed, free of the gap a timed launch adds)."""
     sizes = [70_001, 4096]
     params = [torch.randn(n, device="cuda") * 0.02 for n in sizes]
     grads = [random_grad(n, 5 + i, "cuda") for i, n in enumerate(sizes)]
