@@ -251,6 +251,42 @@ def test_llama2_100m_speculative_all_format_pairs():
                  speculate_from_step=4)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("rounding", ["nearest", "stochastic"])
+def test_llama2_100m_speculative_equals_two_pass_over_100_steps(rounding):
+    """The Llama-2-100M list (110 tensors, 1.1e8 parameters) under both
+    schedules from the same state and the same fresh gradients for 100 steps,
+    stats off as benchmarked: on a list this short the growth model predicts
+    and the fix-up splits its work into pieces, and every tensor's weights,
+    codes and scales stay bit-identical to the two-pass schedule's after steps
+    4, 30 and 100."""
+    w = workloads.llama2_100m()
+    dev = torch.device("cuda")
+    shapes = w.shapes
+    grads = [torch.empty(workloads.numel(s), dtype=torch.bfloat16, device=dev) for _, s in shapes]
+    pa = [workloads.make_param(w, i, s, dev) for i, (_, s) in enumerate(shapes)]
+    pb = [p.clone() for p in pa]
+    a = pk.FP8AdamW(pa, grads, schedule="two_pass", rounding=rounding, seed=3)
+    b = pk.FP8AdamW(pb, grads, schedule="speculative", rounding=rounding, seed=3)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+    try:
+        for t in range(1, 101):
+            for i, (_, s) in enumerate(shapes):
+                grads[i].copy_(workloads.make_grad(w, i, s, t, dev))
+            a.step(step=t, **hp)
+            b.step(step=t, **hp)
+            if t in (4, 30, 100):
+                torch.cuda.synchronize()
+                for i, (name, _) in enumerate(shapes):
+                    for kind, x, y in (("p", pa[i], pb[i]), ("m", a.m[i], b.m[i]), ("v", a.v[i], b.v[i]),
+                                       ("m_scale", a.m_scale[i], b.m_scale[i]),
+                                       ("v_scale", a.v_scale[i], b.v_scale[i])):
+                        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"step {t}: {kind} of {name}"
+    finally:
+        a.close()
+        b.close()
+
+
 @pytest.mark.timeout(300)
 def test_flat_1m_speculative_ten_steps():
     """The 1M flat tensor (per-row gradient scales) as benchmarked: speculative
