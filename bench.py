@@ -9,8 +9,9 @@ each) after W warm-up steps, with inputs resident in HBM, and prints one JSON
 line: params updated/s; the roofline of the dominant kernel (algorithmic bytes
 / its HIP-event duration, against 8 TB/s, and beside it against the pass's own
 byte mix streamed with trivial arithmetic by fp8adam_stream_mix on the same
-GPU); the bytes and rate of the whole step, the speculative schedule's scale
-probe and fix-up included;
+GPU, and against the time its bytes would take at the GPU's read-only and
+write-only rates, fp8adam_stream_rw); the bytes and rate of the whole step, the
+speculative schedule's scale probe and fix-up included;
 and the CPU oracle timed on the same workload (the whole list for the flat 1M
 tensor and the Llama-2-100M list, a bounded sample of the larger lists).  Every
 step gets a fresh gradient draw (generated into the bound gradient buffers
@@ -48,6 +49,9 @@ HBM_PEAK_GBS = 8000.0
 #   block-128 pass, fp32 master: 14 + 2 scales * (read 4 + write 4) / 128      = 14.125
 BYTES_PER_PARAM = {("tensor", "fp32"): 14.0, ("tensor", "bf16"): 10.0,
                    ("block128", "fp32"): 14.125, ("block128", "bf16"): 10.125}
+# of which written: p (4 or 2 bytes) and the two codes, plus the two block scales per 128 elements
+WRITE_BYTES_PER_PARAM = {("tensor", "fp32"): 6.0, ("tensor", "bf16"): 4.0,
+                         ("block128", "fp32"): 6.0625, ("block128", "bf16"): 4.0625}
 KERNEL_SOURCES = ["precision_adam_optimizer_amd/csrc/fp8adam.hip", "precision_adam_optimizer_amd/csrc/fp8adam_engine.h",
                   "precision_adam_optimizer_amd/csrc/fp8_codec.h"]
 
@@ -113,6 +117,35 @@ def copy_bandwidth(stream) -> float:
     gbps = 2 * n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
     return gbps
+
+
+def rw_bandwidth(stream) -> tuple[float, float]:
+    """GB/s of a read-only and of a write-only stream of 4 GiB (fp8adam_stream_rw: the
+    step kernels' access pattern), median of three rounds on fresh allocations, five
+    launches each: the two rates that bound any mix of reads and writes."""
+    import torch
+
+    import precision_adam_optimizer_amd as pk
+    n = 4 << 30
+    reads, writes = [], []
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            a = torch.ones(n, dtype=torch.uint8, device="cuda")
+            b = torch.empty(n, dtype=torch.uint8, device="cuda")
+            for src, dst, out in ((a, None, reads), (None, b, writes)):
+                for _ in range(2):
+                    pk.fp8adam_stream_rw(src, dst, stream.cuda_stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(5):
+                    pk.fp8adam_stream_rw(src, dst, stream.cuda_stream)
+                e1.record(stream)
+                e1.synchronize()
+                out.append(n * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+            del a, b
+            torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    return sorted(reads)[1], sorted(writes)[1]
 
 
 def mix_bandwidth(stream, master: str) -> tuple[float, float]:
@@ -445,6 +478,18 @@ def main():
     roofline["mix_GBps_best"] = round(mix_best, 1)
     roofline["frac_of_mix"] = round(achieved / mix_med, 4)
     roofline["copy_GBps"] = round(copy_gbps, 1)
+    # the kernel's bytes at the read-only and the write-only rates, one after the other: the
+    # bound its read/write mix would reach if the two streams did not slow each other down
+    read_gbps, write_gbps = rw_bandwidth(stream)
+    wpp = WRITE_BYTES_PER_PARAM[(w.granularity, w.master)]
+    rw_bound = bpp / ((bpp - wpp) / read_gbps + wpp / write_gbps)
+    log(f"read-only stream {read_gbps:.0f} GB/s, write-only {write_gbps:.0f} GB/s: {kernel}'s "
+        f"{bpp - wpp:g} B read + {wpp:g} B written per param at those rates {rw_bound:.0f} GB/s; "
+        f"{kernel} at {achieved / rw_bound:.1%} of it")
+    roofline["read_GBps"] = round(read_gbps, 1)
+    roofline["write_GBps"] = round(write_gbps, 1)
+    roofline["rw_bound_GBps"] = round(rw_bound, 1)
+    roofline["frac_of_rw_bound"] = round(achieved / rw_bound, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

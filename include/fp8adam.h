@@ -344,6 +344,14 @@ int fp8adam_encode_sr(int32_t fmt, const float *x, const uint16_t *r16, uint8_t 
  * 16 (EINVAL otherwise, EALIGN for misaligned pointers). */
 int fp8adam_stream_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
 
+/* Read read_bytes of src and write write_bytes of dst on `stream` with fp8adam_stream_copy's
+ * access pattern: dst[i] = src[i] where both sizes cover byte i, 0 where only write_bytes
+ * does.  write_bytes = 0 gives a read-only stream and read_bytes = 0 a write-only one: the
+ * two rates that bound any mix of reads and writes (such as the step's).  src, dst: device,
+ * 16-byte aligned, not overlapping (either may be NULL where its size is 0); sizes
+ * non-negative multiples of 16 (EINVAL otherwise, EALIGN for misaligned pointers). */
+int fp8adam_stream_rw(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes, hipStream_t stream);
+
 /* The update pass's access pattern with trivial arithmetic, over n elements: reads p (n fp32
  * weights, or bf16 with master FP8ADAM_MASTER_BF16), g (n bf16), m_in and v_in (n bytes each),
  * writes p in place (p += g) and m_out, v_out (n bytes each): 14 bytes per element (10 with a

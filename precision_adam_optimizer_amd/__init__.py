@@ -47,7 +47,7 @@ EXPORTS = ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_destroy", "
            "fp8adam_set_timing_kinds",
            "fp8adam_kernel_times", "fp8adam_runtime_version", "fp8adam_num_chunks", "fp8adam_current_buffer",
            "fp8adam_step_amp", "fp8adam_encode_sr_bits_range", "fp8adam_encode_sr", "fp8adam_stream_copy",
-           "fp8adam_step_noalloc", "fp8adam_stream_mix")
+           "fp8adam_step_noalloc", "fp8adam_stream_mix", "fp8adam_stream_rw")
 
 # limits of fp8adam_step_noalloc (the header's FP8ADAM_NOALLOC_* macros)
 NOALLOC_MAX_TENSORS = 4096
@@ -140,6 +140,7 @@ def load() -> ctypes.CDLL:
     L.fp8adam_encode_sr.argtypes = [i32, vp, vp, vp, i64, vp]
     L.fp8adam_stream_copy.argtypes = [vp, vp, i64, vp]
     L.fp8adam_stream_mix.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, vp]
+    L.fp8adam_stream_rw.argtypes = [vp, i64, vp, i64, vp]
     L.fp8adam_step_noalloc.argtypes = [ctypes.POINTER(TensorArg), i32, ctypes.POINTER(ConfigArg),
                                        ctypes.POINTER(HParamsArg), vp]
     for name in ("fp8adam_init", "fp8adam_step", "fp8adam_stats", "fp8adam_encode", "fp8adam_decode",
@@ -147,7 +148,7 @@ def load() -> ctypes.CDLL:
                  "fp8adam_kernel_times",
                  "fp8adam_runtime_version", "fp8adam_step_amp", "fp8adam_encode_sr_bits_range",
                  "fp8adam_encode_sr", "fp8adam_stream_copy", "fp8adam_step_noalloc",
-                 "fp8adam_stream_mix"):
+                 "fp8adam_stream_mix", "fp8adam_stream_rw"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -261,6 +262,15 @@ def fp8adam_stream_copy(src: torch.Tensor, dst: torch.Tensor, stream: int | None
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= nbytes
     _check(load().fp8adam_stream_copy(_ptr(src), _ptr(dst), nbytes, current_stream() if stream is None else stream))
+
+
+def fp8adam_stream_rw(src: torch.Tensor | None, dst: torch.Tensor | None, stream: int | None = None) -> None:
+    """Read all of src and write all of dst (a read-only stream if dst is None, a
+    write-only one if src is None)."""
+    nr = 0 if src is None else src.numel() * src.element_size()
+    nw = 0 if dst is None else dst.numel() * dst.element_size()
+    assert (src is None or src.is_contiguous()) and (dst is None or dst.is_contiguous())
+    _check(load().fp8adam_stream_rw(_ptr(src), nr, _ptr(dst), nw, current_stream() if stream is None else stream))
 
 
 def fp8adam_stream_mix(p: torch.Tensor, g: torch.Tensor, m_in: torch.Tensor, v_in: torch.Tensor,

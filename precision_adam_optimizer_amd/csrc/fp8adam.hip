@@ -280,6 +280,48 @@ __global__ __launch_bounds__(kThreads) void k_stream_copy(const vu4* __restrict_
   }
 }
 
+// A read stream and a write stream with k_stream_copy's access pattern:
+// work-group b covers 16-byte elements [1024 b, 1024 b + 1024); it reads those
+// below n_read and writes those below n_write (src's value where it was read,
+// else zero).  With n_write = 0 it is a read-only stream (each loaded value is
+// consumed by an empty asm statement, so the loads are neither dropped nor left
+// in flight when the wave ends), with n_read = 0 a write-only one: the two rates
+// any mix of reads and writes is measured against.  A work-group whose whole
+// range lies below a size issues its four accesses per lane unconditionally,
+// all loads before the first wait.
+__global__ __launch_bounds__(kThreads) void k_stream_rw(const vu4* __restrict__ src, int64_t n_read,
+                                                        vu4* __restrict__ dst, int64_t n_write) {
+  const int64_t first = (int64_t)blockIdx.x * (4 * kThreads);
+  const int64_t base = first + threadIdx.x;
+  vu4 x[4];
+  if (first + 4 * kThreads <= n_read) {  // uniform
+#pragma unroll
+    for (int u = 0; u < 4; u++) x[u] = ld_stream<vu4, true>(src + base + (int64_t)u * kThreads);
+#pragma unroll
+    for (int u = 0; u < 4; u++) asm volatile("" ::"v"(x[u].x), "v"(x[u].y), "v"(x[u].z), "v"(x[u].w));
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int64_t i = base + (int64_t)u * kThreads;
+      x[u] = vu4{0u, 0u, 0u, 0u};
+      if (i < n_read) {
+        x[u] = ld_stream<vu4, true>(src + i);
+        asm volatile("" ::"v"(x[u].x), "v"(x[u].y), "v"(x[u].z), "v"(x[u].w));
+      }
+    }
+  }
+  if (first + 4 * kThreads <= n_write) {  // uniform
+#pragma unroll
+    for (int u = 0; u < 4; u++) st_stream<vu4, true>(dst + base + (int64_t)u * kThreads, x[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int64_t i = base + (int64_t)u * kThreads;
+      if (i < n_write) st_stream<vu4, true>(dst + i, x[u]);
+    }
+  }
+}
+
 // The update pass's byte stream with trivial arithmetic (p += g, codes xor g):
 // per group of four elements it reads the weights (16 bytes fp32 / 8 bf16),
 // the gradients (8) and two code words (4 each), writes the weights back in
@@ -1049,6 +1091,21 @@ int fp8adam_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
   if (groups > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "copy too large");
   hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)groups), dim3(kThreads), 0, stream, static_cast<const vu4*>(src),
                      static_cast<vu4*>(dst), n16);
+  HIP_TRY(hipGetLastError());
+  return 0;
+}
+
+int fp8adam_stream_rw(const void* src, int64_t read_bytes, void* dst, int64_t write_bytes, hipStream_t stream) {
+  if (read_bytes < 0 || write_bytes < 0 || ((read_bytes | write_bytes) & 15) || (read_bytes > 0 && !src) ||
+      (write_bytes > 0 && !dst))
+    return fail(FP8ADAM_EINVAL, "sizes must be non-negative multiples of 16, with a non-null pointer where nonzero");
+  if (((uintptr_t)src & 15u) || ((uintptr_t)dst & 15u)) return fail(FP8ADAM_EALIGN, "src and dst must be 16-byte aligned");
+  const int64_t n_read = read_bytes / 16, n_write = write_bytes / 16;
+  const int64_t groups = (std::max(n_read, n_write) + 4 * kThreads - 1) / (4 * kThreads);
+  if (groups > (int64_t)INT32_MAX) return fail(FP8ADAM_EINVAL, "stream too large");
+  if (groups == 0) return 0;
+  hipLaunchKernelGGL(k_stream_rw, dim3((unsigned)groups), dim3(kThreads), 0, stream, static_cast<const vu4*>(src),
+                     n_read, static_cast<vu4*>(dst), n_write);
   HIP_TRY(hipGetLastError());
   return 0;
 }

@@ -80,6 +80,12 @@ def test_error_paths_without_a_gpu():
     assert L.fp8adam_stream_copy(None, None, 32, None) == -1        # null pointers
     assert L.fp8adam_stream_copy(8, 16, 32, None) == -2             # misaligned
     assert L.fp8adam_stream_copy(None, None, 0, None) == 0
+    assert L.fp8adam_stream_rw(None, 24, None, 0, None) == -1         # not a multiple of 16
+    assert L.fp8adam_stream_rw(None, 0, None, -16, None) == -1        # negative
+    assert L.fp8adam_stream_rw(None, 32, None, 0, None) == -1         # null source
+    assert L.fp8adam_stream_rw(None, 0, None, 32, None) == -1         # null destination
+    assert L.fp8adam_stream_rw(8, 32, None, 0, None) == -2            # misaligned
+    assert L.fp8adam_stream_rw(None, 0, None, 0, None) == 0
     assert L.fp8adam_num_chunks(None) == -1
     assert L.fp8adam_set_timing_kinds(None, 1) == -1
     amp = pk.AmpConfigArg(1.0, 2.0, 0.5, 2000)

@@ -167,6 +167,25 @@ def test_stream_copy_copies_every_byte():
         assert bool((dst[nbytes:] == 0xA5).all()), nbytes
 
 
+def test_stream_rw_reads_and_writes_what_it_counts():
+    """The read and write streams the benchmark decomposes the byte mix with:
+    equal sizes copy; a longer destination gets zeros past the source; a
+    read-only call leaves memory untouched; a write-only call writes zeros; bytes
+    past the written range stay untouched.  Sizes around the 16 KiB tile."""
+    for nr, nw in ((16384, 16384), (16, 4096), (3 * 16384 + 48, 3 * 16384 + 48 + 4096 + 16), (1 << 22, 0),
+                   (0, 16384 + 16), (4096, 16)):
+        src = torch.randint(0, 256, (max(nr, 16),), dtype=torch.uint8, device="cuda")
+        dst = torch.full((nw + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+        src0 = src.clone()
+        pk.fp8adam_stream_rw(src[:nr] if nr else None, dst[:nw] if nw else None)
+        torch.cuda.synchronize()
+        k = min(nr, nw)
+        assert torch.equal(dst[:k], src[:k]), (nr, nw)
+        assert bool((dst[k:nw] == 0).all()), (nr, nw)
+        assert bool((dst[nw:] == 0xA5).all()), (nr, nw)
+        assert torch.equal(src, src0), (nr, nw)
+
+
 @pytest.mark.parametrize("master", ["fp32", "bf16"])
 def test_stream_mix_reads_and_writes_every_element(master):
     """The byte-mix probe the benchmark uses as the update pass's ceiling moves
