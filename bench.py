@@ -300,8 +300,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in the design notes); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the step has no multi-GPU path; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()

@@ -28,8 +28,7 @@
  *           round-to-nearest is the standard rounding;
  *         - "Code example": the optimizer is AdamW (decoupled weight decay).
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes of the repository):
+ * Readings where the pages are silent:
  *  - Formats are the OCP ones: E4M3FN (bias 7, max 448, no infinities, NaN =
  *    S.1111.111) and E5M2 (bias 15, max 57344, IEEE infinities and NaNs).
  *    Subnormals are kept.  Encoding rounds to nearest, ties to even, and
