@@ -17,14 +17,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "precision_adam_optimizer_amd")
 
 
-def _build(tmp_path) -> str:
-    exe = str(tmp_path / "c_abi_demo")
+def build_c_demo(tmp_path, name: str = "c_abi_demo") -> str:
+    """Compile and link tests/<name>.c against the library and the HIP runtime."""
+    exe = str(tmp_path / name)
     subprocess.run(["gcc", "-std=c11", "-O1", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
                     f"-I{os.path.join(ROOT, 'include')}", "-I/opt/rocm/include",
-                    os.path.join(ROOT, "tests", "c_abi_demo.c"), f"-L{PKG}", "-lfp8adam", "-L/opt/rocm/lib",
+                    os.path.join(ROOT, "tests", f"{name}.c"), f"-L{PKG}", "-lfp8adam", "-L/opt/rocm/lib",
                     "-lamdhip64", f"-Wl,-rpath,{PKG}", "-Wl,-rpath,/opt/rocm/lib", "-o", exe],
                    check=True, capture_output=True, text=True)
     return exe
+
+
+def _build(tmp_path) -> str:
+    return build_c_demo(tmp_path)
 
 
 def test_c_caller_compiles_and_links(tmp_path):
@@ -34,6 +39,16 @@ def test_c_caller_compiles_and_links(tmp_path):
     libs = subprocess.run(["ldd", exe], check=True, capture_output=True, text=True).stdout
     assert "libfp8adam.so" in libs and "libamdhip64" in libs
     assert "torch" not in libs and "python" not in libs
+
+
+def test_c_graph_caller_of_the_allocation_free_step_compiles():
+    """tests/c_noalloc_graph_demo.c (run on the GPU by the allocation-free
+    step's tests) is plain C against the header and the HIP runtime."""
+    import tempfile
+    import pathlib
+    with tempfile.TemporaryDirectory() as d:
+        exe = build_c_demo(pathlib.Path(d), "c_noalloc_graph_demo")
+        assert os.path.exists(exe)
 
 
 @pytest.mark.gpu

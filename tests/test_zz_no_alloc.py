@@ -224,3 +224,17 @@ def test_noalloc_step_replayed_from_a_graph(granularity):
                 assert torch.equal(_bits(x), _bits(y)), f"replay {r + 1}: {k} of tensor {i} (numel {sizes[i]})"
     del g
     torch.cuda.synchronize()
+
+
+def test_noalloc_step_in_a_graph_from_plain_c(tmp_path):
+    """The allocation-free step from a plain C program with no torch and no
+    Python in the process (tests/c_noalloc_graph_demo.c): after one eager call
+    that sets up the device's scratch address, a step is captured with the HIP
+    graph API (the capture leaves the state untouched) and replayed three
+    times, bit for bit against the same step called eagerly on a copy."""
+    import subprocess
+
+    from tests.test_c_abi import build_c_demo
+    exe = build_c_demo(tmp_path, "c_noalloc_graph_demo")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
